@@ -1,0 +1,157 @@
+/*
+ * kvq.h — decode attention over a mixed-precision, group-quantized KV cache (AMD CDNA4).
+ *
+ * Plain C ABI. No exception crosses it; every call that can fail returns a kvq_status and
+ * leaves a thread-local message for kvq_last_error(). Pointers are plain addresses: those
+ * named *_dev are device (HBM) addresses, everything else is host memory. Streams are
+ * hipStream_t handles passed as void* (NULL = the default stream).
+ *
+ * The method (sources: the RateQuant and InnerQ pages):
+ *   - keys are quantized in groups of 32 consecutive head_dim channels of one token, values
+ *     in groups of 32 consecutive tokens of one channel: grouping along the inner dimension
+ *     of q.K^T and P.V (InnerQ, abstract and "Core claim");
+ *   - each group is asymmetric min/max, or in hybrid mode the lower-error of symmetric and
+ *     asymmetric (InnerQ, technique (i)), with float16 scale s and zero z;
+ *   - the first n_sink tokens and the most recent n_recent..n_recent+31 tokens stay in 16
+ *     bits (InnerQ, technique (ii));
+ *   - bits per KV head come from the distortion model D(b) = alpha * beta^-b fitted on a
+ *     calibration slice and allocated by reverse waterfilling / greedy integer allocation
+ *     (RateQuant, sections 3.1, 3.3, 3.4);
+ *   - decode reads the packed codes with dequantization fused into q.K^T and P.V, split-K
+ *     over tokens, merged by log-sum-exp (InnerQ, "Algorithm 1 ... decode phase").
+ *
+ * Ownership: the caller allocates and frees every device buffer (cache blob, inputs,
+ * outputs, workspace). The library never allocates or frees device memory and keeps no
+ * global state besides the thread-local error string.
+ */
+#ifndef KVQ_H_
+#define KVQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_MAX_KV_HEADS 128
+#define KVQ_GROUP 32
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_ARG = -1,         /* bad argument or shape; nothing was enqueued */
+  KVQ_ERR_BUDGET = -2,      /* n*b_lo > total or total > n*b_hi */
+  KVQ_ERR_CAPACITY = -3,    /* append would exceed the cache capacity */
+  KVQ_ERR_RANGE = -4,       /* a quantized input was non-finite or |x| > 2^14 */
+  KVQ_ERR_UNSUPPORTED = -5, /* a configuration this build does not implement */
+  KVQ_ERR_DEVICE = -6       /* a HIP call failed; kvq_last_error() has HIP's message */
+} kvq_status;
+
+typedef enum { KVQ_F16 = 0, KVQ_BF16 = 1 } kvq_dtype;
+enum { KVQ_QUANT_ASYM = 0, KVQ_QUANT_HYBRID = 1 };
+enum { KVQ_AXIS_KEY = 0, KVQ_AXIS_VALUE = 1 };
+enum { KVQ_ALLOC_CAP_W = 1u }; /* w_i <- min(w_i, 5 * mean(w)) before allocating (RateQuant W.14) */
+
+/* Cache geometry. Host memory, owned by the caller. */
+typedef struct {
+  int32_t batch;        /* rows B >= 1 */
+  int32_t n_kv_heads;   /* Hkv, 1..KVQ_MAX_KV_HEADS */
+  int32_t n_q_heads;    /* Hq, a multiple of Hkv; query head i reads KV head i / (Hq/Hkv) */
+  int32_t head_dim;     /* D: 64 or 128 */
+  int32_t capacity;     /* maximum tokens per row */
+  int32_t group;        /* must be KVQ_GROUP (32) */
+  int32_t n_sink;       /* first tokens kept in 16 bits, >= 0 */
+  int32_t n_recent;     /* recent tokens kept in 16 bits, >= 0 (the window holds
+                           n_recent..n_recent+31 once the body has started) */
+  int32_t dtype;        /* kvq_dtype of keys, values and queries */
+  int32_t quant;        /* KVQ_QUANT_ASYM or KVQ_QUANT_HYBRID */
+  uint8_t k_bits[KVQ_MAX_KV_HEADS]; /* per KV head: 2..8, or 16 = unquantized */
+  uint8_t v_bits[KVQ_MAX_KV_HEADS];
+} kvq_config;
+
+/* A cache handle: the caller's POD. `dev` is a device blob of `bytes` bytes laid out by
+ * kvq_cache_init; `len` is the token count of every row. kvq_append changes `len`, so
+ * calls on one cache must be serialized by the caller (same stream, or host order). */
+typedef struct {
+  kvq_config cfg;
+  void* dev;
+  uint64_t bytes;
+  int32_t len;
+  int32_t reserved;
+} kvq_cache;
+
+/* Blob bytes needed for `cfg` (0 if cfg is invalid; kvq_last_error() says why). */
+size_t kvq_cache_bytes(const kvq_config* cfg);
+
+/* Validate cfg, write the blob header and region table into dev_mem (synchronously on
+ * `stream`), clear the sticky range flag, and set cache->len = 0. dev_mem must be at least
+ * kvq_cache_bytes(cfg) bytes and 256-byte aligned. */
+kvq_status kvq_cache_init(kvq_cache* cache, const kvq_config* cfg, void* dev_mem, size_t bytes,
+                          void* stream);
+
+/* Calibration + distortion fit (RateQuant sections 3.1, 3.4, 4.1, W.10).
+ * x_dev: [n_heads][n_tokens][head_dim] 16-bit (dtype), one calibration slice per head.
+ * axis KVQ_AXIS_KEY groups 32 channels of a token; KVQ_AXIS_VALUE groups 32 tokens of a
+ * channel (n_tokens must then be a multiple of 32). For every head and b = b_lo..b_hi the
+ * device computes each group's squared quantization error in float64 (quant = asym or
+ * hybrid); the host adds them in group order, divides by n_tokens*head_dim to get D(b),
+ * fits ln D(b) = ln alpha - b ln beta by least squares and applies the beta fallback
+ * (R^2 < 0.96: beta = min(beta, mean beta of the well-fitted heads)).
+ * Outputs alpha, beta, r2: host arrays [n_heads]. Needs 2 <= b_lo, b_lo + 2 <= b_hi <= 8.
+ * ws_dev: device scratch of at least kvq_calibrate_workspace_bytes(...) bytes.
+ * BLOCKS until the result is on the host. A head whose inputs are out of range makes the
+ * call return KVQ_ERR_RANGE. */
+size_t kvq_calibrate_workspace_bytes(int32_t n_heads, int32_t n_tokens, int32_t head_dim,
+                                     int32_t b_lo, int32_t b_hi);
+kvq_status kvq_calibrate_fit(const void* x_dev, int32_t dtype, int32_t n_heads,
+                             int32_t n_tokens, int32_t head_dim, int32_t axis, int32_t quant,
+                             int32_t b_lo, int32_t b_hi, void* ws_dev, size_t ws_bytes,
+                             double* alpha, double* beta, double* r2, void* stream);
+
+/* Bit allocation (RateQuant sections 3.1, 3.3, B.1, B.3, U): host only, pure.
+ * Minimizes sum_i w_i alpha_i beta_i^-b_i over integers b_lo <= b_i <= b_hi with
+ * sum b_i = total_bits: every head starts at b_lo and a max-heap hands out the remaining
+ * bits one at a time to the largest marginal gain w a beta^-b (1 - 1/beta) (ties: lowest
+ * index). bits_cont_out (nullable) receives the continuous reverse-waterfilling solution.
+ * alpha >= 0, beta > 1, w > 0, 2 <= b_lo <= b_hi <= 8; flags: KVQ_ALLOC_CAP_W. */
+kvq_status kvq_allocate_bits(int32_t n, const double* alpha, const double* beta,
+                             const double* w, int32_t total_bits, int32_t b_lo, int32_t b_hi,
+                             uint32_t flags, uint8_t* bits_out, double* bits_cont_out);
+
+/* Append n_new tokens to every row (InnerQ techniques (i)-(ii); asynchronous on stream).
+ * k_dev, v_dev: [batch][n_kv_heads][n_new][head_dim] 16-bit. Tokens 0..n_sink-1 of a row
+ * go to the sink; later tokens enter the recent ring; whenever the ring holds
+ * n_recent + 32 tokens its oldest 32 are quantized and packed as one body block.
+ * len + n_new must not exceed capacity (else KVQ_ERR_CAPACITY, nothing enqueued).
+ * Out-of-range quantized inputs set the cache's sticky flag (see kvq_cache_check). */
+kvq_status kvq_append(kvq_cache* cache, const void* k_dev, const void* v_dev, int32_t n_new,
+                      void* stream);
+
+/* Split-K decode attention for one query token per row (InnerQ Algorithm 1 structure).
+ * q_dev: [batch][n_q_heads][head_dim] 16-bit; out_dev: [batch][n_q_heads][head_dim] fp32.
+ * The body is cut into n_splits token chunks (1..1024); the 16-bit windows form one more
+ * partial; the partials (m, l, o) are merged by log-sum-exp. scale <= 0 means 1/sqrt(D).
+ * workspace_dev: at least kvq_decode_workspace_bytes(cache, n_splits) bytes.
+ * Asynchronous on stream. len must be >= 1. */
+size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t n_splits);
+kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q_dev, float* out_dev,
+                                int32_t n_splits, float scale, void* workspace_dev,
+                                size_t ws_bytes, void* stream);
+
+/* Synchronize `stream`, read the sticky range flag; KVQ_ERR_RANGE if it is set. */
+kvq_status kvq_cache_check(const kvq_cache* cache, void* stream);
+
+/* Byte offset, from the blob start, of region `region` (0..8: key codes, key meta, value
+ * codes, value meta, hybrid flags, sink keys, sink values, ring keys, ring values) of
+ * (row, kv_head), and its size; returns 0 and sets *size = 0 on bad arguments. */
+uint64_t kvq_region_offset(const kvq_config* cfg, int32_t row, int32_t kv_head, int32_t region,
+                           uint64_t* size);
+
+/* Message of the last non-OK status on this thread ("" if none). */
+const char* kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H_ */

@@ -1,0 +1,255 @@
+"""Python binding of libkvq: decode attention over a mixed-precision quantized KV cache.
+
+Argument marshalling only. Every step of the path (quantize, pack, calibrate, decode, merge)
+runs in the HIP kernels of libkvq.so, reached through its C ABI (include/kvq.h); the
+allocator, fit and layout planner run in the library's C++ host code. PyTorch supplies
+device memory and streams. If the shared library is missing, every call raises: there is no
+fallback implementation.
+
+Names follow the C calls: cache_bytes, cache_init, calibrate_fit, allocate_bits, append,
+decode_workspace_bytes, decode_attention, cache_check, region_offset, last_error.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "KvqError", "Config", "KVCache", "lib", "lib_path", "cache_bytes", "cache_init",
+    "calibrate_fit", "calibrate_workspace_bytes", "allocate_bits", "append",
+    "decode_workspace_bytes", "decode_attention", "cache_check", "region_offset", "last_error",
+    "F16", "BF16", "QUANT_ASYM", "QUANT_HYBRID", "AXIS_KEY", "AXIS_VALUE", "ALLOC_CAP_W",
+    "EXPORTS",
+]
+
+F16, BF16 = 0, 1
+QUANT_ASYM, QUANT_HYBRID = 0, 1
+AXIS_KEY, AXIS_VALUE = 0, 1
+ALLOC_CAP_W = 1
+MAX_KV_HEADS = 128
+REGIONS = ("key_codes", "key_meta", "value_codes", "value_meta", "flags", "sink_keys",
+           "sink_values", "ring_keys", "ring_values")
+
+STATUS = {0: "OK", -1: "ERR_ARG", -2: "ERR_BUDGET", -3: "ERR_CAPACITY", -4: "ERR_RANGE",
+          -5: "ERR_UNSUPPORTED", -6: "ERR_DEVICE"}
+
+EXPORTS = ("kvq_cache_bytes", "kvq_cache_init", "kvq_calibrate_workspace_bytes",
+           "kvq_calibrate_fit", "kvq_allocate_bits", "kvq_append", "kvq_decode_workspace_bytes",
+           "kvq_decode_attention", "kvq_cache_check", "kvq_region_offset", "kvq_last_error")
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("n_sink", ctypes.c_int32), ("n_recent", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("quant", ctypes.c_int32),
+                ("k_bits", ctypes.c_uint8 * MAX_KV_HEADS), ("v_bits", ctypes.c_uint8 * MAX_KV_HEADS)]
+
+    @classmethod
+    def make(cls, batch, n_kv_heads, n_q_heads, head_dim, capacity, n_sink, n_recent, dtype,
+             quant, k_bits, v_bits):
+        c = cls()
+        c.batch, c.n_kv_heads, c.n_q_heads, c.head_dim = batch, n_kv_heads, n_q_heads, head_dim
+        c.capacity, c.group, c.n_sink, c.n_recent = capacity, 32, n_sink, n_recent
+        c.dtype = dtype if isinstance(dtype, int) else {"fp16": F16, "bf16": BF16}[dtype]
+        c.quant = quant if isinstance(quant, int) else {"asym": QUANT_ASYM, "hybrid": QUANT_HYBRID}[quant]
+        for i, b in enumerate(k_bits):
+            c.k_bits[i] = int(b)
+        for i, b in enumerate(v_bits):
+            c.v_bits[i] = int(b)
+        return c
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("cfg", Config), ("dev", ctypes.c_void_p), ("bytes", ctypes.c_uint64),
+                ("len", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libkvq.so")
+
+
+def lib():
+    """Load libkvq.so (built in-tree by mixed_precision_quantized_kvq_amd.build)."""
+    global _LIB
+    if _LIB is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: run __graft_entry__.build() first "
+                              "(there is no fallback implementation)")
+        L = ctypes.CDLL(path)
+        P, I32, U32, U64, SZ, D = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32,
+                                   ctypes.c_uint64, ctypes.c_size_t, ctypes.POINTER(ctypes.c_double))
+        CP = ctypes.POINTER(Config)
+        KP = ctypes.POINTER(_Cache)
+        sig = {
+            "kvq_cache_bytes": (SZ, [CP]),
+            "kvq_cache_init": (I32, [KP, CP, P, SZ, P]),
+            "kvq_calibrate_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
+            "kvq_calibrate_fit": (I32, [P, I32, I32, I32, I32, I32, I32, I32, I32, P, SZ, D, D, D, P]),
+            "kvq_allocate_bits": (I32, [I32, D, D, D, I32, I32, I32, U32,
+                                        ctypes.POINTER(ctypes.c_uint8), D]),
+            "kvq_append": (I32, [KP, P, P, I32, P]),
+            "kvq_decode_workspace_bytes": (SZ, [KP, I32]),
+            "kvq_decode_attention": (I32, [KP, P, P, I32, ctypes.c_float, P, SZ, P]),
+            "kvq_cache_check": (I32, [KP, P]),
+            "kvq_region_offset": (U64, [CP, I32, I32, I32, ctypes.POINTER(U64)]),
+            "kvq_last_error": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _LIB = L
+    return _LIB
+
+
+def last_error() -> str:
+    return lib().kvq_last_error().decode()
+
+
+def _check(st: int):
+    if st != 0:
+        raise KvqError(st, last_error())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _darr(x):
+    vals = [float(v) for v in x]
+    return (ctypes.c_double * len(vals))(*vals)
+
+
+# ------------------------------------------------------------------------- host calls --
+
+def cache_bytes(cfg: Config) -> int:
+    n = lib().kvq_cache_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise KvqError(-1, last_error())
+    return int(n)
+
+
+def region_offset(cfg: Config, row: int, kv_head: int, region: int):
+    size = ctypes.c_uint64(0)
+    off = lib().kvq_region_offset(ctypes.byref(cfg), row, kv_head, region, ctypes.byref(size))
+    if off == 0:
+        raise KvqError(-1, last_error())
+    return int(off), int(size.value)
+
+
+def allocate_bits(alpha, beta, w, total_bits: int, b_lo: int, b_hi: int, cap: bool = False):
+    """Integer bits (greedy / max-heap) and the continuous waterfilling solution."""
+    n = len(alpha)
+    out = (ctypes.c_uint8 * n)()
+    cont = (ctypes.c_double * n)()
+    _check(lib().kvq_allocate_bits(n, _darr(alpha), _darr(beta), _darr(w), int(total_bits),
+                                   int(b_lo), int(b_hi), ALLOC_CAP_W if cap else 0, out, cont))
+    return [int(v) for v in out], [float(v) for v in cont]
+
+
+# ------------------------------------------------------------------------- device calls --
+
+class KVCache:
+    """A cache blob in a torch uint8 device tensor plus the C handle."""
+
+    def __init__(self, cfg: Config, device="cuda", stream=None, blob=None):
+        import torch
+        self.cfg = cfg
+        nbytes = cache_bytes(cfg)
+        self.blob = blob if blob is not None else torch.empty(nbytes, dtype=torch.uint8, device=device)
+        if self.blob.numel() < nbytes:
+            raise ValueError("blob tensor too small")
+        self.handle = _Cache()
+        _check(lib().kvq_cache_init(ctypes.byref(self.handle), ctypes.byref(cfg), _dptr(self.blob),
+                                    nbytes, _stream(stream)))
+
+    @property
+    def len(self) -> int:
+        return int(self.handle.len)
+
+    def region(self, row: int, kv_head: int, region: int):
+        off, size = region_offset(self.cfg, row, kv_head, region)
+        return self.blob[off:off + size]
+
+
+def cache_init(cfg: Config, device="cuda", stream=None) -> KVCache:
+    return KVCache(cfg, device, stream)
+
+
+def append(cache: KVCache, k, v, stream=None):
+    """k, v: [batch][n_kv_heads][n_new][head_dim] 16-bit device tensors (contiguous)."""
+    assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape and k.dim() == 4
+    c = cache.cfg
+    assert tuple(k.shape[:2]) == (c.batch, c.n_kv_heads) and k.shape[3] == c.head_dim
+    assert k.element_size() == 2 and v.element_size() == 2
+    _check(lib().kvq_append(ctypes.byref(cache.handle), _dptr(k), _dptr(v), int(k.shape[2]),
+                            _stream(stream)))
+
+
+def decode_workspace_bytes(cache: KVCache, n_splits: int) -> int:
+    n = lib().kvq_decode_workspace_bytes(ctypes.byref(cache.handle), int(n_splits))
+    if n == 0:
+        raise KvqError(-1, last_error())
+    return int(n)
+
+
+def decode_attention(cache: KVCache, q, out, n_splits: int, workspace, scale: float = 0.0,
+                     stream=None):
+    """q: [batch][n_q_heads][head_dim] 16-bit; out: same shape float32 (written)."""
+    import torch
+    c = cache.cfg
+    assert q.is_contiguous() and out.is_contiguous() and out.dtype == torch.float32
+    assert tuple(q.shape) == (c.batch, c.n_q_heads, c.head_dim) and tuple(out.shape) == tuple(q.shape)
+    _check(lib().kvq_decode_attention(ctypes.byref(cache.handle), _dptr(q), _dptr(out), int(n_splits),
+                                      float(scale), _dptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)))
+
+
+def cache_check(cache: KVCache, stream=None):
+    _check(lib().kvq_cache_check(ctypes.byref(cache.handle), _stream(stream)))
+
+
+def calibrate_workspace_bytes(n_heads, n_tokens, head_dim, b_lo=2, b_hi=8) -> int:
+    return int(lib().kvq_calibrate_workspace_bytes(n_heads, n_tokens, head_dim, b_lo, b_hi))
+
+
+def calibrate_fit(x, dtype, axis: int, quant: int = QUANT_ASYM, b_lo: int = 2, b_hi: int = 8,
+                  workspace=None, stream=None):
+    """x: [n_heads][n_tokens][head_dim] 16-bit device tensor. Returns (alpha, beta, r2)."""
+    import torch
+    assert x.is_contiguous() and x.dim() == 3 and x.element_size() == 2
+    H, T, D = x.shape
+    need = calibrate_workspace_bytes(H, T, D, b_lo, b_hi)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    a = (ctypes.c_double * H)()
+    b = (ctypes.c_double * H)()
+    r = (ctypes.c_double * H)()
+    dt = dtype if isinstance(dtype, int) else {"fp16": F16, "bf16": BF16}[dtype]
+    _check(lib().kvq_calibrate_fit(_dptr(x), dt, H, T, D, axis, quant, b_lo, b_hi, _dptr(workspace),
+                                   workspace.numel(), a, b, r, _stream(stream)))
+    return list(a), list(b), list(r)
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,165 @@
+// Append kernels: quantize + pack the 32-token blocks that leave the recent window, and copy
+// new sink / recent tokens into their 16-bit windows (InnerQ techniques (i) and (ii)).
+// Built with -ffp-contract=off: the quantizer must round exactly as quant_device.h states.
+#include <hip/hip_runtime.h>
+
+#include "kvq_internal.h"
+#include "quant_device.h"
+
+namespace kvq {
+namespace {
+
+// Address of absolute token t of (row, head): the ring if it was appended before this call
+// (only live ring tokens are ever flushed), else the new input.
+__device__ __forceinline__ const uint16_t* token_row(const AppendPlan& p, const char* base_ring,
+                                                     const uint16_t* in, int t) {
+  if (t < p.len0) {
+    const int slot = (t - p.n_sink) % (p.n_recent + kGroup);
+    return reinterpret_cast<const uint16_t*>(base_ring) + (size_t)slot * p.D;
+  }
+  return in + (size_t)(t - p.len0) * p.D;
+}
+
+__device__ __forceinline__ void load_row32(const uint16_t* src, int dtype, float (&x)[32]) {
+  const uint4* s4 = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const uint4 u = s4[v];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[v * 8 + 2 * k] = widen16((uint16_t)(w[k] & 0xFFFFu), dtype);
+      x[v * 8 + 2 * k + 1] = widen16((uint16_t)(w[k] >> 16), dtype);
+    }
+  }
+}
+
+// One workgroup per (flushed block, head, row); 2*D threads: thread i < D handles key group
+// i = (token tt of the block) * (D/32) + channel group g, thread D + c handles value channel c.
+__global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
+  const int j = p.body0 / kGroup + blockIdx.x;  // body block index
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int D = p.D, Gd = D / kGroup;
+  const uint64_t* off = p.off + ((size_t)b * p.H + h) * kRegions;
+  const size_t in_off = ((size_t)b * p.H + h) * p.n_new * D;
+  const uint16_t* kin = reinterpret_cast<const uint16_t*>(p.k_in) + in_off;
+  const uint16_t* vin = reinterpret_cast<const uint16_t*>(p.v_in) + in_off;
+  const int tid = threadIdx.x;
+  const bool is_key = tid < D;
+  const int bits = is_key ? p.k_bits[h] : p.v_bits[h];
+  const int tile = j >> 1, jj = j & 1;
+  float x[32];
+  if (is_key) {
+    const int tt = tid / Gd, g = tid % Gd;
+    const int t = p.n_sink + j * kGroup + tt;
+    const uint16_t* src = token_row(p, p.blob + off[RK], kin, t) + g * kGroup;
+    if (bits == 16) {
+      uint4* dst = reinterpret_cast<uint4*>(p.blob + off[KC]) +
+                   ((size_t)(j * kGroup + tt) * D + g * kGroup) / 8;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dst[v] = reinterpret_cast<const uint4*>(src)[v];
+      return;
+    }
+    load_row32(src, p.dtype, x);
+  } else {
+    const int c = tid - D;
+    const char* ring = p.blob + off[RV];
+    if (bits == 16) {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(p.blob + off[VC]);
+#pragma unroll
+      for (int k = 0; k < 32; ++k)
+        dst[(size_t)(j * kGroup + k) * D + c] = token_row(p, ring, vin, p.n_sink + j * kGroup + k)[c];
+      return;
+    }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int t = p.n_sink + j * kGroup + k;
+      x[k] = widen16(token_row(p, ring, vin, t)[c], p.dtype);
+    }
+  }
+  if (out_of_range(x)) atomicOr(p.range_flag, 1u);
+  const GroupQ q = choose_quant(x, bits, p.hybrid != 0);
+  const uint32_t meta = (uint32_t)q.s_bits | ((uint32_t)q.z_bits << 16);
+  if (is_key) {
+    const int tt = tid / Gd, g = tid % Gd;
+    const int W = Gd * bits;                       // words per token
+    const int t_in_tile = jj * kGroup + tt;
+    uint32_t* kc = reinterpret_cast<uint32_t*>(p.blob + off[KC]) + (size_t)tile * kTile * W;
+    pack_group(x, q, bits, [&](int k, uint32_t word) {
+      const int w = g * bits + k;
+      const int qc = w >> 2, nq = min(4, W - 4 * qc);
+      kc[256 * qc + t_in_tile * nq + (w - 4 * qc)] = word;
+    });
+    reinterpret_cast<uint32_t*>(p.blob + off[KM])[(size_t)(j * kGroup + tt) * Gd + g] = meta;
+  } else {
+    const int c = tid - D;
+    uint32_t* vc = reinterpret_cast<uint32_t*>(p.blob + off[VC]) + ((size_t)tile * 2 * D + c * 2 + jj) * bits;
+    pack_group(x, q, bits, [&](int k, uint32_t word) { vc[k] = word; });
+    reinterpret_cast<uint32_t*>(p.blob + off[VM])[(size_t)tile * 2 * D + c * 2 + jj] = meta;
+  }
+  if (p.hybrid) {
+    // flag bit i of this block's key (value) words = group i of thread i (D + i)
+    const unsigned long long m = __ballot(q.sym);
+    if ((tid & 63) == 0) {
+      uint32_t* fl = reinterpret_cast<uint32_t*>(p.blob + off[FL]) + (size_t)j * 2 * Gd;
+      const int wbase = (is_key ? 0 : Gd) + ((is_key ? tid : tid - D) >> 5);
+      fl[wbase] = (uint32_t)m;
+      fl[wbase + 1] = (uint32_t)(m >> 32);
+    }
+  }
+}
+
+// Copy new tokens that land in the sink or in the recent ring: one thread per 16 bytes of a
+// key or value row. Token index k < n_a is sink token len0 + k, else ring token t_b + k - n_a.
+__global__ __launch_bounds__(256) void append_window_kernel(const AppendPlan p, int n_a, int t_b, int n_tok) {
+  const int chunks = p.D / 8;                   // 16-byte chunks per row
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)p.B * p.H * n_tok * 2 * chunks;
+  if (gid >= total) return;
+  const int ch = (int)(gid % chunks);
+  long long r = gid / chunks;
+  const int kv = (int)(r % 2);
+  r /= 2;
+  const int k = (int)(r % n_tok);
+  r /= n_tok;
+  const int h = (int)(r % p.H), b = (int)(r / p.H);
+  const int t = k < n_a ? p.len0 + k : t_b + (k - n_a);
+  const uint64_t* off = p.off + ((size_t)b * p.H + h) * kRegions;
+  const uint16_t* in = reinterpret_cast<const uint16_t*>(kv ? p.v_in : p.k_in) +
+                       (((size_t)b * p.H + h) * p.n_new + (t - p.len0)) * p.D;
+  char* dst_row;
+  if (t < p.n_sink) {
+    dst_row = p.blob + off[kv ? SV : SK] + (size_t)t * p.D * 2;
+  } else {
+    const int slot = (t - p.n_sink) % (p.n_recent + kGroup);
+    dst_row = p.blob + off[kv ? RV : RK] + (size_t)slot * p.D * 2;
+  }
+  reinterpret_cast<uint4*>(dst_row)[ch] = reinterpret_cast<const uint4*>(in)[ch];
+}
+
+}  // namespace
+
+int launch_append_flush(const AppendPlan& p, void* stream) {
+  const int nblk = (p.body1 - p.body0) / kGroup;
+  if (nblk <= 0) return (int)hipSuccess;
+  dim3 grid(nblk, p.H, p.B);
+  hipLaunchKernelGGL(append_flush_kernel, grid, dim3(2 * p.D), 0, (hipStream_t)stream, p);
+  return (int)hipGetLastError();
+}
+
+int launch_append_window(const AppendPlan& p, void* stream) {
+  // sink tokens [len0, min(len1, n_sink)); ring tokens [max(len0, n_sink + body1), len1)
+  const int n_a = max(0, min(p.len1, p.n_sink) - p.len0);
+  const int t_b = max(p.len0, p.n_sink + p.body1);
+  const int n_b = max(0, p.len1 - t_b);
+  const int n_tok = n_a + n_b;
+  if (n_tok == 0) return (int)hipSuccess;
+  const long long total = (long long)p.B * p.H * n_tok * 2 * (p.D / 8);
+  const int threads = 256;
+  const long long blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(append_window_kernel, dim3((unsigned)blocks), dim3(threads), 0,
+                     (hipStream_t)stream, p, n_a, t_b, n_tok);
+  return (int)hipGetLastError();
+}
+
+}  // namespace kvq

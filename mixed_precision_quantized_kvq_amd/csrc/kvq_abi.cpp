@@ -1,0 +1,283 @@
+// C ABI entry points of libkvq (declared in include/kvq.h): argument checks on the host,
+// then kernel launches on the caller's stream. No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+kvq_status hip_fail(hipError_t e, const char* what) {
+  return fail(KVQ_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+kvq_status check_launch(int e, const char* what) {
+  if (e != (int)hipSuccess) return hip_fail((hipError_t)e, what);
+  return KVQ_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+kvq_status check_cache(const kvq_cache* c) {
+  if (!c) return fail(KVQ_ERR_ARG, "cache is NULL");
+  kvq_status st = check_config(&c->cfg);
+  if (st != KVQ_OK) return st;
+  if (!c->dev) return fail(KVQ_ERR_ARG, "cache has no device memory");
+  if (c->len < 0 || c->len > c->cfg.capacity) return fail(KVQ_ERR_ARG, "cache len out of range");
+  if (c->bytes < plan_layout(c->cfg, nullptr)) return fail(KVQ_ERR_ARG, "cache blob too small");
+  return KVQ_OK;
+}
+
+const uint64_t* table_ptr(const kvq_cache* c) {
+  return reinterpret_cast<const uint64_t*>(static_cast<const char*>(c->dev) + kHeaderBytes);
+}
+uint32_t* flag_ptr(const kvq_cache* c) {
+  return reinterpret_cast<uint32_t*>(static_cast<char*>(c->dev) + offsetof(BlobHeader, range_flag));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_last_error(void) { return last_error(); }
+
+size_t kvq_cache_bytes(const kvq_config* cfg) {
+  if (check_config(cfg) != KVQ_OK) return 0;
+  return (size_t)plan_layout(*cfg, nullptr);
+}
+
+uint64_t kvq_region_offset(const kvq_config* cfg, int32_t row, int32_t kv_head, int32_t region,
+                           uint64_t* size) {
+  if (size) *size = 0;
+  if (check_config(cfg) != KVQ_OK) return 0;
+  if (row < 0 || row >= cfg->batch || kv_head < 0 || kv_head >= cfg->n_kv_heads || region < 0 ||
+      region >= kRegions) {
+    set_error("region index out of range");
+    return 0;
+  }
+  std::vector<uint64_t> off((size_t)cfg->batch * cfg->n_kv_heads * kRegions);
+  plan_layout(*cfg, off.data());
+  uint64_t sz[kRegions];
+  region_sizes(*cfg, kv_head, sz);
+  if (size) *size = sz[region];
+  return off[((size_t)row * cfg->n_kv_heads + kv_head) * kRegions + region];
+}
+
+kvq_status kvq_cache_init(kvq_cache* cache, const kvq_config* cfg, void* dev_mem, size_t bytes,
+                          void* stream) {
+  if (!cache) return fail(KVQ_ERR_ARG, "cache is NULL");
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!dev_mem || !aligned(dev_mem, 256)) return fail(KVQ_ERR_ARG, "dev_mem must be 256-byte aligned");
+  const size_t n_off = (size_t)cfg->batch * cfg->n_kv_heads * kRegions;
+  std::vector<uint64_t> host(kHeaderBytes / 8 + n_off, 0);
+  const uint64_t total = plan_layout(*cfg, host.data() + kHeaderBytes / 8);
+  if (bytes < total) return fail(KVQ_ERR_ARG, "dev_mem smaller than kvq_cache_bytes()");
+  BlobHeader hdr{};
+  hdr.magic = kMagic;
+  hdr.version = 1;
+  hdr.range_flag = 0;
+  hdr.n_regions = kRegions;
+  hdr.batch = cfg->batch;
+  hdr.n_kv_heads = cfg->n_kv_heads;
+  hdr.head_dim = cfg->head_dim;
+  hdr.capacity = cfg->capacity;
+  hdr.table_offset = kHeaderBytes;
+  hdr.total_bytes = total;
+  std::memcpy(host.data(), &hdr, sizeof(hdr));
+  hipError_t e = hipMemcpyAsync(dev_mem, host.data(), host.size() * 8, hipMemcpyHostToDevice,
+                                as_stream(stream));
+  if (e == hipSuccess) e = hipStreamSynchronize(as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "cache init copy");
+  cache->cfg = *cfg;
+  cache->dev = dev_mem;
+  cache->bytes = bytes;
+  cache->len = 0;
+  cache->reserved = 0;
+  return KVQ_OK;
+}
+
+kvq_status kvq_cache_check(const kvq_cache* cache, void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  uint32_t flag = 0;
+  hipError_t e = hipMemcpyAsync(&flag, flag_ptr(cache), 4, hipMemcpyDeviceToHost, as_stream(stream));
+  if (e == hipSuccess) e = hipStreamSynchronize(as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "cache check");
+  if (flag) return fail(KVQ_ERR_RANGE, "a quantized input was non-finite or |x| > 2^14");
+  return KVQ_OK;
+}
+
+kvq_status kvq_append(kvq_cache* cache, const void* k_dev, const void* v_dev, int32_t n_new,
+                      void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (n_new < 0) return fail(KVQ_ERR_ARG, "n_new must be >= 0");
+  if (n_new == 0) return KVQ_OK;
+  if (!k_dev || !v_dev) return fail(KVQ_ERR_ARG, "NULL input");
+  if (!aligned(k_dev, 16) || !aligned(v_dev, 16)) return fail(KVQ_ERR_ARG, "inputs must be 16-byte aligned");
+  const kvq_config& c = cache->cfg;
+  if ((int64_t)cache->len + n_new > c.capacity) return fail(KVQ_ERR_CAPACITY, "append exceeds capacity");
+  AppendPlan p{};
+  p.k_in = k_dev;
+  p.v_in = v_dev;
+  p.blob = static_cast<char*>(cache->dev);
+  p.off = table_ptr(cache);
+  p.range_flag = flag_ptr(cache);
+  p.B = c.batch;
+  p.H = c.n_kv_heads;
+  p.D = c.head_dim;
+  p.n_new = n_new;
+  p.len0 = cache->len;
+  p.len1 = cache->len + n_new;
+  p.body0 = (int)body_len(p.len0, c.n_sink, c.n_recent);
+  p.body1 = (int)body_len(p.len1, c.n_sink, c.n_recent);
+  p.n_sink = c.n_sink;
+  p.n_recent = c.n_recent;
+  p.dtype = c.dtype;
+  p.hybrid = c.quant == KVQ_QUANT_HYBRID;
+  std::memcpy(p.k_bits, c.k_bits, sizeof(p.k_bits));
+  std::memcpy(p.v_bits, c.v_bits, sizeof(p.v_bits));
+  // Blocks leaving the ring are quantized first; the window copy runs after it on the same
+  // stream, so new ring tokens never overwrite ring slots that a flushed block still reads.
+  if (p.body1 > p.body0) {
+    st = check_launch(launch_append_flush(p, stream), "append flush launch");
+    if (st != KVQ_OK) return st;
+  }
+  st = check_launch(launch_append_window(p, stream), "append window launch");
+  if (st != KVQ_OK) return st;
+  cache->len = p.len1;
+  return KVQ_OK;
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t n_splits) {
+  if (check_cache(cache) != KVQ_OK) return 0;
+  if (n_splits < 1 || n_splits > 1024) {
+    set_error("n_splits must be in 1..1024");
+    return 0;
+  }
+  const kvq_config& c = cache->cfg;
+  const size_t parts = (size_t)n_splits + 1;
+  const size_t rows = (size_t)c.batch * c.n_q_heads;
+  return align_up(parts * rows * c.head_dim * 4) + align_up(parts * rows * 2 * 4);
+}
+
+kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q_dev, float* out_dev,
+                                int32_t n_splits, float scale, void* ws, size_t ws_bytes,
+                                void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (cache->len < 1) return fail(KVQ_ERR_ARG, "decode on an empty cache");
+  if (!q_dev || !out_dev || !ws) return fail(KVQ_ERR_ARG, "NULL pointer");
+  if (n_splits < 1 || n_splits > 1024) return fail(KVQ_ERR_ARG, "n_splits must be in 1..1024");
+  if (!aligned(q_dev, 16) || !aligned(out_dev, 16) || !aligned(ws, 256))
+    return fail(KVQ_ERR_ARG, "q/out must be 16-byte and workspace 256-byte aligned");
+  if (!(std::isfinite(scale))) return fail(KVQ_ERR_ARG, "scale must be finite");
+  const size_t need = kvq_decode_workspace_bytes(cache, n_splits);
+  if (ws_bytes < need) return fail(KVQ_ERR_ARG, "workspace too small");
+  const kvq_config& c = cache->cfg;
+  DecodePlan p{};
+  p.blob = static_cast<const char*>(cache->dev);
+  p.off = table_ptr(cache);
+  p.q = q_dev;
+  p.out = out_dev;
+  const size_t parts = (size_t)n_splits + 1;
+  const size_t rows = (size_t)c.batch * c.n_q_heads;
+  p.ws_o = static_cast<float*>(ws);
+  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(parts * rows * c.head_dim * 4));
+  p.B = c.batch;
+  p.H = c.n_kv_heads;
+  p.Hq = c.n_q_heads;
+  p.G = c.n_q_heads / c.n_kv_heads;
+  p.D = c.head_dim;
+  p.T = cache->len;
+  p.body = (int)body_len(cache->len, c.n_sink, c.n_recent);
+  p.n_sink_live = std::min(cache->len, c.n_sink);
+  p.n_win = cache->len - p.n_sink_live - p.body;
+  p.n_sink_cfg = c.n_sink;
+  p.ring = ring_slots(c.n_recent);
+  p.n_splits = n_splits;
+  p.n_tiles = (p.body + kTile - 1) / kTile;
+  p.tiles_per_split = (p.n_tiles + n_splits - 1) / n_splits;
+  p.dtype = c.dtype;
+  const float s = scale > 0.0f ? scale : 1.0f / std::sqrt((float)c.head_dim);
+  p.scale_log2 = s * 1.4426950408889634f;
+  std::memcpy(p.k_bits, c.k_bits, sizeof(p.k_bits));
+  std::memcpy(p.v_bits, c.v_bits, sizeof(p.v_bits));
+  return check_launch(launch_decode(p, stream), "decode launch");
+}
+
+size_t kvq_calibrate_workspace_bytes(int32_t n_heads, int32_t n_tokens, int32_t head_dim,
+                                     int32_t b_lo, int32_t b_hi) {
+  if (n_heads < 1 || n_tokens < 1 || head_dim < 32 || head_dim % kGroup || b_hi < b_lo) return 0;
+  const size_t groups = (size_t)n_tokens * head_dim / kGroup;
+  return align_up((size_t)n_heads * (b_hi - b_lo + 1) * groups * 8) + kAlign;
+}
+
+kvq_status kvq_calibrate_fit(const void* x_dev, int32_t dtype, int32_t n_heads, int32_t n_tokens,
+                             int32_t head_dim, int32_t axis, int32_t quant, int32_t b_lo,
+                             int32_t b_hi, void* ws, size_t ws_bytes, double* alpha,
+                             double* beta, double* r2, void* stream) {
+  if (!x_dev || !ws || !alpha || !beta || !r2) return fail(KVQ_ERR_ARG, "NULL pointer");
+  if (dtype != KVQ_F16 && dtype != KVQ_BF16) return fail(KVQ_ERR_ARG, "bad dtype");
+  if (n_heads < 1 || n_tokens < 1) return fail(KVQ_ERR_ARG, "n_heads and n_tokens must be >= 1");
+  if (head_dim < 32 || head_dim % kGroup || head_dim > 4096)
+    return fail(KVQ_ERR_ARG, "head_dim must be a multiple of 32");
+  if (axis != KVQ_AXIS_KEY && axis != KVQ_AXIS_VALUE) return fail(KVQ_ERR_ARG, "bad axis");
+  if (axis == KVQ_AXIS_VALUE && n_tokens % kGroup)
+    return fail(KVQ_ERR_ARG, "value calibration needs n_tokens % 32 == 0");
+  if (quant != KVQ_QUANT_ASYM && quant != KVQ_QUANT_HYBRID) return fail(KVQ_ERR_ARG, "bad quant");
+  if (!(2 <= b_lo && b_lo + 2 <= b_hi && b_hi <= 8)) return fail(KVQ_ERR_ARG, "need 2 <= b_lo, b_lo + 2 <= b_hi <= 8");
+  if (!aligned(x_dev, 16) || !aligned(ws, 256)) return fail(KVQ_ERR_ARG, "misaligned pointer");
+  const size_t need = kvq_calibrate_workspace_bytes(n_heads, n_tokens, head_dim, b_lo, b_hi);
+  if (ws_bytes < need) return fail(KVQ_ERR_ARG, "workspace too small");
+  const int nb = b_hi - b_lo + 1;
+  const int64_t groups = (int64_t)n_tokens * head_dim / kGroup;
+  CalibPlan p{};
+  p.x = x_dev;
+  p.sse = static_cast<double*>(ws);
+  p.range_flag = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + need - kAlign);
+  p.n_heads = n_heads;
+  p.n_tokens = n_tokens;
+  p.D = head_dim;
+  p.axis = axis;
+  p.hybrid = quant == KVQ_QUANT_HYBRID;
+  p.dtype = dtype;
+  p.b_lo = b_lo;
+  p.nb = nb;
+  p.n_groups = groups;
+  hipStream_t s = as_stream(stream);
+  hipError_t e = hipMemsetAsync(p.range_flag, 0, 4, s);
+  if (e != hipSuccess) return hip_fail(e, "calibrate flag clear");
+  kvq_status st = check_launch(launch_calib(p, stream), "calibrate launch");
+  if (st != KVQ_OK) return st;
+  std::vector<double> sse((size_t)n_heads * nb * groups);
+  uint32_t flag = 0;
+  e = hipMemcpyAsync(sse.data(), p.sse, sse.size() * 8, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(&flag, p.range_flag, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "calibrate copy-back");
+  if (flag) return fail(KVQ_ERR_RANGE, "calibration input non-finite or |x| > 2^14");
+  // D(b) = (sum of per-group SSE in group order) / element count
+  std::vector<double> D((size_t)n_heads * nb);
+  const double n_el = (double)n_tokens * head_dim;
+  for (int h = 0; h < n_heads; ++h)
+    for (int i = 0; i < nb; ++i) {
+      const double* g = sse.data() + ((size_t)h * nb + i) * groups;
+      double tot = 0.0;
+      for (int64_t k = 0; k < groups; ++k) tot = tot + g[k];
+      D[(size_t)h * nb + i] = tot / n_el;
+    }
+  return fit_distortion(n_heads, nb, D.data(), b_lo, alpha, beta, r2);
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// Internal declarations shared by the host side and the kernel launchers of libkvq.
+// Not part of the public ABI (see include/kvq.h).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int kGroup = 32;        // quantization group size (keys: channels, values: tokens)
+constexpr int kTile = 64;         // body tokens per key tile (one wavefront, one token per lane)
+constexpr int kRegions = 9;
+constexpr uint64_t kAlign = 256;  // every region starts on a 256-byte boundary
+constexpr uint64_t kHeaderBytes = 256;
+constexpr uint32_t kMagic = 0x3151564Bu;  // "KVQ1"
+constexpr float kRangeLimit = 16384.0f;   // |x| <= 2^14 for quantized heads
+
+enum Region { KC = 0, KM, VC, VM, FL, SK, SV, RK, RV };
+
+// Blob header (first 256 bytes of every cache blob). The region table follows it.
+struct BlobHeader {
+  uint32_t magic;
+  uint32_t version;
+  uint32_t range_flag;   // sticky: set by the device when a quantized input is out of range
+  uint32_t n_regions;
+  int32_t batch, n_kv_heads, head_dim, capacity;
+  uint64_t table_offset; // byte offset of uint64 off[batch][n_kv_heads][kRegions]
+  uint64_t total_bytes;
+};
+
+inline uint64_t align_up(uint64_t x, uint64_t a = kAlign) { return (x + a - 1) / a * a; }
+
+// Tokens quantized into the body after T tokens: whole 32-token blocks that have left the
+// recent window (the window then holds n_recent..n_recent+31 tokens).
+inline int64_t body_len(int64_t T, int64_t n_sink, int64_t n_recent) {
+  int64_t r = T - n_sink - n_recent;
+  return r <= 0 ? 0 : (r / kGroup) * kGroup;
+}
+inline int ring_slots(int n_recent) { return n_recent + kGroup; }
+
+// Sizes of the 9 regions of one (row, KV head).
+void region_sizes(const kvq_config& cfg, int kv_head, uint64_t sz[kRegions]);
+// Full layout: off[(row*H + head)*9 + region], returns the total blob size.
+uint64_t plan_layout(const kvq_config& cfg, uint64_t* off /* nullable */);
+
+// Validation (sets the error string and returns a status).
+kvq_status check_config(const kvq_config* cfg);
+
+// Error handling.
+void set_error(const std::string& msg);
+kvq_status fail(kvq_status st, const std::string& msg);
+const char* last_error();
+
+// Host algorithms (kvq_host.cpp).
+kvq_status fit_distortion(int n_heads, int nb, const double* D /*[n_heads][nb]*/, int b_lo,
+                          double* alpha, double* beta, double* r2);
+
+// ---------------------------------------------------------------------------------------
+// Kernel launchers (device code in *.hip). All return hipError_t as int.
+// ---------------------------------------------------------------------------------------
+
+// Parameters of one append launch, computed on the host.
+struct AppendPlan {
+  const void* k_in;      // [B][H][n_new][D]
+  const void* v_in;
+  char* blob;            // device blob base
+  const uint64_t* off;   // device region table
+  uint32_t* range_flag;  // device sticky flag
+  int B, H, D, n_new;
+  int len0, len1;        // token counts before / after
+  int body0, body1;      // body lengths before / after
+  int n_sink, n_recent;
+  int dtype, hybrid;
+  uint8_t k_bits[KVQ_MAX_KV_HEADS];
+  uint8_t v_bits[KVQ_MAX_KV_HEADS];
+};
+int launch_append_flush(const AppendPlan& p, void* stream);
+int launch_append_window(const AppendPlan& p, void* stream);
+
+struct CalibPlan {
+  const void* x;          // [n_heads][n_tokens][D]
+  double* sse;            // [n_heads][nb][n_groups]
+  uint32_t* range_flag;   // device
+  int n_heads, n_tokens, D, axis, hybrid, dtype, b_lo, nb;
+  int64_t n_groups;
+};
+int launch_calib(const CalibPlan& p, void* stream);
+
+struct DecodePlan {
+  const char* blob;
+  const uint64_t* off;
+  const void* q;         // [B][Hq][D]
+  float* out;            // [B][Hq][D]
+  float* ws_o;           // [P][B][Hq][D]
+  float* ws_ml;          // [P][B][Hq][2]
+  int B, H, Hq, G, D, T, body, n_sink_live, n_win, n_sink_cfg, ring;
+  int n_splits, tiles_per_split, n_tiles;
+  int dtype;
+  float scale_log2;      // softmax scale times log2(e)
+  uint8_t k_bits[KVQ_MAX_KV_HEADS];
+  uint8_t v_bits[KVQ_MAX_KV_HEADS];
+};
+int launch_decode(const DecodePlan& p, void* stream);
+
+}  // namespace kvq

@@ -1,0 +1,139 @@
+// Device-side group quantizer shared by the append and calibration kernels.
+//
+// One thread quantizes one group of 32 values (keys: 32 channels of a token; values: 32
+// tokens of a channel — grouping along the inner dimension, InnerQ "Core claim").
+// Every step is an IEEE operation in the order written; this file must be compiled with
+// -ffp-contract=off so that no multiply-add is fused:
+//   asymmetric: s = f16(fl32(max - min) / fl32(2^b - 1)), z = f16(min + 0),
+//               c = clamp(rint(fl32(fl32(x - z) * fl32(1/s))), 0, 2^b - 1)  (s == 0: c = 0)
+//   symmetric:  s = f16(fl32(max|x|) / fl32(2^(b-1) - 1)), z = -2^(b-1) s,
+//               c = clamp(rint(fl32(x * fl32(1/s))), -(2^(b-1)-1), 2^(b-1)-1) + 2^(b-1)
+//   both dequantize as x_hat = c s + z; hybrid (InnerQ technique (i)) keeps the variant
+//   whose float64 squared error (summed over elements 0..31 in order) is strictly lower,
+//   ties to asymmetric.
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+__device__ __forceinline__ float widen16(uint16_t raw, int dtype) {
+  if (dtype == KVQ_BF16) return __uint_as_float((uint32_t)raw << 16);
+  return __half2float(__ushort_as_half(raw));
+}
+
+__device__ __forceinline__ uint16_t f16_bits(float x) {  // round to nearest even
+  return __half_as_ushort(__float2half_rn(x));
+}
+__device__ __forceinline__ float f16_value(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+
+struct GroupQ {
+  float s, z, r;        // stored s, z as float; r = fl32(1 / s)
+  uint16_t s_bits, z_bits;
+  float lo, hi;         // clamp range of rint(t)
+  int add;              // code = clamped value + add
+  bool sym, zero;       // zero: s == 0 (every code is the zero level)
+};
+
+__device__ __forceinline__ GroupQ asym_params(const float (&x)[32], int b) {
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) {
+    mn = fminf(mn, x[i]);
+    mx = fmaxf(mx, x[i]);
+  }
+  GroupQ q;
+  const float L = (float)((1 << b) - 1);
+  q.s_bits = f16_bits((mx - mn) / L);
+  q.z_bits = f16_bits(mn + 0.0f);  // + 0 stores a zero minimum as +0 whatever its sign
+  q.s = f16_value(q.s_bits);
+  q.z = f16_value(q.z_bits);
+  q.zero = (q.s == 0.0f);
+  q.r = 1.0f / q.s;
+  q.lo = 0.0f;
+  q.hi = L;
+  q.add = 0;
+  q.sym = false;
+  return q;
+}
+
+__device__ __forceinline__ GroupQ sym_params(const float (&x)[32], int b) {
+  float m = fabsf(x[0]);
+#pragma unroll
+  for (int i = 1; i < 32; ++i) m = fmaxf(m, fabsf(x[i]));
+  GroupQ q;
+  const int half = 1 << (b - 1);
+  const float Q = (float)(half - 1);
+  q.s_bits = f16_bits(m / Q);
+  q.s = f16_value(q.s_bits);
+  q.z_bits = f16_bits(-(float)half * q.s);  // exact: power-of-two multiple of an fp16 value
+  q.z = f16_value(q.z_bits);
+  q.zero = (q.s == 0.0f);
+  q.r = 1.0f / q.s;
+  q.lo = -Q;
+  q.hi = Q;
+  q.add = half;
+  q.sym = true;
+  return q;
+}
+
+__device__ __forceinline__ int code_of(float x, const GroupQ& q) {
+  if (q.zero) return q.sym ? q.add : 0;
+  const float t = q.sym ? x * q.r : (x - q.z) * q.r;
+  const float c = fminf(fmaxf(rintf(t), q.lo), q.hi);
+  return (int)c + q.add;
+}
+
+// sum_i (x_i - (c_i s + z))^2 in float64, elements in order, no fused multiply-add
+__device__ __forceinline__ double group_sse(const float (&x)[32], const GroupQ& q) {
+  const double s = (double)q.s, z = (double)q.z;
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const double xh = (double)code_of(x[i], q) * s + z;
+    const double d = (double)x[i] - xh;
+    const double sq = d * d;
+    acc = acc + sq;
+  }
+  return acc;
+}
+
+// Quantizer for one group: asymmetric, or the hybrid choice.
+__device__ __forceinline__ GroupQ choose_quant(const float (&x)[32], int b, bool hybrid) {
+  GroupQ a = asym_params(x, b);
+  if (!hybrid) return a;
+  GroupQ s = sym_params(x, b);
+  const double ea = group_sse(x, a);
+  const double es = group_sse(x, s);
+  return es < ea ? s : a;
+}
+
+__device__ __forceinline__ bool out_of_range(const float (&x)[32]) {
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) bad |= !(fabsf(x[i]) <= 16384.0f);  // also catches NaN
+  return bad;
+}
+
+// Pack the 32 codes of a group into b little-endian words (code i at stream bits
+// [i*b, i*b+b)) and hand each finished word to store(word_index, word).
+template <class Store>
+__device__ __forceinline__ void pack_group(const float (&x)[32], const GroupQ& q, int b, Store store) {
+  uint64_t acc = 0;
+  int nbits = 0, w = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    acc |= (uint64_t)(uint32_t)code_of(x[i], q) << nbits;
+    nbits += b;
+    if (nbits >= 32) {
+      store(w, (uint32_t)acc);
+      ++w;
+      acc >>= 32;
+      nbits -= 32;
+    }
+  }
+}
+
+}  // namespace kvq

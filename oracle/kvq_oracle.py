@@ -75,7 +75,8 @@ def f16(x) -> np.ndarray:
 def quant_asym(x: np.ndarray, b: int):
     """Asymmetric min/max quantizer of the last axis (length 32), b bits.
 
-    s = f16(fl32(max - min) / fl32(2^b - 1)), z = f16(min); codes are the nearest level of
+    s = f16(fl32(max - min) / fl32(2^b - 1)), z = f16(min + 0) (a zero minimum is stored
+    as +0 whatever its sign); codes are the nearest level of
     (x - z) / s computed as fl32(fl32(x - z) * fl32(1 / s)), ties to even, clamped to
     [0, 2^b - 1]; s == 0 gives all-zero codes.  Dequantization: x_hat = c * s + z.
     Returns (codes uint8 [..., 32], s float16 [...], z float16 [...]).
@@ -85,7 +86,7 @@ def quant_asym(x: np.ndarray, b: int):
     mn = x.min(axis=-1)
     mx = x.max(axis=-1)
     s = f16((mx - mn) / L)
-    z = f16(mn)
+    z = f16(mn + np.float32(0.0))   # + 0 stores a zero minimum as +0 whatever its sign
     s32 = s.astype(np.float32)
     z32 = z.astype(np.float32)
     with np.errstate(divide="ignore", invalid="ignore"):
@@ -540,9 +541,15 @@ def allocate_continuous(alpha, beta, w, total, b_lo, b_hi, cap=False, tol=1e-13)
         return [b_lo if ci == -math.inf else min(b_hi, max(b_lo, (ci - theta) / li))
                 for ci, li in zip(c, lb)]
 
-    fin = [ci for ci in c if ci != -math.inf]
-    if total == n * b_lo or not fin:
-        return [float(b_lo)] * n if total == n * b_lo else bits_at(0.0)
+    # Heads with alpha = 0 have no distortion to remove; like the greedy form they take bits
+    # only once every other head is at b_hi, the remainder shared evenly among them.
+    n_deg = sum(1 for ci in c if ci == -math.inf)
+    full = sum(b_hi for ci in c if ci != -math.inf) + n_deg * b_lo
+    if total >= full:
+        extra = (total - full) / n_deg if n_deg else 0.0
+        return [float(b_hi) if ci != -math.inf else b_lo + extra for ci in c]
+    if total == n * b_lo:
+        return [float(b_lo)] * n
     lo = min(ci - b_hi * li for ci, li in zip(c, lb) if ci != -math.inf) - 1.0
     hi = max(ci - b_lo * li for ci, li in zip(c, lb) if ci != -math.inf) + 1.0
     for _ in range(400):

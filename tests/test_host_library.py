@@ -1,0 +1,152 @@
+"""CPU tests of libkvq's host side through its C ABI: exported symbols, the bit allocator
+(bit-exact against the oracle), the layout planner (against the oracle's layout) and the
+documented error statuses. No GPU is touched: these calls never enqueue device work."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import mixed_precision_quantized_kvq_amd as kvq
+import workloads
+from oracle import kvq_oracle as O
+from tests.kvq_test_util import lib_cfg, oracle_bits, oracle_cfg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _header_functions()
+    assert len(names) == 11
+    assert sorted(kvq.EXPORTS) == names
+    L = ctypes.CDLL(kvq.lib_path())
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", kvq.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (kvq_\w+)", out))
+    assert set(names) <= exported
+
+
+def _rand_model(rng, n):
+    return (list(rng.uniform(0.5, 2.0, n)), list(rng.uniform(3.6, 5.3, n)),
+            list(rng.lognormal(0.0, 1.0, n)))
+
+
+def test_allocate_bits_bit_exact_vs_oracle():
+    rng = np.random.default_rng(21)
+    for trial in range(400):
+        n = int(rng.integers(1, 40))
+        b_lo, b_hi = [(2, 4), (2, 8), (3, 6), (2, 2)][trial % 4]
+        total = int(rng.integers(n * b_lo, n * b_hi + 1))
+        a, bt, w = _rand_model(rng, n)
+        if trial % 7 == 0:
+            a[0] = 0.0                         # an exactly representable head
+        cap = trial % 5 == 0
+        got, cont = kvq.allocate_bits(a, bt, w, total, b_lo, b_hi, cap=cap)
+        want = O.allocate_greedy(a, bt, w, total, b_lo, b_hi, cap=cap)
+        assert got == want
+        wc = O.allocate_continuous(a, bt, w, total, b_lo, b_hi, cap=cap)
+        assert max(abs(x - y) for x, y in zip(cont, wc)) < 1e-8
+        assert abs(sum(cont) - total) < 1e-8
+
+
+def test_allocate_bits_workloads():
+    for name in ("llama8b_t8k", "qwen8b_t32k"):
+        w = workloads.make(name, tokens=64, batch=1)
+        s = w["spec"]
+        kb, vb = oracle_bits(w)
+        if s.alloc == "joint":
+            got, _ = kvq.allocate_bits(w["alpha"], w["beta"], w["w"], s.k_total, 2, 4)
+            assert tuple(got) == kb == vb and sum(got) == 20
+        else:
+            gk, _ = kvq.allocate_bits(w["alpha_k"], w["beta_k"], w["w_k"], s.k_total, 2, 4)
+            gv, _ = kvq.allocate_bits(w["alpha_v"], w["beta_v"], w["w_v"], s.v_total, 2, 4)
+            assert tuple(gk) == kb and tuple(gv) == vb == (2,) * 8 and sum(gk) == 24
+
+
+def test_allocate_bits_errors():
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.allocate_bits([1.0] * 4, [4.0] * 4, [1.0] * 4, 7, 2, 4)
+    assert e.value.status == -2
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.allocate_bits([1.0] * 4, [4.0] * 4, [1.0] * 4, 17, 2, 4)
+    assert e.value.status == -2
+    for bad in (dict(beta=[1.0] * 4), dict(w=[0.0] * 4), dict(alpha=[-1.0] * 4),
+                dict(alpha=[float("nan")] * 4)):
+        args = dict(alpha=[1.0] * 4, beta=[4.0] * 4, w=[1.0] * 4)
+        args.update(bad)
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.allocate_bits(args["alpha"], args["beta"], args["w"], 12, 2, 4)
+        assert e.value.status == -1
+    with pytest.raises(kvq.KvqError):
+        kvq.allocate_bits([1.0] * 4, [4.0] * 4, [1.0] * 4, 12, 1, 4)
+
+
+def _configs():
+    out = []
+    for name in workloads.WORKLOADS:
+        w = workloads.make(name, tokens=64, batch=1)
+        s = w["spec"]
+        kb = vb = (2,) * s.n_kv if s.alloc != "fixed" else s.fixed_bits
+        if s.alloc == "separate":
+            kb = (2, 3, 4, 3, 3, 4, 2, 3)
+        for B, cap in ((1, s.tokens), (3, 1000)):
+            out.append(oracle_cfg(w, kb, vb, capacity=cap, batch=B))
+    out.append(O.CacheConfig(2, 3, 6, 64, 777, 0, 0, "fp16", "hybrid", (16, 2, 8), (5, 16, 7)))
+    out.append(O.CacheConfig(1, 2, 2, 128, 50, 4, 128, "bf16", "asym", (3, 3), (3, 3)))
+    return out
+
+
+@pytest.mark.parametrize("ocfg", _configs(), ids=lambda c: f"B{c.batch}H{c.n_kv}D{c.head_dim}cap{c.capacity}")
+def test_layout_matches_oracle(ocfg):
+    cfg = lib_cfg(kvq, ocfg)
+    off, total = O.layout(ocfg)
+    assert kvq.cache_bytes(cfg) == total
+    for b in range(ocfg.batch):
+        for h in range(ocfg.n_kv):
+            sz = O.region_sizes(ocfg, h)
+            for r in range(O.N_REGIONS):
+                got = kvq.region_offset(cfg, b, h, r)
+                assert got == (int(off[b, h, r]), sz[r])
+
+
+def test_layout_regions_disjoint_and_aligned():
+    ocfg = O.CacheConfig(2, 8, 32, 128, 32768, 4, 128, "bf16", "hybrid", (2, 3, 4, 3, 3, 4, 2, 3), (2,) * 8)
+    off, total = O.layout(ocfg)
+    spans = []
+    for b in range(2):
+        for h in range(8):
+            for r, s in enumerate(O.region_sizes(ocfg, h)):
+                spans.append((int(off[b, h, r]), s))
+    spans.sort()
+    assert spans[0][0] >= 256 + 2 * 8 * 9 * 8
+    for (o1, s1), (o2, _) in zip(spans, spans[1:]):
+        assert o1 % 256 == 0 and o1 + s1 <= o2
+    assert spans[-1][0] + spans[-1][1] <= total
+
+
+def test_config_errors():
+    base = dict(batch=1, n_kv_heads=2, n_q_heads=4, head_dim=64, capacity=100, n_sink=1,
+                n_recent=8, dtype="fp16", quant="asym", k_bits=(2, 4), v_bits=(2, 4))
+    bad = [dict(batch=0), dict(n_q_heads=3), dict(head_dim=96), dict(capacity=0), dict(n_sink=-1),
+           dict(k_bits=(1, 4)), dict(v_bits=(9, 4)), dict(n_q_heads=20)]
+    for b in bad:
+        args = dict(base)
+        args.update(b)
+        cfg = kvq.Config.make(**args)
+        with pytest.raises(kvq.KvqError):
+            kvq.cache_bytes(cfg)
+        assert kvq.last_error()
+    cfg = kvq.Config.make(**base)
+    cfg.group = 16
+    with pytest.raises(kvq.KvqError):
+        kvq.cache_bytes(cfg)
