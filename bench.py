@@ -148,17 +148,20 @@ def main():
             for _ in range(n_new)]
     q = torch.from_numpy(w["q"].view(np.int16)).to(dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    ws = torch.empty(kvq.decode_workspace_bytes(caches[0], s.n_splits) * 2, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(kvq.decode_workspace_bytes(caches[0], s.n_splits) * 2, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(i, evs=None):
+        # one decode step = append the new token + split-K decode + merge (the two launches of
+        # decode_attention, called apart so that events bracket the split-K kernel alone)
         c = caches[i % len(caches)]
         kvq.append(c, newk[i % n_new], newv[i % n_new], stream=stream)
         if evs is not None:
             evs[0].record(stream)
-        kvq.decode_attention(c, q, out, s.n_splits, ws, stream=stream)
+        kvq.decode_splitk(c, q, s.n_splits, ws, stream=stream)
         if evs is not None:
             evs[1].record(stream)
+        kvq.decode_merge(c, out, s.n_splits, ws, stream=stream)
         return c.len
 
     for i in range(args.warmup):
@@ -200,7 +203,7 @@ def main():
                    "step": "append 1 token + split-K decode + LSE merge"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode call (split-K decode + merge), HIP events around each call",
+                     "kernel": "decode_kernel (split-K fused-dequant decode), HIP events around each launch",
                      "bytes_per_launch": nbytes, "avg_us": dec_us},
         "offline": {"allocate_bits_us": alloc_us, "calibrate_fit_ms_k_plus_v": calib_ms,
                     "prefill_append_ms": float(np.median(prefill_ms)),

@@ -18,7 +18,8 @@ import os
 __all__ = [
     "KvqError", "Config", "KVCache", "lib", "lib_path", "cache_bytes", "cache_init",
     "calibrate_fit", "calibrate_workspace_bytes", "allocate_bits", "append",
-    "decode_workspace_bytes", "decode_attention", "cache_check", "region_offset", "last_error",
+    "decode_workspace_bytes", "decode_attention", "decode_splitk", "decode_merge", "cache_check",
+    "region_offset", "last_error",
     "F16", "BF16", "QUANT_ASYM", "QUANT_HYBRID", "AXIS_KEY", "AXIS_VALUE", "ALLOC_CAP_W",
     "EXPORTS",
 ]
@@ -36,7 +37,8 @@ STATUS = {0: "OK", -1: "ERR_ARG", -2: "ERR_BUDGET", -3: "ERR_CAPACITY", -4: "ERR
 
 EXPORTS = ("kvq_cache_bytes", "kvq_cache_init", "kvq_calibrate_workspace_bytes",
            "kvq_calibrate_fit", "kvq_allocate_bits", "kvq_append", "kvq_decode_workspace_bytes",
-           "kvq_decode_attention", "kvq_cache_check", "kvq_region_offset", "kvq_last_error")
+           "kvq_decode_attention", "kvq_decode_splitk", "kvq_decode_merge", "kvq_cache_check",
+           "kvq_region_offset", "kvq_last_error")
 
 
 class KvqError(RuntimeError):
@@ -104,6 +106,8 @@ def lib():
             "kvq_append": (I32, [KP, P, P, I32, P]),
             "kvq_decode_workspace_bytes": (SZ, [KP, I32]),
             "kvq_decode_attention": (I32, [KP, P, P, I32, ctypes.c_float, P, SZ, P]),
+            "kvq_decode_splitk": (I32, [KP, P, I32, ctypes.c_float, P, SZ, P]),
+            "kvq_decode_merge": (I32, [KP, P, I32, P, SZ, P]),
             "kvq_cache_check": (I32, [KP, P]),
             "kvq_region_offset": (U64, [CP, I32, I32, I32, ctypes.POINTER(U64)]),
             "kvq_last_error": (ctypes.c_char_p, []),
@@ -223,6 +227,25 @@ def decode_attention(cache: KVCache, q, out, n_splits: int, workspace, scale: fl
     _check(lib().kvq_decode_attention(ctypes.byref(cache.handle), _dptr(q), _dptr(out), int(n_splits),
                                       float(scale), _dptr(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream)))
+
+
+def decode_splitk(cache: KVCache, q, n_splits: int, workspace, scale: float = 0.0, stream=None):
+    """First launch of decode_attention: the split partials, written into `workspace`."""
+    c = cache.cfg
+    assert q.is_contiguous() and tuple(q.shape) == (c.batch, c.n_q_heads, c.head_dim)
+    _check(lib().kvq_decode_splitk(ctypes.byref(cache.handle), _dptr(q), int(n_splits), float(scale),
+                                   _dptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)))
+
+
+def decode_merge(cache: KVCache, out, n_splits: int, workspace, stream=None):
+    """Second launch of decode_attention: log-sum-exp merge of the partials into `out`."""
+    import torch
+    c = cache.cfg
+    assert out.is_contiguous() and out.dtype == torch.float32
+    assert tuple(out.shape) == (c.batch, c.n_q_heads, c.head_dim)
+    _check(lib().kvq_decode_merge(ctypes.byref(cache.handle), _dptr(out), int(n_splits), _dptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def cache_check(cache: KVCache, stream=None):

@@ -161,8 +161,8 @@ kvq_status kvq_append(kvq_cache* cache, const void* k_dev, const void* v_dev, in
 
 size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t n_splits) {
   if (check_cache(cache) != KVQ_OK) return 0;
-  if (n_splits < 1 || n_splits > 1024) {
-    set_error("n_splits must be in 1..1024");
+  if (n_splits < 1 || n_splits > 256) {
+    set_error("n_splits must be in 1..256");
     return 0;
   }
   const kvq_config& c = cache->cfg;
@@ -171,21 +171,25 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t n_splits) {
   return align_up(parts * rows * c.head_dim * 4) + align_up(parts * rows * 2 * 4);
 }
 
-kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q_dev, float* out_dev,
-                                int32_t n_splits, float scale, void* ws, size_t ws_bytes,
-                                void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the decode entry points; fills the launch plan.
+kvq_status decode_plan(const kvq_cache* cache, const void* q_dev, float* out_dev, int32_t n_splits, float scale,
+                       void* ws, size_t ws_bytes, DecodePlan& p) {
   kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
   if (cache->len < 1) return fail(KVQ_ERR_ARG, "decode on an empty cache");
-  if (!q_dev || !out_dev || !ws) return fail(KVQ_ERR_ARG, "NULL pointer");
-  if (n_splits < 1 || n_splits > 1024) return fail(KVQ_ERR_ARG, "n_splits must be in 1..1024");
-  if (!aligned(q_dev, 16) || !aligned(out_dev, 16) || !aligned(ws, 256))
+  if (!ws) return fail(KVQ_ERR_ARG, "NULL workspace");
+  if (n_splits < 1 || n_splits > 256) return fail(KVQ_ERR_ARG, "n_splits must be in 1..256");
+  if ((q_dev && !aligned(q_dev, 16)) || (out_dev && !aligned(out_dev, 16)) || !aligned(ws, 256))
     return fail(KVQ_ERR_ARG, "q/out must be 16-byte and workspace 256-byte aligned");
   if (!(std::isfinite(scale))) return fail(KVQ_ERR_ARG, "scale must be finite");
   const size_t need = kvq_decode_workspace_bytes(cache, n_splits);
   if (ws_bytes < need) return fail(KVQ_ERR_ARG, "workspace too small");
   const kvq_config& c = cache->cfg;
-  DecodePlan p{};
+  p = DecodePlan{};
   p.blob = static_cast<const char*>(cache->dev);
   p.off = table_ptr(cache);
   p.q = q_dev;
@@ -213,7 +217,41 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q_dev, float
   p.scale_log2 = s * 1.4426950408889634f;
   std::memcpy(p.k_bits, c.k_bits, sizeof(p.k_bits));
   std::memcpy(p.v_bits, c.v_bits, sizeof(p.v_bits));
-  return check_launch(launch_decode(p, stream), "decode launch");
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_decode_splitk(const kvq_cache* cache, const void* q_dev, int32_t n_splits, float scale,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (!q_dev) return fail(KVQ_ERR_ARG, "NULL q");
+  DecodePlan p;
+  kvq_status st = decode_plan(cache, q_dev, nullptr, n_splits, scale, ws, ws_bytes, p);
+  if (st != KVQ_OK) return st;
+  return check_launch(launch_decode_splitk(p, stream), "decode launch");
+}
+
+kvq_status kvq_decode_merge(const kvq_cache* cache, float* out_dev, int32_t n_splits, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!out_dev) return fail(KVQ_ERR_ARG, "NULL out");
+  DecodePlan p;
+  kvq_status st = decode_plan(cache, nullptr, out_dev, n_splits, 0.0f, ws, ws_bytes, p);
+  if (st != KVQ_OK) return st;
+  return check_launch(launch_decode_merge(p, stream), "merge launch");
+}
+
+kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q_dev, float* out_dev,
+                                int32_t n_splits, float scale, void* ws, size_t ws_bytes,
+                                void* stream) {
+  if (!q_dev || !out_dev) return fail(KVQ_ERR_ARG, "NULL pointer");
+  DecodePlan p;
+  kvq_status st = decode_plan(cache, q_dev, out_dev, n_splits, scale, ws, ws_bytes, p);
+  if (st != KVQ_OK) return st;
+  st = check_launch(launch_decode_splitk(p, stream), "decode launch");
+  if (st != KVQ_OK) return st;
+  return check_launch(launch_decode_merge(p, stream), "merge launch");
 }
 
 size_t kvq_calibrate_workspace_bytes(int32_t n_heads, int32_t n_tokens, int32_t head_dim,

@@ -104,6 +104,7 @@ struct DecodePlan {
   uint8_t k_bits[KVQ_MAX_KV_HEADS];
   uint8_t v_bits[KVQ_MAX_KV_HEADS];
 };
-int launch_decode(const DecodePlan& p, void* stream);
+int launch_decode_splitk(const DecodePlan& p, void* stream);
+int launch_decode_merge(const DecodePlan& p, void* stream);
 
 }  // namespace kvq

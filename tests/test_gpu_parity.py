@@ -62,7 +62,7 @@ def assert_regions_equal(cache, oc, rows=None, heads=None, map_bh=lambda b, h: (
 def gpu_decode(cache, q, n_splits, scale=0.0):
     c = cache.cfg
     out = torch.empty((c.batch, c.n_q_heads, c.head_dim), dtype=torch.float32, device=DEV)
-    ws = torch.empty(kvq.decode_workspace_bytes(cache, n_splits), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(kvq.decode_workspace_bytes(cache, n_splits), dtype=torch.uint8, device=DEV)
     kvq.decode_attention(cache, to_dev(q), out, n_splits, ws, scale=scale)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64)
@@ -246,7 +246,7 @@ def test_abi_errors_enqueue_nothing():
     assert e.value.status == -3 and cache.len == 0
     q = torch.zeros((1, 1, 64), dtype=torch.int16, device=DEV)
     out = torch.zeros((1, 1, 64), dtype=torch.float32, device=DEV)
-    ws = torch.empty(1 << 16, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8, device=DEV)
     with pytest.raises(kvq.KvqError) as e:
         kvq.decode_attention(cache, q, out, 1, ws)       # empty cache
     assert e.value.status == -1

@@ -1,0 +1,28 @@
+"""CPU check of the decode kernel's code-unpack plans (host logic, no GPU).
+
+The decode kernel feeds b-bit codes to the MFMA as fp16 subnormals cut out of the packed
+words with a shift and a mask per pair of codes. This compiles the kernel's own
+unpack_step / Slots templates for the host and checks, for every width 2..8, that slot k
+of step s holds code[chan(s, k)] << exp(s, k), inside the 10-bit mantissa, and that every
+element of a group is used exactly once.
+"""
+import os
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "mixed_precision_quantized_kvq_amd", "csrc")
+HIPCC = "/opt/rocm/bin/hipcc"
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
+def test_unpack_plans(tmp_path):
+    exe = tmp_path / "unpack_plans_check"
+    cmd = [HIPCC, "-std=c++20", "--offload-arch=gfx950", "-O1", "-I", os.path.join(ROOT, "include"),
+           "-I", CSRC, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           os.path.join(ROOT, "tests", "unpack_plans_check.hip"), "-o", str(exe)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.count("0 mismatches") == 7, r.stdout
