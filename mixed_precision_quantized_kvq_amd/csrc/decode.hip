@@ -36,7 +36,10 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxG = 4;
-constexpr int kEp = 14;  // softmax weights enter the value MFMA as p * 2^(kEp - e)
+constexpr int kEp = 11;  // softmax weights enter the value MFMA as p * 2^(kEp - e)
+// Lazy rescaling: the running max m moves only when a score exceeds it by more than kTau
+// (log2 units), so weights stay below 2^kTau and p * 2^kEp * 2^kTau fits fp16.
+constexpr float kTau = 4.0f;
 constexpr int kMaxParts = 257;  // n_splits <= 256 body partials + the window partial
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
@@ -223,10 +226,12 @@ __device__ __forceinline__ u32x2 ones_step(int s) {
 
 template <int D>
 struct Smem {
-  uint32_t qA[kMaxG][D / 2];             // key-MFMA A operand: fp16 q * 2^(Eq - e), slot order
-  uint32_t qW[kMaxG][D / 2];             // 16-bit-row A operand: q in the cache dtype
+  // rows of the 4 query slots are padded by 4 words so that the 4 distinct addresses of an
+  // operand read fall in different LDS banks
+  uint32_t qA[kMaxG][D / 2 + 4];         // key-MFMA A operand: fp16 q * 2^(Eq - e), slot order
+  uint32_t qW[kMaxG][D / 2 + 4];         // 16-bit-row A operand: q in the cache dtype
   float qsum[kMaxG][D / 32];             // sum of q over each key group, times the softmax scale
-  uint32_t pw[kWaves][2][kMaxG][2][16];  // per wave: hi/lo, query, block, 32 weight slots
+  uint32_t pw[kWaves][2][kMaxG][36];     // per wave: hi/lo, query, 2 blocks x 16 words (+4 pad)
   float red_o[kWaves][kMaxG][D];
   float red_m[kWaves][kMaxG];
   float red_l[kWaves][kMaxG];
@@ -248,14 +253,16 @@ __device__ __forceinline__ void softmax_tile(Smem<D>& sm, int wave, int lane, bo
 #pragma unroll
   for (int i = 0; i < kMaxG; ++i) {
     const float x = valid ? sc[i] : -INFINITY;
-    const float mt = wave_max(x);
-    const float mn = fmaxf(st.m[i], mt);
-    const float alpha = exp2f(st.m[i] - mn);
-    st.m[i] = mn;
-    st.l[i] *= alpha;
+    if (__ballot(x > st.m[i] + kTau)) {  // rare after the first tile: move the running max
+      const float mn = fmaxf(st.m[i], wave_max(x));
+      const float alpha = __builtin_amdgcn_exp2f(st.m[i] - mn);
+      st.m[i] = mn;
+      st.l[i] *= alpha;
 #pragma unroll
-    for (int h = 0; h < D / 64; ++h) o[i][h] *= alpha;
-    const float p = exp2f(x - mn) * pscl;
+      for (int h = 0; h < D / 64; ++h) o[i][h] *= alpha;
+    }
+    const float mn = st.m[i];
+    const float p = __builtin_amdgcn_exp2f(x - mn) * pscl;
     uint32_t hi, lo;
     if (bf16_weights) {
       hi = f2bf(p);
@@ -264,8 +271,8 @@ __device__ __forceinline__ void softmax_tile(Smem<D>& sm, int wave, int lane, bo
       hi = f2h(p);
       lo = f2h(p - h2f(hi));
     }
-    reinterpret_cast<uint16_t*>(&sm.pw[wave][0][i][jj][0])[ppos] = (uint16_t)hi;
-    reinterpret_cast<uint16_t*>(&sm.pw[wave][1][i][jj][0])[ppos] = (uint16_t)lo;
+    reinterpret_cast<uint16_t*>(&sm.pw[wave][0][i][16 * jj])[ppos] = (uint16_t)hi;
+    reinterpret_cast<uint16_t*>(&sm.pw[wave][1][i][16 * jj])[ppos] = (uint16_t)lo;
   }
   wave_lds_sync();
 }
@@ -372,8 +379,8 @@ __device__ __forceinline__ void value_phase(const Smem<D>& sm, int wave, const V
       for (int h = 0; h < D / 64; ++h) acc[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const u32x2 ahi = *reinterpret_cast<const u32x2*>(&sm.pw[wave][0][qi][jj][2 * s]);
-        const u32x2 alo = *reinterpret_cast<const u32x2*>(&sm.pw[wave][1][qi][jj][2 * s]);
+        const u32x2 ahi = *reinterpret_cast<const u32x2*>(&sm.pw[wave][0][qi][16 * jj + 2 * s]);
+        const u32x2 alo = *reinterpret_cast<const u32x2*>(&sm.pw[wave][1][qi][16 * jj + 2 * s]);
 #pragma unroll
         for (int h = 0; h < D / 64; ++h) {
           const u32x2 b = unpack_step<VB>(t.w[h], jj * VB, s);
@@ -465,8 +472,8 @@ __device__ __forceinline__ void value_phase_16(const Smem<D>& sm, int wave, int 
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const u32x2 ahi = *reinterpret_cast<const u32x2*>(&sm.pw[wave][0][qi][jj][2 * s]);
-      const u32x2 alo = *reinterpret_cast<const u32x2*>(&sm.pw[wave][1][qi][jj][2 * s]);
+      const u32x2 ahi = *reinterpret_cast<const u32x2*>(&sm.pw[wave][0][qi][16 * jj + 2 * s]);
+      const u32x2 alo = *reinterpret_cast<const u32x2*>(&sm.pw[wave][1][qi][16 * jj + 2 * s]);
 #pragma unroll
       for (int h = 0; h < D / 64; ++h) {
         const u32x2 b = u32x2{pk[s][h][0], pk[s][h][1]};
@@ -636,7 +643,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodePlan p) {
   __shared__ Smem<D> sm;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.G;
   const int kb = p.k_bits[h], vb = p.v_bits[h];
   const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)b * p.Hq + (size_t)h * G) * D;
