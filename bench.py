@@ -51,7 +51,7 @@ def decode_bytes(spec, k_bits, v_bits, T, n_splits):
         per_head += body * per_tok + win * D * 4
     rows = spec.batch * spec.n_q
     q = rows * D * 2
-    partials = (n_splits + 1) * rows * (D + 2) * 4
+    partials = n_splits * rows * (D + 2) * 4
     return spec.batch * per_head + q + partials
 
 

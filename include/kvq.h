@@ -129,8 +129,10 @@ kvq_status kvq_append(kvq_cache* cache, const void* k_dev, const void* v_dev, in
 
 /* Split-K decode attention for one query token per row (InnerQ Algorithm 1 structure).
  * q_dev: [batch][n_q_heads][head_dim] 16-bit; out_dev: [batch][n_q_heads][head_dim] fp32.
- * The body is cut into n_splits token chunks (1..256); the 16-bit windows form one more
- * partial; the partials (m, l, o) are merged by log-sum-exp. scale <= 0 means 1/sqrt(D).
+ * The 64-token tiles of each (row, KV head) -- the tiles of the 16-bit sink + recent
+ * windows first, then the packed body tiles -- are cut into n_splits (1..256) contiguous
+ * ranges; each range yields one partial (m, l, o) and the partials are merged by
+ * log-sum-exp. scale <= 0 means 1/sqrt(D).
  * workspace_dev: at least kvq_decode_workspace_bytes(cache, n_splits) bytes, 256-byte
  * aligned, holding the split partials between the decode and merge launches (no
  * initialization needed). Calls that share a workspace must not run concurrently.
@@ -141,7 +143,7 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q_dev, float
                                 size_t ws_bytes, void* stream);
 
 /* The two launches of kvq_decode_attention, for callers that schedule or time them apart:
- * kvq_decode_splitk writes the n_splits + 1 partials (m, l, o) of every query head into the
+ * kvq_decode_splitk writes the n_splits partials (m, l, o) of every query head into the
  * workspace; kvq_decode_merge combines them into out_dev. Same arguments and rules as
  * kvq_decode_attention; the merge must see the same cache, n_splits and workspace as the
  * split-K call before it on the stream. */

@@ -28,7 +28,8 @@ SOURCES = {
     "kvq_abi.cpp": EXACT,
     "append.hip": EXACT,
     "calib.hip": EXACT,
-    "decode.hip": [],
+    # MFMA accumulators in ordinary VGPRs: no accumulator-register copies in the decode loop
+    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -1,18 +1,22 @@
 // Split-K decode attention over the packed cache, dequantization fused into q.K^T and P.V
 // (InnerQ: grouping along the inner dimension of each vector-matrix product; the decode
-// structure of its "Algorithm 1 ... decode phase"), with the log-sum-exp merge of the split
-// partials done by the last workgroup of each (row, KV head).
+// structure of its "Algorithm 1 ... decode phase"); the log-sum-exp merge of the split
+// partials is a second, small kernel.
 //
-// Grid (n_splits + 1, KV heads, rows), 4 wavefronts per workgroup. Workgroup `split` <
-// n_splits owns a contiguous range of 64-token body tiles (wavefronts take tiles round-robin);
-// workgroup n_splits takes the 16-bit sink and recent-window tokens.
+// Grid (n_splits, KV heads, rows), 4 wavefronts per workgroup. The work of a (row, KV head)
+// is a list of 64-token units: first the tiles of the 16-bit sink + recent-window tokens,
+// then the packed body tiles. Workgroup `split` owns a contiguous range of units, so the
+// windows cost no workgroup of their own; its wavefronts take the window tiles, then the
+// body tiles, round-robin.
 //
 // Both products run on the 4x4x4 (16-block) f16/bf16 MFMA. Lane l belongs to block l/4 and
 // to row/column l%4, so with the G <= 4 query heads of a KV head as the 4-wide dimension:
 //   q.K^T  lane = token. B operand = 4 codes of the lane's token, A = the 4 matching q values
 //          of query l%4; output element i is query i's partial dot for that token.
-//   P.V    lane = channel. B operand = 4 tokens' codes of the lane's channel, A = the 4
-//          matching softmax weights of query l%4; output element i is query i's partial.
+//   P.V    lane = channel (for D = 128 the lane owns the adjacent channels 2l and 2l+1, one
+//          MFMA each, so its code words and 16-bit window values arrive in single loads).
+//          B operand = 4 tokens' codes of the channel, A = the 4 matching softmax weights
+//          of query l%4; output element i is query i's partial.
 // Codes enter the MFMA as fp16 subnormals: one shift and one AND of a packed word leave two
 // codes in the top mantissa bits of two fp16 halves, i.e. the values c * 2^(e - 24) (slot
 // plans below). The 2^e of each slot is divided out of the matching A value (q or p), so
@@ -40,7 +44,6 @@ constexpr int kEp = 11;  // softmax weights enter the value MFMA as p * 2^(kEp -
 // Lazy rescaling: the running max m moves only when a score exceeds it by more than kTau
 // (log2 units), so weights stay below 2^kTau and p * 2^kEp * 2^kTau fits fp16.
 constexpr float kTau = 4.0f;
-constexpr int kMaxParts = 257;  // n_splits <= 256 body partials + the window partial
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -228,10 +231,11 @@ template <int D>
 struct Smem {
   // rows of the 4 query slots are padded by 4 words so that the 4 distinct addresses of an
   // operand read fall in different LDS banks
-  uint32_t qA[kMaxG][D / 2 + 4];         // key-MFMA A operand: fp16 q * 2^(Eq - e), slot order
-  uint32_t qW[kMaxG][D / 2 + 4];         // 16-bit-row A operand: q in the cache dtype
-  float qsum[kMaxG][D / 32];             // sum of q over each key group, times the softmax scale
-  uint32_t pw[kWaves][2][kMaxG][36];     // per wave: hi/lo, query, 2 blocks x 16 words (+4 pad)
+  // (16-byte alignment lets operand reads use one ds_read_b64 with an immediate offset)
+  alignas(16) uint32_t qA[kMaxG][D / 2 + 4];      // key-MFMA A operand: fp16 q * 2^(Eq - e), slot order
+  alignas(16) uint32_t qW[kMaxG][D / 2 + 4];      // 16-bit-row A operand: q in the cache dtype
+  alignas(16) float qsum[kMaxG][D / 32];          // sum of q over each key group, times the softmax scale
+  alignas(16) uint32_t pw[kWaves][2][kMaxG][36];  // per wave: hi/lo, query, 2 blocks x 16 words (+4 pad)
   float red_o[kWaves][kMaxG][D];
   float red_m[kWaves][kMaxG];
   float red_l[kWaves][kMaxG];
@@ -292,54 +296,79 @@ struct VTile {
   uint32_t m[D / 64][2];
 };
 
+// Body regions read through buffer descriptors: each load is base (descriptor) + the lane's
+// fixed byte offset (a VGPR computed once) + the tile's byte offset (an SGPR). No address
+// register is rewritten per tile, so none can alias the destination of a load still in
+// flight, and an offset past the region returns zeros instead of faulting.
+struct BodySrc {
+  __amdgpu_buffer_rsrc_t kc, km, vc, vm;
+};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t region_rsrc(const char* blob, const uint64_t* off, int r) {
+  // 0x00020000: raw (untyped) buffer, 32-bit dwords
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(blob + off[r]), (short)0,
+                                           (int)(uint32_t)(off[r + 1] - off[r]), 0x00020000);
+}
+__device__ __forceinline__ BodySrc body_src(const DecodePlan& p, const uint64_t* off) {
+  return BodySrc{region_rsrc(p.blob, off, KC), region_rsrc(p.blob, off, KM), region_rsrc(p.blob, off, VC),
+                 region_rsrc(p.blob, off, VM)};
+}
+__device__ __forceinline__ void bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* d) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
+}
+__device__ __forceinline__ void bload2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* d) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+  d[0] = v[0]; d[1] = v[1];
+}
+
 template <int D, int KB>
-__device__ __forceinline__ void load_k(KTile<D, KB>& t, const uint32_t* kc, const uint32_t* km, int tile, int lane) {
+__device__ __forceinline__ void load_k(KTile<D, KB>& t, const BodySrc& src, int tile, int lane) {
   constexpr int W = KTile<D, KB>::W;
-  const uint32_t* base = kc + (size_t)tile * kTile * W;
+  const uint32_t soff = (uint32_t)tile * (kTile * W * 4);
 #pragma unroll
   for (int q = 0; q < (W + 3) / 4; ++q) {
     const int nq = (W - 4 * q) < 4 ? (W - 4 * q) : 4;  // 4, or 2 for the last chunk
-    const uint32_t* src = base + 256 * q + lane * nq;
-    if (nq == 4) {
-      const uint4 v = *reinterpret_cast<const uint4*>(src);
-      t.w[4 * q] = v.x; t.w[4 * q + 1] = v.y; t.w[4 * q + 2] = v.z; t.w[4 * q + 3] = v.w;
-    } else {
-      const uint2 v = *reinterpret_cast<const uint2*>(src);
-      t.w[4 * q] = v.x; t.w[4 * q + 1] = v.y;
-    }
+    const uint32_t voff = (uint32_t)(256 * q + lane * nq) * 4;
+    if (nq == 4)
+      bload4(src.kc, voff, soff, &t.w[4 * q]);
+    else
+      bload2(src.kc, voff, soff, &t.w[4 * q]);
   }
-  const uint32_t* mp = km + ((size_t)tile * kTile + lane) * (D / 32);
-  if constexpr (D == 128) {
-    const uint4 v = *reinterpret_cast<const uint4*>(mp);
-    t.m[0] = v.x; t.m[1] = v.y; t.m[2] = v.z; t.m[3] = v.w;
-  } else {
-    const uint2 v = *reinterpret_cast<const uint2*>(mp);
-    t.m[0] = v.x; t.m[1] = v.y;
-  }
+  const uint32_t msoff = (uint32_t)tile * (kTile * (D / 32) * 4), mvoff = (uint32_t)lane * (D / 32) * 4;
+  if constexpr (D == 128)
+    bload4(src.km, mvoff, msoff, t.m);
+  else
+    bload2(src.km, mvoff, msoff, t.m);
 }
 
 template <int D, int VB>
-__device__ __forceinline__ void load_v(VTile<D, VB>& t, const uint32_t* vc, const uint32_t* vm, int tile, int lane) {
+__device__ __forceinline__ void load_v(VTile<D, VB>& t, const BodySrc& src, int tile, int lane) {
+  // the lane's D/64 adjacent channels NH*lane .. NH*lane + NH-1: their code words (2 blocks of
+  // VB words each, channel after channel) and their (s|z) words are contiguous
+  constexpr int NH = D / 64, NW = NH * 2 * VB;
+  const uint32_t soff = (uint32_t)tile * (2 * D * VB * 4), voff = (uint32_t)lane * NW * 4;
+  uint32_t w[NW];
+  if constexpr (NW % 4 == 0) {
 #pragma unroll
-  for (int h = 0; h < D / 64; ++h) {
-    const int c = lane + 64 * h;
-    const uint32_t* src = vc + (size_t)tile * 2 * D * VB + (size_t)c * 2 * VB;
-    if constexpr (VB % 2 == 0) {
+    for (int x = 0; x < NW; x += 4) bload4(src.vc, voff + 4 * x, soff, &w[x]);
+  } else {
 #pragma unroll
-      for (int x = 0; x < 2 * VB; x += 4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src + x);
-        t.w[h][x] = v.x; t.w[h][x + 1] = v.y; t.w[h][x + 2] = v.z; t.w[h][x + 3] = v.w;
-      }
-    } else {
+    for (int x = 0; x < NW; x += 2) bload2(src.vc, voff + 4 * x, soff, &w[x]);
+  }
 #pragma unroll
-      for (int x = 0; x < 2 * VB; x += 2) {
-        const uint2 v = *reinterpret_cast<const uint2*>(src + x);
-        t.w[h][x] = v.x; t.w[h][x + 1] = v.y;
-      }
-    }
-    const uint2 mv = *reinterpret_cast<const uint2*>(vm + (size_t)tile * 2 * D + c * 2);
-    t.m[h][0] = mv.x;
-    t.m[h][1] = mv.y;
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int x = 0; x < 2 * VB; ++x) t.w[h][x] = w[h * 2 * VB + x];
+  const uint32_t msoff = (uint32_t)tile * (2 * D * 4), mvoff = (uint32_t)lane * NH * 2 * 4;
+  uint32_t m[2 * NH];
+  if constexpr (NH == 2)
+    bload4(src.vm, mvoff, msoff, m);
+  else
+    bload2(src.vm, mvoff, msoff, m);
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    t.m[h][0] = m[2 * h];
+    t.m[h][1] = m[2 * h + 1];
   }
 }
 
@@ -348,8 +377,6 @@ template <int D, int KB>
 __device__ __forceinline__ void key_phase(const Smem<D>& sm, const KTile<D, KB>& t, int lane, float kscale,
                                           float (&sc)[kMaxG]) {
   const int qi = lane & 3;
-#pragma unroll
-  for (int i = 0; i < kMaxG; ++i) sc[i] = 0.0f;
 #pragma unroll
   for (int g = 0; g < D / 32; ++g) {
     float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -361,7 +388,8 @@ __device__ __forceinline__ void key_phase(const Smem<D>& sm, const KTile<D, KB>&
     const float sg = h2f(t.m[g] & 0xFFFFu) * kscale;
     const float zg = h2f(t.m[g] >> 16);
 #pragma unroll
-    for (int i = 0; i < kMaxG; ++i) sc[i] += sg * acc[i] + zg * sm.qsum[i][g];
+    for (int i = 0; i < kMaxG; ++i)
+      sc[i] = __builtin_fmaf(sg, acc[i], g == 0 ? zg * sm.qsum[i][0] : __builtin_fmaf(zg, sm.qsum[i][g], sc[i]));
   }
 }
 
@@ -395,10 +423,10 @@ __device__ __forceinline__ void value_phase(const Smem<D>& sm, int wave, const V
       for (int h = 0; h < D / 64; ++h) {
         const float sv = h2f(t.m[h][jj] & 0xFFFFu) * kV, zv = h2f(t.m[h][jj] >> 16) * kV1;
 #pragma unroll
-        for (int i = 0; i < kMaxG; ++i) o[i][h] += sv * acc[h][i] + zv * acc1[i];
+        for (int i = 0; i < kMaxG; ++i) o[i][h] = __builtin_fmaf(sv, acc[h][i], __builtin_fmaf(zv, acc1[i], o[i][h]));
       }
 #pragma unroll
-      for (int i = 0; i < kMaxG; ++i) st.l[i] += acc1[i] * kV1;
+      for (int i = 0; i < kMaxG; ++i) st.l[i] = __builtin_fmaf(acc1[i], kV1, st.l[i]);
     }
   }
 }
@@ -432,6 +460,7 @@ __device__ __forceinline__ void key_phase_16(const Smem<D>& sm, const uint16_t* 
     uint4 x[8];
 #pragma unroll
     for (int v = 0; v < 8; ++v) x[v] = r4[part * 8 + v];
+    issue_barrier();  // all eight loads in flight before the first is used
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
       const int vv = part * 8 + v;
@@ -445,43 +474,60 @@ __device__ __forceinline__ void key_phase_16(const Smem<D>& sm, const uint16_t* 
   for (int i = 0; i < kMaxG; ++i) sc[i] = acc[i] * scale_log2;
 }
 
-// lane = channel; row_of(k) is the row of token k of the tile (k < n_valid)
-template <int D, bool BF16, class RowOf>
+// Value rows of one 64-token tile of 16-bit rows, both 32-token blocks: for token k the
+// lane's D/64 adjacent channels (one dword for D = 128, one 16-bit value for D = 64); tokens
+// past n_valid repeat the last valid row (their weights are zero). All loads are issued
+// before any is used.
+template <int D, class RowOf>
+__device__ __forceinline__ void load_v16(uint32_t (&vr)[2][32], int lane, int n_valid, RowOf row_of) {
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const uint16_t* r = row_of(min(jj * 32 + k, n_valid - 1));
+      if constexpr (D == 128)
+        vr[jj][k] = *reinterpret_cast<const uint32_t*>(r + 2 * lane);
+      else
+        vr[jj][k] = r[lane];
+    }
+}
+
+// fp16/bf16 pair (channel NH*lane + h of token a, same channel of token b)
+template <int H>
+__device__ __forceinline__ uint32_t pair16(uint32_t a, uint32_t b) {
+  return H == 0 ? __builtin_amdgcn_perm(b, a, 0x05040100u) : __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// lane = channel; P.V of one tile of 16-bit rows from the operands load_v16 fetched
+template <int D, bool BF16>
 __device__ __forceinline__ void value_phase_16(const Smem<D>& sm, int wave, int lane, int n_valid,
-                                               RowOf row_of, float (&o)[kMaxG][D / 64], WaveState& st) {
+                                               const uint32_t (&vr)[2][32], float (&o)[kMaxG][D / 64],
+                                               WaveState& st) {
   const int qi = lane & 3;
   const uint32_t one1 = BF16 ? 0x3F80u : 0x3C00u;
   const u32x2 one = u32x2{one1 | (one1 << 16), one1 | (one1 << 16)};
   float4_t acc[D / 64], acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int h = 0; h < D / 64; ++h) acc[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int jj = 0; jj * 32 < n_valid; ++jj) {
-    uint32_t pk[8][D / 64][2];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const uint16_t* r0 = row_of(min(jj * 32 + 4 * s + 0, n_valid - 1));
-      const uint16_t* r1 = row_of(min(jj * 32 + 4 * s + 1, n_valid - 1));
-      const uint16_t* r2 = row_of(min(jj * 32 + 4 * s + 2, n_valid - 1));
-      const uint16_t* r3 = row_of(min(jj * 32 + 4 * s + 3, n_valid - 1));
+  for (int jj = 0; jj < 2; ++jj) {
+    if (jj * 32 < n_valid) {
 #pragma unroll
-      for (int h = 0; h < D / 64; ++h) {
-        const int c = lane + 64 * h;
-        pk[s][h][0] = (uint32_t)r0[c] | ((uint32_t)r1[c] << 16);
-        pk[s][h][1] = (uint32_t)r2[c] | ((uint32_t)r3[c] << 16);
+      for (int s = 0; s < 8; ++s) {
+        const u32x2 ahi = *reinterpret_cast<const u32x2*>(&sm.pw[wave][0][qi][16 * jj + 2 * s]);
+        const u32x2 alo = *reinterpret_cast<const u32x2*>(&sm.pw[wave][1][qi][16 * jj + 2 * s]);
+        const uint32_t* r = &vr[jj][4 * s];
+        const u32x2 b0 = u32x2{pair16<0>(r[0], r[1]), pair16<0>(r[2], r[3])};
+        acc[0] = mfma16<BF16>(ahi, b0, acc[0]);
+        acc[0] = mfma16<BF16>(alo, b0, acc[0]);
+        if constexpr (D == 128) {
+          const u32x2 b1 = u32x2{pair16<1>(r[0], r[1]), pair16<1>(r[2], r[3])};
+          acc[1] = mfma16<BF16>(ahi, b1, acc[1]);
+          acc[1] = mfma16<BF16>(alo, b1, acc[1]);
+        }
+        acc1 = mfma16<BF16>(ahi, one, acc1);
+        acc1 = mfma16<BF16>(alo, one, acc1);
       }
-    }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const u32x2 ahi = *reinterpret_cast<const u32x2*>(&sm.pw[wave][0][qi][16 * jj + 2 * s]);
-      const u32x2 alo = *reinterpret_cast<const u32x2*>(&sm.pw[wave][1][qi][16 * jj + 2 * s]);
-#pragma unroll
-      for (int h = 0; h < D / 64; ++h) {
-        const u32x2 b = u32x2{pk[s][h][0], pk[s][h][1]};
-        acc[h] = mfma16<BF16>(ahi, b, acc[h]);
-        acc[h] = mfma16<BF16>(alo, b, acc[h]);
-      }
-      acc1 = mfma16<BF16>(ahi, one, acc1);
-      acc1 = mfma16<BF16>(alo, one, acc1);
     }
   }
 #pragma unroll
@@ -496,65 +542,74 @@ __device__ __forceinline__ void value_phase_16(const Smem<D>& sm, int wave, int 
 // Tile loops
 // ---------------------------------------------------------------------------------------
 
-// Quantized keys and values, both widths fixed: loads of the next tile are issued before the
-// current tile is computed.
-template <int D, int KB, int VB>
+// Quantized keys and values, both widths fixed: the loads of the tile two steps ahead are
+// issued before the current tile is computed.
+template <int D, int KB, int VB, class Prologue, class Window>
 __device__ __forceinline__ void body_loop(Smem<D>& sm, const DecodePlan& p, const uint64_t* off, int t0, int t1,
-                                          int lane, int wave, float kscale, WaveState& st,
+                                          int lane, int wave, Prologue prologue, Window window, WaveState& st,
                                           float (&o)[kMaxG][D / 64]) {
-  const uint32_t* kc = reinterpret_cast<const uint32_t*>(p.blob + off[KC]);
-  const uint32_t* km = reinterpret_cast<const uint32_t*>(p.blob + off[KM]);
-  const uint32_t* vc = reinterpret_cast<const uint32_t*>(p.blob + off[VC]);
-  const uint32_t* vm = reinterpret_cast<const uint32_t*>(p.blob + off[VM]);
+  const BodySrc src = body_src(p, off);
+  int tile = t0 + wave;
+  const bool any = tile < t1;
+  // three register buffers: while one tile is computed the next two are in flight
+  KTile<D, KB> kt[3];
+  VTile<D, VB> vt[3];
+  if (any) {  // the first tiles are in flight while the query operands are prepared
+    const int second = tile + kWaves < t1 ? tile + kWaves : tile;
+    load_k<D, KB>(kt[0], src, tile, lane);
+    load_v<D, VB>(vt[0], src, tile, lane);
+    load_k<D, KB>(kt[1], src, second, lane);
+    load_v<D, VB>(vt[1], src, second, lane);
+  }
+  issue_barrier();
+  const float kscale = prologue();
+  window();
+  if (!any) return;
   int ppos, pe;
   value_slot<VB>(lane & 31, ppos, pe);
   const float pscl = __builtin_ldexpf(1.0f, kEp - pe);
-  int tile = t0 + wave;
-  if (tile >= t1) return;
-  KTile<D, KB> kt[2];
-  VTile<D, VB> vt[2];
-  load_k<D, KB>(kt[0], kc, km, tile, lane);
-  load_v<D, VB>(vt[0], vc, vm, tile, lane);
-  auto run = [&](const KTile<D, KB>& kcur, const VTile<D, VB>& vcur, KTile<D, KB>& knext, VTile<D, VB>& vnext) {
-    // the next tile (or, past the end, this one again) is always fetched, so both buffers
-    // keep fixed registers and the loads stay in flight while this tile is computed
-    const int next = tile + kWaves;
-    const int fetch = next < t1 ? next : tile;
-    load_k<D, KB>(knext, kc, km, fetch, lane);
-    load_v<D, VB>(vnext, vc, vm, fetch, lane);
+  auto run = [&](const KTile<D, KB>& kcur, const VTile<D, VB>& vcur, KTile<D, KB>& kfree, VTile<D, VB>& vfree) {
+    // the tile two steps ahead (or, past the end, this one again) is always fetched, so the
+    // buffers keep fixed registers and the loads stay in flight while this tile is computed
+    const int ahead = tile + 2 * kWaves;
+    const int fetch = ahead < t1 ? ahead : tile;
+    load_k<D, KB>(kfree, src, fetch, lane);
+    load_v<D, VB>(vfree, src, fetch, lane);
     issue_barrier();
     float sc[kMaxG];
     key_phase<D, KB>(sm, kcur, lane, kscale, sc);
     softmax_tile<D>(sm, wave, lane, tile * kTile + lane < p.body, sc, st, o, ppos, pscl, false);
     value_phase<D, VB>(sm, wave, vcur, lane, min(2, (p.body - tile * kTile) / 32), o, st);
     wave_lds_sync();
-    tile = next;
+    tile += kWaves;
   };
   while (true) {
-    run(kt[0], vt[0], kt[1], vt[1]);
+    run(kt[0], vt[0], kt[2], vt[2]);
     if (tile >= t1) break;
     run(kt[1], vt[1], kt[0], vt[0]);
+    if (tile >= t1) break;
+    run(kt[2], vt[2], kt[1], vt[1]);
     if (tile >= t1) break;
   }
 }
 
 template <int D, int KB>
-__device__ __forceinline__ void key_tile_q(const Smem<D>& sm, const uint32_t* kc, const uint32_t* km, int tile, int lane,
+__device__ __forceinline__ void key_tile_q(const Smem<D>& sm, const BodySrc& src, int tile, int lane,
                                            float kscale, float (&sc)[kMaxG]) {
   KTile<D, KB> t;
-  load_k<D, KB>(t, kc, km, tile, lane);
+  load_k<D, KB>(t, src, tile, lane);
   key_phase<D, KB>(sm, t, lane, kscale, sc);
 }
 
 template <int D, int VB>
-__device__ __forceinline__ void value_tile_q(Smem<D>& sm, int wave, const uint32_t* vc, const uint32_t* vm, int tile,
+__device__ __forceinline__ void value_tile_q(Smem<D>& sm, int wave, const BodySrc& src, int tile,
                                              int lane, bool valid, const float (&sc)[kMaxG], int nblk, WaveState& st,
                                              float (&o)[kMaxG][D / 64]) {
   int ppos, pe;
   value_slot<VB>(lane & 31, ppos, pe);
   softmax_tile<D>(sm, wave, lane, valid, sc, st, o, ppos, __builtin_ldexpf(1.0f, kEp - pe), false);
   VTile<D, VB> t;
-  load_v<D, VB>(t, vc, vm, tile, lane);
+  load_v<D, VB>(t, src, tile, lane);
   value_phase<D, VB>(sm, wave, t, lane, nblk, o, st);
 }
 
@@ -567,23 +622,20 @@ __device__ __forceinline__ void mixed_body_loop(Smem<D>& sm, const DecodePlan& p
   const bool bf16 = p.dtype == KVQ_BF16;
   const uint16_t* kr = reinterpret_cast<const uint16_t*>(p.blob + off[KC]);
   const uint16_t* vr = reinterpret_cast<const uint16_t*>(p.blob + off[VC]);
-  const uint32_t* kc = reinterpret_cast<const uint32_t*>(p.blob + off[KC]);
-  const uint32_t* km = reinterpret_cast<const uint32_t*>(p.blob + off[KM]);
-  const uint32_t* vc = reinterpret_cast<const uint32_t*>(p.blob + off[VC]);
-  const uint32_t* vm = reinterpret_cast<const uint32_t*>(p.blob + off[VM]);
+  const BodySrc src = body_src(p, off);
   for (int tile = t0 + wave; tile < t1; tile += kWaves) {
     const int tok = tile * kTile + lane;
     const bool valid = tok < p.body;
     const int n_valid = min(kTile, p.body - tile * kTile);
     float sc[kMaxG];
     switch (kb) {
-      case 2: key_tile_q<D, 2>(sm, kc, km, tile, lane, kscale, sc); break;
-      case 3: key_tile_q<D, 3>(sm, kc, km, tile, lane, kscale, sc); break;
-      case 4: key_tile_q<D, 4>(sm, kc, km, tile, lane, kscale, sc); break;
-      case 5: key_tile_q<D, 5>(sm, kc, km, tile, lane, kscale, sc); break;
-      case 6: key_tile_q<D, 6>(sm, kc, km, tile, lane, kscale, sc); break;
-      case 7: key_tile_q<D, 7>(sm, kc, km, tile, lane, kscale, sc); break;
-      case 8: key_tile_q<D, 8>(sm, kc, km, tile, lane, kscale, sc); break;
+      case 2: key_tile_q<D, 2>(sm, src, tile, lane, kscale, sc); break;
+      case 3: key_tile_q<D, 3>(sm, src, tile, lane, kscale, sc); break;
+      case 4: key_tile_q<D, 4>(sm, src, tile, lane, kscale, sc); break;
+      case 5: key_tile_q<D, 5>(sm, src, tile, lane, kscale, sc); break;
+      case 6: key_tile_q<D, 6>(sm, src, tile, lane, kscale, sc); break;
+      case 7: key_tile_q<D, 7>(sm, src, tile, lane, kscale, sc); break;
+      case 8: key_tile_q<D, 8>(sm, src, tile, lane, kscale, sc); break;
       default:
         if (bf16)
           key_phase_16<D, true>(sm, kr + (size_t)(valid ? tok : tile * kTile) * D, lane, p.scale_log2, sc);
@@ -593,20 +645,23 @@ __device__ __forceinline__ void mixed_body_loop(Smem<D>& sm, const DecodePlan& p
     }
     const int nblk = n_valid / 32;
     switch (vb) {
-      case 2: value_tile_q<D, 2>(sm, wave, vc, vm, tile, lane, valid, sc, nblk, st, o); break;
-      case 3: value_tile_q<D, 3>(sm, wave, vc, vm, tile, lane, valid, sc, nblk, st, o); break;
-      case 4: value_tile_q<D, 4>(sm, wave, vc, vm, tile, lane, valid, sc, nblk, st, o); break;
-      case 5: value_tile_q<D, 5>(sm, wave, vc, vm, tile, lane, valid, sc, nblk, st, o); break;
-      case 6: value_tile_q<D, 6>(sm, wave, vc, vm, tile, lane, valid, sc, nblk, st, o); break;
-      case 7: value_tile_q<D, 7>(sm, wave, vc, vm, tile, lane, valid, sc, nblk, st, o); break;
-      case 8: value_tile_q<D, 8>(sm, wave, vc, vm, tile, lane, valid, sc, nblk, st, o); break;
-      default:
+      case 2: value_tile_q<D, 2>(sm, wave, src, tile, lane, valid, sc, nblk, st, o); break;
+      case 3: value_tile_q<D, 3>(sm, wave, src, tile, lane, valid, sc, nblk, st, o); break;
+      case 4: value_tile_q<D, 4>(sm, wave, src, tile, lane, valid, sc, nblk, st, o); break;
+      case 5: value_tile_q<D, 5>(sm, wave, src, tile, lane, valid, sc, nblk, st, o); break;
+      case 6: value_tile_q<D, 6>(sm, wave, src, tile, lane, valid, sc, nblk, st, o); break;
+      case 7: value_tile_q<D, 7>(sm, wave, src, tile, lane, valid, sc, nblk, st, o); break;
+      case 8: value_tile_q<D, 8>(sm, wave, src, tile, lane, valid, sc, nblk, st, o); break;
+      default: {
+        uint32_t rows[2][32];
+        load_v16<D>(rows, lane, n_valid, [&](int k) { return vr + (size_t)(tile * kTile + k) * D; });
         softmax_tile<D>(sm, wave, lane, valid, sc, st, o, lane & 31, 1.0f, bf16);
         if (bf16)
-          value_phase_16<D, true>(sm, wave, lane, n_valid, [&](int k) { return vr + (size_t)(tile * kTile + k) * D; }, o, st);
+          value_phase_16<D, true>(sm, wave, lane, n_valid, rows, o, st);
         else
-          value_phase_16<D, false>(sm, wave, lane, n_valid, [&](int k) { return vr + (size_t)(tile * kTile + k) * D; }, o, st);
+          value_phase_16<D, false>(sm, wave, lane, n_valid, rows, o, st);
         break;
+      }
     }
     wave_lds_sync();
   }
@@ -620,10 +675,14 @@ __device__ __forceinline__ void rows16_loop_t(Smem<D>& sm, const DecodePlan& p, 
   for (int base = first + wave * kTile; base < n_tok; base += kWaves * kTile) {
     const int u = base + lane;
     const bool valid = u < n_tok;
+    const int n_valid = min(kTile, n_tok - base);
+    uint32_t vr[2][32];
+    load_v16<D>(vr, lane, n_valid, [&](int k) { return vrow(base + k); });
+    issue_barrier();
     float sc[kMaxG];
     key_phase_16<D, BF16>(sm, krow(valid ? u : base), lane, p.scale_log2, sc);
     softmax_tile<D>(sm, wave, lane, valid, sc, st, o, lane & 31, 1.0f, BF16);
-    value_phase_16<D, BF16>(sm, wave, lane, min(kTile, n_tok - base), [&](int k) { return vrow(base + k); }, o, st);
+    value_phase_16<D, BF16>(sm, wave, lane, n_valid, vr, o, st);
     wave_lds_sync();
   }
 }
@@ -649,44 +708,50 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodePlan p) {
   const int kb = p.k_bits[h], vb = p.v_bits[h];
   const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)b * p.Hq + (size_t)h * G) * D;
 
-  // ---- q operands in LDS: raw 16-bit copy, and the fp16 key operand in slot order with
-  // q scaled by 2^Eq so that max|q| * 2^Eq lies in [2^14, 2^15)
-  float qmax = 0.0f;
-  for (int idx = tid; idx < kMaxG * D; idx += kThreads) {
-    const int i = idx / D, c = idx % D;
-    const uint32_t raw = i < G ? q[(size_t)i * D + c] : 0u;
-    reinterpret_cast<uint16_t*>(sm.qW[i])[c] = (uint16_t)raw;
-    qmax = fmaxf(qmax, fabsf(widen(raw, p.dtype)));
-  }
-  qmax = wave_max(qmax);
-  if (lane == 0) sm.qmax[wave] = qmax;
-  __syncthreads();
-  qmax = fmaxf(fmaxf(sm.qmax[0], sm.qmax[1]), fmaxf(sm.qmax[2], sm.qmax[3]));
-  int qe = 0;
-  if (qmax > 0.0f) (void)frexpf(qmax, &qe);
-  const int Eq = 15 - qe;
-  const float kscale = __builtin_ldexpf(p.scale_log2, 24 - Eq);
-  for (int idx = tid; idx < kMaxG * D; idx += kThreads) {
-    const int i = idx / D, slot = idx % D;  // slot = (g * 8 + s) * 4 + k
-    const int g = slot / 32, s = (slot / 4) % 8, k = slot % 4;
-    int ch = 0, e = 0;
-    switch (kb) {
+  // ---- q operands in LDS: raw 16-bit copy, the per-group sums of q, and the fp16 key
+  // operand in slot order with q scaled by 2^Eq so that max|q| * 2^Eq lies in [2^14, 2^15).
+  // Returns the key-score factor scale_log2 * 2^(24 - Eq). Every wavefront calls it once.
+  auto prologue = [&]() -> float {
+    constexpr int E = kMaxG * D / kThreads;  // consecutive elements per thread (2 or 1)
+    float qmax = 0.0f, qs = 0.0f;
+    const int i0 = (tid * E) / D;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int c = (tid * E + e) % D;
+      const uint32_t raw = i0 < G ? q[(size_t)i0 * D + c] : 0u;
+      reinterpret_cast<uint16_t*>(sm.qW[i0])[c] = (uint16_t)raw;
+      const float v = widen(raw, p.dtype);
+      qmax = fmaxf(qmax, fabsf(v));
+      qs += v;
+    }
+    // a 32-channel group spans 32 / E aligned lanes
+#pragma unroll
+    for (int o2 = 16 / E; o2 >= 1; o2 >>= 1) qs += __shfl_xor(qs, o2, 64);
+    if ((tid * E) % 32 == 0) sm.qsum[i0][((tid * E) % D) / 32] = qs * p.scale_log2;
+    qmax = wave_max(qmax);
+    if (lane == 0) sm.qmax[wave] = qmax;
+    __syncthreads();
+    qmax = fmaxf(fmaxf(sm.qmax[0], sm.qmax[1]), fmaxf(sm.qmax[2], sm.qmax[3]));
+    int qe = 0;
+    if (qmax > 0.0f) (void)frexpf(qmax, &qe);
+    const int Eq = 15 - qe;
+    for (int idx = tid; idx < kMaxG * D; idx += kThreads) {
+      const int i = idx / D, slot = idx % D;  // slot = (g * 8 + s) * 4 + k
+      const int g = slot / 32, s = (slot / 4) % 8, k = slot % 4;
+      int ch = 0, e = 0;
+      switch (kb) {
 #define KVQ_SLOT(B_) \
   case B_: ch = Slots<B_>::chan(s, k); e = Slots<B_>::exp(s, k); break;
-      KVQ_SLOT(2) KVQ_SLOT(3) KVQ_SLOT(4) KVQ_SLOT(5) KVQ_SLOT(6) KVQ_SLOT(7) KVQ_SLOT(8)
+        KVQ_SLOT(2) KVQ_SLOT(3) KVQ_SLOT(4) KVQ_SLOT(5) KVQ_SLOT(6) KVQ_SLOT(7) KVQ_SLOT(8)
 #undef KVQ_SLOT
-      default: break;
+        default: break;
+      }
+      const float qv = widen(reinterpret_cast<const uint16_t*>(sm.qW[i])[g * 32 + ch], p.dtype);
+      reinterpret_cast<uint16_t*>(sm.qA[i])[slot] = (uint16_t)f2h(__builtin_ldexpf(qv, Eq - e));
     }
-    const float qv = widen(reinterpret_cast<const uint16_t*>(sm.qW[i])[g * 32 + ch], p.dtype);
-    reinterpret_cast<uint16_t*>(sm.qA[i])[slot] = (uint16_t)f2h(__builtin_ldexpf(qv, Eq - e));
-  }
-  if (tid < kMaxG * (D / 32)) {
-    const int i = tid / (D / 32), g = tid % (D / 32);
-    float s = 0.0f;
-    for (int k = 0; k < 32; ++k) s += widen(reinterpret_cast<const uint16_t*>(sm.qW[i])[g * 32 + k], p.dtype);
-    sm.qsum[i][g] = s * p.scale_log2;
-  }
-  __syncthreads();
+    __syncthreads();
+    return __builtin_ldexpf(p.scale_log2, 24 - Eq);
+  };
 
   WaveState st;
   float o[kMaxG][D / 64];
@@ -699,39 +764,54 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodePlan p) {
   }
   const uint64_t* off = p.off + ((size_t)b * p.H + h) * kRegions;
 
-  if (split < p.n_splits) {
-    const int t0 = split * p.tiles_per_split;
-    const int t1 = min(p.n_tiles, t0 + p.tiles_per_split);
-    if (kb == 16 && vb == 16) {
-      const uint16_t* kr = reinterpret_cast<const uint16_t*>(p.blob + off[KC]);
-      const uint16_t* vr = reinterpret_cast<const uint16_t*>(p.blob + off[VC]);
-      rows16_loop<D>(sm, p, t0 * kTile, min(p.body, t1 * kTile), lane, wave, st, o,
-                     [&](int u) { return kr + (size_t)u * D; }, [&](int u) { return vr + (size_t)u * D; });
-    } else if (kb <= 4 && vb <= 4) {
-      // the widths the allocator hands out in {2,3,4}: prefetching loop per combination
-#define KVQ_BODY(KB_, VB_) \
-  case KB_ * 16 + VB_: body_loop<D, KB_, VB_>(sm, p, off, t0, t1, lane, wave, kscale, st, o); break;
-      switch (kb * 16 + vb) {
-        KVQ_BODY(2, 2) KVQ_BODY(2, 3) KVQ_BODY(2, 4) KVQ_BODY(3, 2) KVQ_BODY(3, 3) KVQ_BODY(3, 4)
-        KVQ_BODY(4, 2) KVQ_BODY(4, 3) KVQ_BODY(4, 4)
-        default: break;
-      }
-#undef KVQ_BODY
-    } else {
-      // wider codes or a 16-bit side: one phase at a time
-      mixed_body_loop<D>(sm, p, off, t0, t1, lane, wave, kscale, st, o);
-    }
-  } else {
-    // 16-bit windows: token u < n_sink_live is sink row u, else the ring slot of absolute
-    // token n_sink + body + (u - n_sink_live)
+  // ---- this workgroup's units: window tiles [w0, w1), then body tiles [t0, t1). A window
+  // tile (16-bit rows, loads not prefetched) counts as kWindowUnits units, a body tile as one.
+  const int wu = kWindowUnits * p.n_wtiles;
+  const int u0 = split * p.units_per_split, u1 = min(wu + p.n_tiles, u0 + p.units_per_split);
+  const int w0 = min((u0 + kWindowUnits - 1) / kWindowUnits, p.n_wtiles);
+  const int w1 = min((max(u1, 0) + kWindowUnits - 1) / kWindowUnits, p.n_wtiles);
+  const int t0 = max(u0, wu) - wu, t1 = max(u1, wu) - wu;
+
+  // 16-bit windows: window token u < n_sink_live is sink row u, else ring slot
+  // (ring0 + u - n_sink_live) mod ring, ring0 = body mod ring (the ring's oldest live slot)
+  auto window = [&]() {
+    if (w0 >= w1) return;
     const uint16_t* sk = reinterpret_cast<const uint16_t*>(p.blob + off[SK]);
     const uint16_t* sv = reinterpret_cast<const uint16_t*>(p.blob + off[SV]);
     const uint16_t* rk = reinterpret_cast<const uint16_t*>(p.blob + off[RK]);
     const uint16_t* rv = reinterpret_cast<const uint16_t*>(p.blob + off[RV]);
-    const int nsl = p.n_sink_live, body = p.body, ring = p.ring;
-    auto krow = [&](int u) { return u < nsl ? sk + (size_t)u * D : rk + (size_t)((body + u - nsl) % ring) * D; };
-    auto vrow = [&](int u) { return u < nsl ? sv + (size_t)u * D : rv + (size_t)((body + u - nsl) % ring) * D; };
-    rows16_loop<D>(sm, p, 0, p.n_sink_live + p.n_win, lane, wave, st, o, krow, vrow);
+    const int nsl = p.n_sink_live, ring0 = p.ring0, ring = p.ring;
+    auto slot = [=](int u) {
+      const int r = ring0 + (u - nsl);
+      return r >= ring ? r - ring : r;
+    };
+    auto krow = [=](int u) { return u < nsl ? sk + (size_t)u * D : rk + (size_t)slot(u) * D; };
+    auto vrow = [=](int u) { return u < nsl ? sv + (size_t)u * D : rv + (size_t)slot(u) * D; };
+    rows16_loop<D>(sm, p, w0 * kTile, min(p.n_sink_live + p.n_win, w1 * kTile), lane, wave, st, o, krow, vrow);
+  };
+
+  if (kb == 16 && vb == 16) {
+    (void)prologue();
+    window();
+    const uint16_t* kr = reinterpret_cast<const uint16_t*>(p.blob + off[KC]);
+    const uint16_t* vr = reinterpret_cast<const uint16_t*>(p.blob + off[VC]);
+    rows16_loop<D>(sm, p, t0 * kTile, min(p.body, t1 * kTile), lane, wave, st, o,
+                   [&](int u) { return kr + (size_t)u * D; }, [&](int u) { return vr + (size_t)u * D; });
+  } else if (kb <= 4 && vb <= 4) {
+    // the widths the allocator hands out in {2,3,4}: prefetching loop per combination
+#define KVQ_BODY(KB_, VB_) \
+  case KB_ * 16 + VB_: body_loop<D, KB_, VB_>(sm, p, off, t0, t1, lane, wave, prologue, window, st, o); break;
+    switch (kb * 16 + vb) {
+      KVQ_BODY(2, 2) KVQ_BODY(2, 3) KVQ_BODY(2, 4) KVQ_BODY(3, 2) KVQ_BODY(3, 3) KVQ_BODY(3, 4)
+      KVQ_BODY(4, 2) KVQ_BODY(4, 3) KVQ_BODY(4, 4)
+      default: (void)prologue(); break;
+    }
+#undef KVQ_BODY
+  } else {
+    // wider codes or a 16-bit side: one phase at a time
+    const float kscale = prologue();
+    window();
+    mixed_body_loop<D>(sm, p, off, t0, t1, lane, wave, kscale, st, o);
   }
 
   // ---- combine the wavefronts of this workgroup into one partial (m, l, o)
@@ -742,7 +822,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodePlan p) {
       sm.red_l[wave][i] = st.l[i];
     }
 #pragma unroll
-    for (int hh = 0; hh < D / 64; ++hh) sm.red_o[wave][i][lane + 64 * hh] = o[i][hh];
+    for (int hh = 0; hh < D / 64; ++hh) sm.red_o[wave][i][(D / 64) * lane + hh] = o[i][hh];
   }
   __syncthreads();
   const size_t rows = (size_t)p.B * p.Hq;
@@ -769,73 +849,58 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodePlan p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Log-sum-exp merge of the n_splits + 1 partials of one (row, KV head):
+// Log-sum-exp merge of the n_splits partials (m_j, l_j, o_j) of one output row:
 //   out = sum_j 2^(m_j - m*) o_j / sum_j 2^(m_j - m*) l_j,  m* = max_j m_j.
 // A separate launch: the kernel boundary makes every partial visible, so no workgroup has
-// to write back or invalidate the L2 caches.
+// to write back or invalidate the L2 caches. One thread per output element; the partials
+// are read in chunks of kMergeChunk whose loads are all in flight together, and combined
+// online (the running sums are rescaled when a chunk raises the maximum).
 // ---------------------------------------------------------------------------------------
-struct MergeSmem {
-  float part_m[kMaxParts][kMaxG];  // (m, l) of every partial, then its weight
-  float part_l[kMaxParts][kMaxG];
-  float linv[kMaxG];
-};
+constexpr int kMergeChunk = 16;
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const DecodePlan p) {
-  __shared__ MergeSmem sm;
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int G = p.G, parts = p.n_splits + 1;
   const size_t rows = (size_t)p.B * p.Hq;
-  const size_t row0 = (size_t)b * p.Hq + (size_t)h * G;
-  for (int idx = tid; idx < parts * G; idx += kThreads) {
-    const int j = idx / G, i = idx % G;
-    const float* ml = p.ws_ml + ((size_t)j * rows + row0 + i) * 2;
-    sm.part_m[j][i] = ml[0];
-    sm.part_l[j][i] = ml[1];
-  }
-  __syncthreads();
-  // wavefront i reduces query i: m* = max_j m_j, l* = sum_j 2^(m_j - m*) l_j
-  if (wave < G) {
-    float mx = -INFINITY;
-    for (int j = lane; j < parts; j += 64) mx = fmaxf(mx, sm.part_m[j][wave]);
-    mx = wave_max(mx);
-    float ls = 0.0f;
-    for (int j = lane; j < parts; j += 64) {
-      const float mj = sm.part_m[j][wave];
-      const float f = mj == -INFINITY ? 0.0f : exp2f(mj - mx);
-      sm.part_m[j][wave] = f;  // the partial's weight from here on
-      ls += f * sm.part_l[j][wave];
+  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= rows * D) return;
+  const size_t r = idx / D;
+  const int parts = p.n_splits;
+  const float* op = p.ws_o + idx;
+  const float* mlp = p.ws_ml + r * 2;
+  float mx = -INFINITY, num = 0.0f, den = 0.0f;
+  for (int j0 = 0; j0 < parts; j0 += kMergeChunk) {
+    float m[kMergeChunk], l[kMergeChunk], o[kMergeChunk];
+#pragma unroll
+    for (int u = 0; u < kMergeChunk; ++u) {
+      const int j = min(j0 + u, parts - 1);  // past the end: a repeat, weighted 0 below
+      const float2 ml = *reinterpret_cast<const float2*>(mlp + (size_t)j * rows * 2);
+      m[u] = j0 + u < parts ? ml.x : -INFINITY;
+      l[u] = ml.y;
+      o[u] = op[(size_t)j * rows * D];
     }
+    float cm = mx;
 #pragma unroll
-    for (int o2 = 32; o2 >= 1; o2 >>= 1) ls += __shfl_xor(ls, o2, 64);
-    if (lane == 0) sm.linv[wave] = 1.0f / ls;
-  }
-  __syncthreads();
-  // eight partials per batch of independent loads
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int i = idx / D, c = idx % D;
-    const float* op = p.ws_o + (row0 + i) * D + c;
-    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    int j = 0;
-    for (; j + 8 <= parts; j += 8) {
-      float v[8];
+    for (int u = 0; u < kMergeChunk; ++u) cm = fmaxf(cm, m[u]);
+    if (cm == -INFINITY) continue;  // nothing but empty partials so far
+    const float rescale = exp2f(mx - cm);  // 0 while mx is still -inf
+    num *= rescale;
+    den *= rescale;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = op[(size_t)(j + u) * rows * D];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc[u] += sm.part_m[j + u][i] * v[u];
+    for (int u = 0; u < kMergeChunk; ++u) {
+      const float f = m[u] == -INFINITY ? 0.0f : exp2f(m[u] - cm);
+      num += f * o[u];
+      den += f * l[u];
     }
-    for (; j < parts; ++j) acc[0] += sm.part_m[j][i] * op[(size_t)j * rows * D];
-    const float oo = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
-    p.out[(row0 + i) * D + c] = oo * sm.linv[i];
+    mx = cm;
   }
+  p.out[idx] = num / den;
 }
 
 }  // namespace
 
 int launch_decode_splitk(const DecodePlan& p, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  dim3 grid(p.n_splits + 1, p.H, p.B);
+  dim3 grid(p.n_splits, p.H, p.B);
   if (p.D == 128)
     hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(kThreads), 0, s, p);
   else
@@ -845,10 +910,11 @@ int launch_decode_splitk(const DecodePlan& p, void* stream) {
 
 int launch_decode_merge(const DecodePlan& p, void* stream) {
   hipStream_t s = (hipStream_t)stream;
+  const unsigned blocks = (unsigned)(((size_t)p.B * p.Hq * p.D + kThreads - 1) / kThreads);
   if (p.D == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, dim3(p.H, p.B), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(merge_kernel<128>, dim3(blocks), dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL(merge_kernel<64>, dim3(p.H, p.B), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(merge_kernel<64>, dim3(blocks), dim3(kThreads), 0, s, p);
   return (int)hipGetLastError();
 }
 

@@ -166,7 +166,7 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t n_splits) {
     return 0;
   }
   const kvq_config& c = cache->cfg;
-  const size_t parts = (size_t)n_splits + 1;
+  const size_t parts = (size_t)n_splits;
   const size_t rows = (size_t)c.batch * c.n_q_heads;
   return align_up(parts * rows * c.head_dim * 4) + align_up(parts * rows * 2 * 4);
 }
@@ -194,7 +194,7 @@ kvq_status decode_plan(const kvq_cache* cache, const void* q_dev, float* out_dev
   p.off = table_ptr(cache);
   p.q = q_dev;
   p.out = out_dev;
-  const size_t parts = (size_t)n_splits + 1;
+  const size_t parts = (size_t)n_splits;
   const size_t rows = (size_t)c.batch * c.n_q_heads;
   p.ws_o = static_cast<float*>(ws);
   p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(parts * rows * c.head_dim * 4));
@@ -210,8 +210,11 @@ kvq_status decode_plan(const kvq_cache* cache, const void* q_dev, float* out_dev
   p.n_sink_cfg = c.n_sink;
   p.ring = ring_slots(c.n_recent);
   p.n_splits = n_splits;
+  p.ring0 = p.body % p.ring;
   p.n_tiles = (p.body + kTile - 1) / kTile;
-  p.tiles_per_split = (p.n_tiles + n_splits - 1) / n_splits;
+  p.n_wtiles = (p.n_sink_live + p.n_win + kTile - 1) / kTile;
+  // a window tile weighs kWindowUnits body tiles (16-bit rows, not prefetched)
+  p.units_per_split = (p.n_tiles + kWindowUnits * p.n_wtiles + n_splits - 1) / n_splits;
   p.dtype = c.dtype;
   const float s = scale > 0.0f ? scale : 1.0f / std::sqrt((float)c.head_dim);
   p.scale_log2 = s * 1.4426950408889634f;

@@ -13,6 +13,7 @@ namespace kvq {
 
 constexpr int kGroup = 32;        // quantization group size (keys: channels, values: tokens)
 constexpr int kTile = 64;         // body tokens per key tile (one wavefront, one token per lane)
+constexpr int kWindowUnits = 2;   // decode work units of a 16-bit window tile (a body tile is one)
 constexpr int kRegions = 9;
 constexpr uint64_t kAlign = 256;  // every region starts on a 256-byte boundary
 constexpr uint64_t kHeaderBytes = 256;
@@ -98,7 +99,9 @@ struct DecodePlan {
   float* ws_o;           // [P][B][Hq][D]
   float* ws_ml;          // [P][B][Hq][2]
   int B, H, Hq, G, D, T, body, n_sink_live, n_win, n_sink_cfg, ring;
-  int n_splits, tiles_per_split, n_tiles;
+  int ring0;             // ring slot of the oldest live window token (body mod ring)
+  int n_splits, n_tiles, n_wtiles;  // partials, 64-token body tiles, 64-token window tiles
+  int units_per_split;   // work units (window tiles first, then body tiles) per split
   int dtype;
   float scale_log2;      // softmax scale times log2(e)
   uint8_t k_bits[KVQ_MAX_KV_HEADS];

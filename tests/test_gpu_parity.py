@@ -181,6 +181,22 @@ def test_decode_edge_lengths(T):
     check_decode(cache, oc, q, splits=(1, 3))
 
 
+@pytest.mark.parametrize("T", [250, 700, 1333])
+def test_long_window_across_splits(T):
+    # a 200-token recent window (up to 4 window tiles, wrapping around the ring) shared out
+    # over several splits together with the body tiles; some splits get no tile at all
+    say(f"case: long window T={T}")
+    rng = np.random.default_rng(70 + T)
+    ocfg = O.CacheConfig(1, 2, 8, 128, 2000, 5, 200, "fp16", "hybrid", (3, 2), (2, 4))
+    k = workloads.random_raw16(rng, (1, 2, T, 128), "fp16", 2.0)
+    v = workloads.random_raw16(rng, (1, 2, T, 128), "fp16")
+    q = workloads.random_raw16(rng, (1, 8, 128), "fp16")
+    oc = O.build_cache(k, v, ocfg)
+    cache = gpu_cache(ocfg, k, v, chunks=[T // 2, T - T // 2])
+    assert_regions_equal(cache, oc)
+    check_decode(cache, oc, q, splits=(1, 2, 3, 6, 40))
+
+
 def test_explicit_scale():
     rng = np.random.default_rng(40)
     ocfg = O.CacheConfig(1, 1, 4, 128, 500, 4, 64, "bf16", "asym", (3,), (3,))
