@@ -36,7 +36,48 @@ def parse():
     ap.add_argument("--instances", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run only the launches the HBM-counter passes measure: a 256 MiB "
+                         "elementwise copy (counter calibration), then 30 decode launches")
     return ap.parse_args()
+
+
+def traffic_probe():
+    """The launches behind the committed FETCH_SIZE / WRITE_SIZE summary: torch.add over 64 Mi
+    int32 (256 MiB read + 256 MiB written, a plain copy of known size) 10 times, then 30
+    split-K decode launches over 5 rotating full-size cache instances."""
+    import torch
+
+    import mixed_precision_quantized_kvq_amd as kvq
+    import workloads
+    dev = torch.device("cuda:0")
+    n = 64 << 20
+    src = torch.arange(n, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        torch.add(src, 1, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    w = workloads.make(WORKLOAD)
+    s = w["spec"]
+    kb, _ = kvq.allocate_bits(w["alpha_k"], w["beta_k"], w["w_k"], s.k_total, s.b_lo, s.b_hi)
+    vb, _ = kvq.allocate_bits(w["alpha_v"], w["beta_v"], w["w_v"], s.v_total, s.b_lo, s.b_hi)
+    cfg = kvq.Config.make(s.batch, s.n_kv, s.n_q, s.head_dim, s.tokens, s.n_sink, s.n_recent, s.dtype,
+                          s.quant, kb, vb)
+    kd = torch.from_numpy(w["k"].view(np.int16)).to(dev)
+    vd = torch.from_numpy(w["v"].view(np.int16)).to(dev)
+    caches = []
+    for _ in range(5):
+        c = kvq.KVCache(cfg, device=dev)
+        kvq.append(c, kd, vd)
+        caches.append(c)
+    del kd, vd
+    q = torch.from_numpy(w["q"].view(np.int16)).to(dev)
+    ws = torch.zeros(kvq.decode_workspace_bytes(caches[0], s.n_splits), dtype=torch.uint8, device=dev)
+    for i in range(30):
+        kvq.decode_splitk(caches[i % 5], q, s.n_splits, ws)
+    torch.cuda.synchronize()
+    print("traffic probe done", flush=True)
 
 
 def decode_bytes(spec, k_bits, v_bits, T, n_splits):
@@ -53,6 +94,27 @@ def decode_bytes(spec, k_bits, v_bits, T, n_splits):
     q = rows * D * 2
     partials = n_splits * rows * (D + 2) * 4
     return spec.batch * per_head + q + partials
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "decode_kernel_qwen8b_t32k_traffic.txt")
+KERNEL_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "mixed_precision_quantized_kvq_amd",
+                          "csrc", "decode.hip")
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed FETCH_SIZE + WRITE_SIZE summary, or None
+    when that summary was taken on another version of the kernel source (sha256 mismatch)."""
+    import hashlib
+    try:
+        fields = dict(l.split("=", 1) for l in open(TRAFFIC_FILE).read().split()
+                      if "=" in l and not l.startswith("#"))
+        src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        if fields.get("decode_hip_sha256") != src_hash:
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, k_bits, v_bits, seconds):
@@ -92,6 +154,9 @@ def main():
         print("bench.py: this build runs on one GPU only (the decode path has no multi-GPU "
               "stage); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_probe:
+        traffic_probe()
+        return
     import torch
 
     import mixed_precision_quantized_kvq_amd as kvq
@@ -178,10 +243,26 @@ def main():
     el = time.perf_counter() - t0
     for c in caches:
         kvq.cache_check(c)
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
-    dec_us = float(np.mean(dec_ms)) * 1e3
+    step_dec_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
     T_mean = toks / (args.steps * B * H)
-    nbytes = decode_bytes(s, k_bits, v_bits, int(round(T_mean)), s.n_splits)
+
+    # ---- the split-K kernel alone, for the roofline: launches queued back to back behind a
+    # spin kernel (so the host is ahead and no launch gap enters the events), rotating over
+    # the cache instances; events on the launch stream bracket each batch
+    n_batch, per_batch = 4, 50
+    t_us = []
+    for _ in range(n_batch):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(20_000_000)
+        e0.record(stream)
+        for i in range(per_batch):
+            kvq.decode_splitk(caches[i % len(caches)], q, s.n_splits, ws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_us.append(e0.elapsed_time(e1) * 1e3 / per_batch)
+    dec_us = float(np.median(t_us))
+    T_now = int(round(np.mean([c.len for c in caches])))
+    nbytes = decode_bytes(s, k_bits, v_bits, T_now, s.n_splits)
     achieved = nbytes / (dec_us * 1e-6) / 1e9
     res = {
         "metric": "decode-attention KV tokens*heads/s over the packed mixed-precision cache",
@@ -202,9 +283,11 @@ def main():
                    "cache_instances": args.instances, "cache_mb_each": round(cache_mb, 1),
                    "step": "append 1 token + split-K decode + LSE merge"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode_kernel (split-K fused-dequant decode), HIP events around each launch",
-                     "bytes_per_launch": nbytes, "avg_us": dec_us},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "kernel": "decode_kernel (split-K fused-dequant decode), HIP events around "
+                               f"{n_batch}x{per_batch} back-to-back launches",
+                     "bytes_per_launch": nbytes, "avg_us": dec_us, "context": T_now,
+                     "in_step_avg_us": step_dec_us},
         "offline": {"allocate_bits_us": alloc_us, "calibrate_fit_ms_k_plus_v": calib_ms,
                     "prefill_append_ms": float(np.median(prefill_ms)),
                     "prefill_append_gbs": (B * H * T0 * D * 4) / (float(np.median(prefill_ms)) * 1e-3) / 1e9},
