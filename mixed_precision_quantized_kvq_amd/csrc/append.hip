@@ -3,6 +3,7 @@
 // Built with -ffp-contract=off: the quantizer must round exactly as quant_device.h states.
 #include <hip/hip_runtime.h>
 
+#include "code_plans.h"
 #include "kvq_internal.h"
 #include "quant_device.h"
 
@@ -34,9 +35,43 @@ __device__ __forceinline__ void load_row32(const uint16_t* src, int dtype, float
   }
 }
 
+// Value stream of one decode lane: the 32 codes of virtual stream vg of lane (g4, n) of the
+// block's half of the tile (g4 = 2 * (block % 2) + jp). Stream position chan(s, k) holds the
+// code of token 16 kk + 8 jp + u of channel 16 nb + n, with chunk c = s / 2, nb = 2 vg + c / 2,
+// kk = c % 2, u = 4 (s % 2) + k: the order the decode kernel's value plan reads.
+template <int B>
+__device__ __forceinline__ void pack_value_stream(const uint8_t (*codes)[kGroup + 1], int vg, int jp, int n,
+                                                  uint32_t* dst) {
+  uint64_t acc = 0;
+  int nbits = 0, w = 0;
+#pragma unroll
+  for (int qpos = 0; qpos < kGroup; ++qpos) {
+    int s = 0, k = 0;
+#pragma unroll
+    for (int ss = 0; ss < 8; ++ss)
+#pragma unroll
+      for (int kk4 = 0; kk4 < 4; ++kk4)
+        if (VSlots<B>::chan(ss, kk4) == qpos) {
+          s = ss;
+          k = kk4;
+        }
+    const int c = s >> 1, nb = 2 * vg + (c >> 1), kk = c & 1, u = 4 * (s & 1) + k;
+    acc |= (uint64_t)codes[16 * nb + n][16 * kk + 8 * jp + u] << nbits;
+    nbits += B;
+    if (nbits >= 32) {
+      dst[w++] = (uint32_t)acc;
+      acc >>= 32;
+      nbits -= 32;
+    }
+  }
+}
+
 // One workgroup per (flushed block, head, row); 2*D threads: thread i < D handles key group
 // i = (token tt of the block) * (D/32) + channel group g, thread D + c handles value channel c.
+// Value codes are staged in LDS and then written, one (decode lane, stream) per thread, in the
+// decode kernel's value order.
 __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
+  __shared__ uint8_t vcodes[128][kGroup + 1];   // [channel][token of the block]
   const int j = p.body0 / kGroup + blockIdx.x;  // body block index
   const int h = blockIdx.y, b = blockIdx.z;
   const int D = p.D, Gd = D / kGroup;
@@ -47,64 +82,87 @@ __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
   const int tid = threadIdx.x;
   const bool is_key = tid < D;
   const int bits = is_key ? p.k_bits[h] : p.v_bits[h];
+  const int vbits = p.v_bits[h];
   const int tile = j >> 1, jj = j & 1;
-  float x[32];
-  if (is_key) {
-    const int tt = tid / Gd, g = tid % Gd;
-    const int t = p.n_sink + j * kGroup + tt;
-    const uint16_t* src = token_row(p, p.blob + off[RK], kin, t) + g * kGroup;
-    if (bits == 16) {
-      uint4* dst = reinterpret_cast<uint4*>(p.blob + off[KC]) +
-                   ((size_t)(j * kGroup + tt) * D + g * kGroup) / 8;
+  bool sym = false;
+  if (bits == 16) {
+    // unquantized head: the block's rows are copied
+    if (is_key) {
+      const int tt = tid / Gd, g = tid % Gd;
+      const uint16_t* src = token_row(p, p.blob + off[RK], kin, p.n_sink + j * kGroup + tt) + g * kGroup;
+      uint4* dst = reinterpret_cast<uint4*>(p.blob + off[KC]) + ((size_t)(j * kGroup + tt) * D + g * kGroup) / 8;
 #pragma unroll
       for (int v = 0; v < 4; ++v) dst[v] = reinterpret_cast<const uint4*>(src)[v];
-      return;
-    }
-    load_row32(src, p.dtype, x);
-  } else {
-    const int c = tid - D;
-    const char* ring = p.blob + off[RV];
-    if (bits == 16) {
+    } else {
+      const int c = tid - D;
       uint16_t* dst = reinterpret_cast<uint16_t*>(p.blob + off[VC]);
 #pragma unroll
       for (int k = 0; k < 32; ++k)
-        dst[(size_t)(j * kGroup + k) * D + c] = token_row(p, ring, vin, p.n_sink + j * kGroup + k)[c];
-      return;
+        dst[(size_t)(j * kGroup + k) * D + c] = token_row(p, p.blob + off[RV], vin, p.n_sink + j * kGroup + k)[c];
     }
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      const int t = p.n_sink + j * kGroup + k;
-      x[k] = widen16(token_row(p, ring, vin, t)[c], p.dtype);
-    }
-  }
-  if (out_of_range(x)) atomicOr(p.range_flag, 1u);
-  const GroupQ q = choose_quant(x, bits, p.hybrid != 0);
-  const uint32_t meta = (uint32_t)q.s_bits | ((uint32_t)q.z_bits << 16);
-  if (is_key) {
-    const int tt = tid / Gd, g = tid % Gd;
-    const int W = Gd * bits;                       // words per token
-    const int t_in_tile = jj * kGroup + tt;
-    uint32_t* kc = reinterpret_cast<uint32_t*>(p.blob + off[KC]) + (size_t)tile * kTile * W;
-    pack_group(x, q, bits, [&](int k, uint32_t word) {
-      const int w = g * bits + k;
-      const int qc = w >> 2, nq = min(4, W - 4 * qc);
-      kc[256 * qc + t_in_tile * nq + (w - 4 * qc)] = word;
-    });
-    reinterpret_cast<uint32_t*>(p.blob + off[KM])[(size_t)(j * kGroup + tt) * Gd + g] = meta;
   } else {
-    const int c = tid - D;
-    uint32_t* vc = reinterpret_cast<uint32_t*>(p.blob + off[VC]) + ((size_t)tile * 2 * D + c * 2 + jj) * bits;
-    pack_group(x, q, bits, [&](int k, uint32_t word) { vc[k] = word; });
-    reinterpret_cast<uint32_t*>(p.blob + off[VM])[(size_t)tile * 2 * D + c * 2 + jj] = meta;
+    float x[32];
+    if (is_key) {
+      const int tt = tid / Gd, g = tid % Gd;
+      load_row32(token_row(p, p.blob + off[RK], kin, p.n_sink + j * kGroup + tt) + g * kGroup, p.dtype, x);
+    } else {
+      const int c = tid - D;
+#pragma unroll
+      for (int k = 0; k < 32; ++k)
+        x[k] = widen16(token_row(p, p.blob + off[RV], vin, p.n_sink + j * kGroup + k)[c], p.dtype);
+    }
+    if (out_of_range(x)) atomicOr(p.range_flag, 1u);
+    const GroupQ q = choose_quant(x, bits, p.hybrid != 0);
+    sym = q.sym;
+    const uint32_t meta = (uint32_t)q.s_bits | ((uint32_t)q.z_bits << 16);
+    if (is_key) {
+      const int tt = tid / Gd, g = tid % Gd;
+      const int W = Gd * bits;  // words per token
+      const int t_in_tile = jj * kGroup + tt;
+      uint32_t* kc = reinterpret_cast<uint32_t*>(p.blob + off[KC]) + (size_t)tile * kTile * W;
+      pack_group(x, q, bits, [&](int k, uint32_t word) {
+        const int w = g * bits + k;
+        const int qc = w >> 2, nq = min(4, W - 4 * qc);
+        kc[256 * qc + t_in_tile * nq + (w - 4 * qc)] = word;
+      });
+      reinterpret_cast<uint32_t*>(p.blob + off[KM])[(size_t)(j * kGroup + tt) * Gd + g] = meta;
+    } else {
+      const int c = tid - D;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) vcodes[c][k] = (uint8_t)code_of(x[k], q);
+      // (s|z) of channel c = 16 nb + n for this block, at [tile][block][n][nb]
+      reinterpret_cast<uint32_t*>(p.blob + off[VM])[(size_t)tile * 2 * D + jj * D + (c & 15) * (D / 16) + (c >> 4)] =
+          meta;
+    }
   }
-  if (p.hybrid) {
+  if (p.hybrid && bits != 16) {
     // flag bit i of this block's key (value) words = group i of thread i (D + i)
-    const unsigned long long m = __ballot(q.sym);
+    const unsigned long long m = __ballot(sym);
     if ((tid & 63) == 0) {
       uint32_t* fl = reinterpret_cast<uint32_t*>(p.blob + off[FL]) + (size_t)j * 2 * Gd;
       const int wbase = (is_key ? 0 : Gd) + ((is_key ? tid : tid - D) >> 5);
       fl[wbase] = (uint32_t)m;
       fl[wbase + 1] = (uint32_t)(m >> 32);
+    }
+  }
+  if (vbits == 16) return;  // uniform over the workgroup
+  __syncthreads();
+  if (!is_key) {
+    // value streams of this block: 32 decode lanes (g4 = 2 jj + jp, n) x D/32 streams each
+    const int x = tid - D, nv = D / 32;
+    const int lane_local = x / nv, vg = x % nv;
+    const int jp = lane_local >> 4, n = lane_local & 15;
+    const int lane = (2 * jj + jp) * 16 + n;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(p.blob + off[VC]) + (size_t)tile * 2 * D * vbits +
+                    ((size_t)lane * nv + vg) * vbits;
+    switch (vbits) {
+      case 2: pack_value_stream<2>(vcodes, vg, jp, n, dst); break;
+      case 3: pack_value_stream<3>(vcodes, vg, jp, n, dst); break;
+      case 4: pack_value_stream<4>(vcodes, vg, jp, n, dst); break;
+      case 5: pack_value_stream<5>(vcodes, vg, jp, n, dst); break;
+      case 6: pack_value_stream<6>(vcodes, vg, jp, n, dst); break;
+      case 7: pack_value_stream<7>(vcodes, vg, jp, n, dst); break;
+      default: pack_value_stream<8>(vcodes, vg, jp, n, dst); break;
     }
   }
 }

@@ -3,35 +3,35 @@
 // structure of its "Algorithm 1 ... decode phase"); the log-sum-exp merge of the split
 // partials is a second, small kernel.
 //
-// Grid (n_splits, KV heads, rows), 4 wavefronts per workgroup. The work of a (row, KV head)
-// is a list of 64-token units: first the tiles of the 16-bit sink + recent-window tokens,
-// then the packed body tiles. Workgroup `split` owns a contiguous range of units, so the
-// windows cost no workgroup of their own; its wavefronts take the window tiles, then the
-// body tiles, round-robin.
+// Grid (n_splits, KV heads, rows), 4 wavefronts per workgroup. Workgroup `split` owns a
+// contiguous range of 64-token body tiles (its wavefronts take them round-robin); the 64-token
+// tiles of the 16-bit sink + recent-window tokens are dealt out one per workgroup to the
+// wavefronts with the fewest body tiles, so the windows cost no workgroup of their own.
 //
-// Both products run on the 4x4x4 (16-block) f16/bf16 MFMA. Lane l belongs to block l/4 and
-// to row/column l%4, so with the G <= 4 query heads of a KV head as the 4-wide dimension:
-//   q.K^T  lane = token. B operand = 4 codes of the lane's token, A = the 4 matching q values
-//          of query l%4; output element i is query i's partial dot for that token.
-//   P.V    lane = channel (for D = 128 the lane owns the adjacent channels 2l and 2l+1, one
-//          MFMA each, so its code words and 16-bit window values arrive in single loads).
-//          B operand = 4 tokens' codes of the channel, A = the 4 matching softmax weights
-//          of query l%4; output element i is query i's partial.
+// q.K^T runs on the 4x4x4 (16-block) f16/bf16 MFMA. Lane l belongs to block l/4 and to
+// row/column l%4, and the G <= 4 query heads of a KV head are the 4-wide dimension: lane =
+// token, B operand = 4 codes of the lane's token, A = the 4 matching q values of query l%4;
+// output element i is query i's partial dot for that token.
+// P.V of packed tiles runs on the 16x16x32 f16 MFMA: rows = (32-token block, hi/lo half of
+// the weight, query), K = 16 tokens of each block per step, columns = 16 channels; the lane's
+// B operand is 8 consecutive tokens of one channel. 16-bit window rows use the 4x4x4 MFMA with
+// lane = channel (for D = 128 the adjacent channels 2l and 2l+1).
 // Codes enter the MFMA as fp16 subnormals: one shift and one AND of a packed word leave two
 // codes in the top mantissa bits of two fp16 halves, i.e. the values c * 2^(e - 24) (slot
-// plans below). The 2^e of each slot is divided out of the matching A value (q or p), so
-// every product is exact and each sum carries one known power of two.
+// plans in code_plans.h). The 2^e of each slot is divided out of the matching A value (q or
+// p), so every product is exact and each sum carries one known power of two.
 // Each group's scale and zero are applied once to its partial sums:
 //   q . k_hat = s (q . c) + z sum(q)                     key group: 32 channels of a token
 //   sum_t p_t v_hat_t = s sum_t p_t c_t + z sum_t p_t    value group: 32 tokens of a channel
 // Softmax weights travel as an fp16 (bf16 for bf16 windows) pair hi + lo; sum_t p_t comes
-// from the same MFMA with a constant operand in every slot, so numerator and denominator use
-// identical weights.
+// from the same MFMA with a constant operand, so numerator and denominator use identical
+// weights.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
 #include <math.h>
 
+#include "code_plans.h"  // slot plans and code unpacking (shared with the append kernel)
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -48,13 +48,20 @@ constexpr float kTau = 4.0f;
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float4_t mfma_f16(u32x2 a, u32x2 b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, a), __builtin_bit_cast(half4_t, b), c, 0, 0, 0);
 }
 __device__ __forceinline__ float4_t mfma_bf16(u32x2 a, u32x2 b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(short4_t, a), __builtin_bit_cast(short4_t, b), c, 0, 0, 0);
+}
+// 16x16x32 f16: lane l holds A[l % 16][8 (l / 16) + 0..7] and B[8 (l / 16) + 0..7][l % 16] (8
+// halves each, as 4 registers) and D[4 (l / 16) + r][l % 16], r = 0..3
+__device__ __forceinline__ float4_t mfma_f16_k32(u32x4 a, u32x4 b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0,
+                                                0, 0);
 }
 template <bool BF16>
 __device__ __forceinline__ float4_t mfma16(u32x2 a, u32x2 b, float4_t c) {
@@ -97,134 +104,17 @@ __device__ __forceinline__ void wave_lds_sync() { __asm__ __volatile__("" ::: "m
 // Keeps global loads issued above this point from being sunk below it (software prefetch).
 __device__ __forceinline__ void issue_barrier() { __asm__ __volatile__("" ::: "memory"); }
 
-// ---------------------------------------------------------------------------------------
-// Slot plans: MFMA step s (0..7) of a 32-element group takes 4 codes; slot k of step s
-// holds group element chan(s, k) as the fp16 subnormal c * 2^(exp(s, k) - 24).
-// Codes sit at the TOP of the 10-bit subnormal mantissa (exp = 10 - b or close to it): the
-// 4x4x4 f16 MFMA keeps fp32 accuracy in its sums only when the subnormal operands are not
-// deeply denormalized (codes at the bottom bits lose up to ~2^-16 of relative accuracy).
-// Each pair of codes is cut out of the packed words with one shift/funnel shift and one AND:
-//   b = 2: codes k, k+8 of a word; k even at bits 8-9, k odd at bits 6-7 (exp 8 / 6)
-//   b = 3: pairs (a, a+5) or (a, a+6): code a at bits 5-7, code b at high-half bits 4-6 / 7-9
-//   b = 4: codes k, k+4 of a word at bits 6-9 (exp 6)
-//   b = 8: codes k, k+2 of a word at bits 2-9 (exp 2)
-//   b = 5, 6, 7: codes 4s .. 4s+3 in order, each field extracted and placed at exp 10 - b
-// ---------------------------------------------------------------------------------------
-__host__ __device__ constexpr int pair3_a(int j) { return j < 5 ? j : (j < 10 ? j + 5 : j + 10); }
-__host__ __device__ constexpr int pair3_b(int j) { return j < 10 ? pair3_a(j) + 5 : pair3_a(j) + 6; }
-
-template <int B>
-struct Slots {
-  __host__ __device__ static constexpr int chan(int s, int k) {
-    if constexpr (B == 2) {
-      return 16 * (s >> 2) + 2 * (s & 3) + (k >> 1) + 8 * (k & 1);
-    } else if constexpr (B == 3) {
-      const int j = 2 * s + (k >> 1);
-      return (k & 1) ? pair3_b(j) : pair3_a(j);
-    } else if constexpr (B == 4) {
-      return 8 * (s >> 1) + 2 * (s & 1) + (k >> 1) + 4 * (k & 1);
-    } else if constexpr (B == 8) {
-      return 4 * s + (k >> 1) + 2 * (k & 1);
-    } else {
-      return 4 * s + k;
-    }
-  }
-  __host__ __device__ static constexpr int exp(int s, int k) {
-    if constexpr (B == 2) {
-      return ((2 * (s & 3) + (k >> 1)) & 1) ? 6 : 8;
-    } else if constexpr (B == 3) {
-      const int j = 2 * s + (k >> 1);
-      return (k & 1) ? (j < 10 ? 4 : 7) : 5;
-    } else if constexpr (B == 4) {
-      return 6;
-    } else if constexpr (B == 8) {
-      return 2;
-    } else {
-      return 10 - B;
-    }
-  }
-};
-
-// Low 32 bits of (hi:lo) >> n, 0 <= n < 32 (v_alignbit_b32 on the device; written as a funnel
-// shift of two registers so the code words stay in registers).
-__host__ __device__ __forceinline__ uint32_t funnel(uint32_t hi, uint32_t lo, int n) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  return __builtin_amdgcn_alignbit(hi, lo, n);
-#else
-  return (uint32_t)((((uint64_t)hi << 32) | lo) >> n);
-#endif
-}
-
-// Bits [pos, pos + B) of a group's little-endian code stream starting at word `base`.
-template <int B, int N>
-__host__ __device__ __forceinline__ uint32_t field(const uint32_t (&w)[N], int base, int pos) {
-  const int wi = base + (pos >> 5), off = pos & 31;
-  if (off + B <= 32) return (w[wi] >> off) & ((1u << B) - 1u);
-  return funnel(w[wi + 1], w[wi], off) & ((1u << B) - 1u);
-}
-
-// 32 bits of the group's stream starting at stream bit `sh` (sh may be negative: shifted
-// in zeros), read from the group's B words.
-template <int B, int N>
-__host__ __device__ __forceinline__ uint32_t window(const uint32_t (&w)[N], int base, int sh) {
-  if (sh < 0) return w[base] << (-sh);
-  const int wi = sh >> 5, off = sh & 31;
-  if (wi + 1 >= B || off == 0) return w[base + wi] >> off;
-  return funnel(w[base + wi + 1], w[base + wi], off);
-}
-
-// B operand (two fp16 pairs) of step s for the group whose words start at w[base].
-template <int B, int N>
-__host__ __device__ __forceinline__ u32x2 unpack_step(const uint32_t (&w)[N], int base, int s) {
-  if constexpr (B == 2) {
-    const uint32_t x = w[base + (s >> 2)];
-    uint32_t r[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = 2 * (s & 3) + h;            // pair (k, k + 8) of this word
-      const int sh = (k & 1) ? 2 * k - 6 : 2 * k - 8;
-      const uint32_t y = sh >= 0 ? (x >> sh) : (x << -sh);
-      r[h] = y & ((k & 1) ? 0x00C000C0u : 0x03000300u);
-    }
-    return u32x2{r[0], r[1]};
-  } else if constexpr (B == 3) {
-    uint32_t r[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int j = 2 * s + h;
-      const int a = pair3_a(j);
-      const uint32_t y = window<3>(w, base, 3 * a - 5);
-      r[h] = y & ((7u << 5) | (7u << (16 + (j < 10 ? 4 : 7))));
-    }
-    return u32x2{r[0], r[1]};
-  } else if constexpr (B == 4) {
-    const uint32_t x = w[base + (s >> 1)];
-    uint32_t r[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = 2 * (s & 1) + h;            // pair (k, k + 4) of this word
-      const int sh = 4 * k - 6;
-      const uint32_t y = sh >= 0 ? (x >> sh) : (x << -sh);
-      r[h] = y & 0x03C003C0u;
-    }
-    return u32x2{r[0], r[1]};
-  } else if constexpr (B == 8) {
-    const uint32_t x = w[base + s];
-    return u32x2{(x << 2) & 0x03FC03FCu, (x >> 6) & 0x03FC03FCu};
-  } else {
-    constexpr int e = 10 - B;
-    const uint32_t c0 = field<B>(w, base, (4 * s + 0) * B), c1 = field<B>(w, base, (4 * s + 1) * B);
-    const uint32_t c2 = field<B>(w, base, (4 * s + 2) * B), c3 = field<B>(w, base, (4 * s + 3) * B);
-    return u32x2{(c0 << e) | (c1 << (16 + e)), (c2 << e) | (c3 << (16 + e))};
-  }
-}
-
-// fp16 2^(exp(s, k) - 14) in every slot of step s: the weight sum sum_t p_t comes out of the
-// value MFMA with this operand (normal numbers, so its sums are exact to fp32).
 template <int B>
 __device__ __forceinline__ u32x2 ones_step(int s) {
   auto one = [&](int k) { return (uint32_t)(Slots<B>::exp(s, k) + 1) << 10; };
   return u32x2{one(0) | (one(1) << 16), one(2) | (one(3) << 16)};
+}
+
+template <int B>
+__device__ __forceinline__ u32x4 ones_chunk() {
+  auto one = [](int u) { return (uint32_t)(VSlots<B>::exp(u >> 2, u & 3) + 1) << 10; };
+  return u32x4{one(0) | (one(1) << 16), one(2) | (one(3) << 16), one(4) | (one(5) << 16),
+               one(6) | (one(7) << 16)};
 }
 
 template <int D>
@@ -236,24 +126,35 @@ struct Smem {
   alignas(16) uint32_t qW[kMaxG][D / 2 + 4];      // 16-bit-row A operand: q in the cache dtype
   alignas(16) float qsum[kMaxG][D / 32];          // sum of q over each key group, times the softmax scale
   alignas(16) uint32_t pw[kWaves][2][kMaxG][36];  // per wave: hi/lo, query, 2 blocks x 16 words (+4 pad)
+  // packed-body weights per wave: [32-token block][hi/lo][query][token], fp16, rows padded to
+  // 40 halves; plus 32 zero halves for the operand rows of the other block
+  alignas(16) uint16_t pv[kWaves][2][2][kMaxG][40];
+  alignas(16) uint16_t zero16[32];
   float red_o[kWaves][kMaxG][D];
   float red_m[kWaves][kMaxG];
   float red_l[kWaves][kMaxG];
   float qmax[kWaves];
 };
 
+template <int D>
 struct WaveState {
-  float m[kMaxG];  // running max of the scores (log2 units), uniform over the wave
-  float l[kMaxG];  // running sum of the weights, uniform over the wave
+  float m[kMaxG];          // running max of the scores (log2 units), uniform over the wave
+  float l[kMaxG];          // weight sum of the 16-bit rows, uniform over the wave
+  float o[kMaxG][D / 64];  // 16-bit rows: channel (D/64) lane + h
+  // packed body: lane (g4, n) holds channel 16 nb + n for its (block, hi/lo) = g4; the four
+  // lane groups are added at the end
+  float ob[D / 16][kMaxG];
+  float lb[kMaxG];
 };
 
-// Softmax for one tile (lane = token): weights written to LDS as a hi/lo pair at the value
-// slot `ppos` of the lane's token, scaled by pscl; accumulators rescaled when the max moves.
-template <int D>
-__device__ __forceinline__ void softmax_tile(Smem<D>& sm, int wave, int lane, bool valid, const float (&sc)[kMaxG],
-                                             WaveState& st, float (&o)[kMaxG][D / 64], int ppos, float pscl,
-                                             bool bf16_weights) {
-  const int jj = lane >> 5;
+// Softmax for one tile (lane = token): the weight of query i, scaled by pscl, is written to
+// LDS as a hi/lo pair at wdst[i * i_stride] and wdst[hl_stride + i * i_stride]; the
+// accumulators in use are rescaled when the running max moves. 16-bit rows (kBody false) are
+// all processed before the first packed body tile, so then the body accumulators are still
+// zero and left alone.
+template <int D, bool kBody>
+__device__ __forceinline__ void softmax_tile(bool valid, const float (&sc)[kMaxG], WaveState<D>& st, uint16_t* wdst,
+                                             int hl_stride, int i_stride, float pscl, bool bf16_weights) {
 #pragma unroll
   for (int i = 0; i < kMaxG; ++i) {
     const float x = valid ? sc[i] : -INFINITY;
@@ -263,7 +164,12 @@ __device__ __forceinline__ void softmax_tile(Smem<D>& sm, int wave, int lane, bo
       st.m[i] = mn;
       st.l[i] *= alpha;
 #pragma unroll
-      for (int h = 0; h < D / 64; ++h) o[i][h] *= alpha;
+      for (int h = 0; h < D / 64; ++h) st.o[i][h] *= alpha;
+      if (kBody) {
+        st.lb[i] *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb) st.ob[nb][i] *= alpha;
+      }
     }
     const float mn = st.m[i];
     const float p = __builtin_amdgcn_exp2f(x - mn) * pscl;
@@ -275,10 +181,25 @@ __device__ __forceinline__ void softmax_tile(Smem<D>& sm, int wave, int lane, bo
       hi = f2h(p);
       lo = f2h(p - h2f(hi));
     }
-    reinterpret_cast<uint16_t*>(&sm.pw[wave][0][i][16 * jj])[ppos] = (uint16_t)hi;
-    reinterpret_cast<uint16_t*>(&sm.pw[wave][1][i][16 * jj])[ppos] = (uint16_t)lo;
+    wdst[i * i_stride] = (uint16_t)hi;
+    wdst[hl_stride + i * i_stride] = (uint16_t)lo;
   }
   wave_lds_sync();
+}
+
+// LDS destination of the softmax weights of the lane's token, for 16-bit rows (value slot
+// ppos of block lane / 32) and for the packed body (token lane % 32 of block lane / 32)
+template <int D>
+__device__ __forceinline__ void softmax_rows16(Smem<D>& sm, int wave, int lane, bool valid, const float (&sc)[kMaxG],
+                                               WaveState<D>& st, int ppos, float pscl, bool bf16_weights) {
+  uint16_t* dst = reinterpret_cast<uint16_t*>(&sm.pw[wave][0][0][16 * (lane >> 5)]) + ppos;
+  softmax_tile<D, false>(valid, sc, st, dst, kMaxG * 36 * 2, 36 * 2, pscl, bf16_weights);
+}
+template <int D>
+__device__ __forceinline__ void softmax_body(Smem<D>& sm, int wave, int lane, bool valid, const float (&sc)[kMaxG],
+                                             WaveState<D>& st, float pscl) {
+  uint16_t* dst = &sm.pv[wave][lane >> 5][0][0][lane & 31];
+  softmax_tile<D, true>(valid, sc, st, dst, kMaxG * 40, 40, pscl, false);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -292,8 +213,9 @@ struct KTile {
 };
 template <int D, int VB>
 struct VTile {
-  uint32_t w[D / 64][2 * VB];
-  uint32_t m[D / 64][2];
+  static constexpr int NB = D / 16;  // 16-channel column blocks of the value MFMA
+  uint32_t w[(NB / 2) * VB];         // the lane's NB/2 streams of 32 codes
+  uint32_t m[NB];                    // (s|z) of channel 16 nb + lane % 16, block lane / 32
 };
 
 // Body regions read through buffer descriptors: each load is base (descriptor) + the lane's
@@ -341,35 +263,25 @@ __device__ __forceinline__ void load_k(KTile<D, KB>& t, const BodySrc& src, int 
     bload2(src.km, mvoff, msoff, t.m);
 }
 
+// Value tile of the lane (g4, n) = (lane / 16, lane % 16): its NB/2 code streams (each 32
+// codes of b bits, b words) are contiguous at word (tile * 64 + lane) * (NB/2) * b, and the
+// (s|z) words of its NB channels 16 nb + n for block g4 / 2 at word tile * 2D + (g4 / 2) D +
+// n NB. Both are read with 16-byte loads (8-byte ones where the count is not a multiple of 4).
 template <int D, int VB>
 __device__ __forceinline__ void load_v(VTile<D, VB>& t, const BodySrc& src, int tile, int lane) {
-  // the lane's D/64 adjacent channels NH*lane .. NH*lane + NH-1: their code words (2 blocks of
-  // VB words each, channel after channel) and their (s|z) words are contiguous
-  constexpr int NH = D / 64, NW = NH * 2 * VB;
+  constexpr int NB = D / 16, NW = (NB / 2) * VB;
   const uint32_t soff = (uint32_t)tile * (2 * D * VB * 4), voff = (uint32_t)lane * NW * 4;
-  uint32_t w[NW];
   if constexpr (NW % 4 == 0) {
 #pragma unroll
-    for (int x = 0; x < NW; x += 4) bload4(src.vc, voff + 4 * x, soff, &w[x]);
+    for (int x = 0; x < NW; x += 4) bload4(src.vc, voff + 4 * x, soff, &t.w[x]);
   } else {
 #pragma unroll
-    for (int x = 0; x < NW; x += 2) bload2(src.vc, voff + 4 * x, soff, &w[x]);
+    for (int x = 0; x < NW; x += 2) bload2(src.vc, voff + 4 * x, soff, &t.w[x]);
   }
+  const uint32_t msoff = (uint32_t)tile * (2 * D * 4);
+  const uint32_t mvoff = (uint32_t)((lane >> 5) * D + (lane & 15) * NB) * 4;
 #pragma unroll
-  for (int h = 0; h < NH; ++h)
-#pragma unroll
-    for (int x = 0; x < 2 * VB; ++x) t.w[h][x] = w[h * 2 * VB + x];
-  const uint32_t msoff = (uint32_t)tile * (2 * D * 4), mvoff = (uint32_t)lane * NH * 2 * 4;
-  uint32_t m[2 * NH];
-  if constexpr (NH == 2)
-    bload4(src.vm, mvoff, msoff, m);
-  else
-    bload2(src.vm, mvoff, msoff, m);
-#pragma unroll
-  for (int h = 0; h < NH; ++h) {
-    t.m[h][0] = m[2 * h];
-    t.m[h][1] = m[2 * h + 1];
-  }
+  for (int x = 0; x < NB; x += 4) bload4(src.vm, mvoff + 4 * x, msoff, &t.m[x]);
 }
 
 // Scores (log2 units) of the lane's token for the 4 query slots.
@@ -393,82 +305,68 @@ __device__ __forceinline__ void key_phase(const Smem<D>& sm, const KTile<D, KB>&
   }
 }
 
+// P.V of one packed tile on the 16x16x32 MFMA. Rows m = (block, hi/lo, query) = 8 blk + 4 hl
+// + i; the 32 K of a step are 16 tokens of each block (tokens 16 kk + 0..15), the A row of a
+// block reading zeros for the other block's tokens; columns are 16 channels. Two steps (kk)
+// give D[m][n] = sum over the block's 32 tokens; the weight sums come from the same A with
+// the constant operand. Lane (g4, n) then holds the 4 queries of (block, hl) = g4 for channel
+// 16 nb + n and applies that block's scale and zero. nblk: valid 32-token blocks (1 or 2).
 template <int D, int VB>
 __device__ __forceinline__ void value_phase(const Smem<D>& sm, int wave, const VTile<D, VB>& t, int lane, int nblk,
-                                            float (&o)[kMaxG][D / 64], WaveState& st) {
-  const int qi = lane & 3;
+                                            WaveState<D>& st) {
+  constexpr int NB = D / 16;
   constexpr float kV = (float)(1 << (24 - kEp));   // code products carry 2^(kEp - 24)
   constexpr float kV1 = (float)(1 << (14 - kEp));  // weight sums carry 2^(kEp - 14)
+  const int m = lane & 15, g4 = lane >> 4;
+  const uint16_t* asrc = (m >> 3) == (g4 >> 1) ? &sm.pv[wave][m >> 3][(m >> 2) & 1][m & 3][8 * (g4 & 1)] : sm.zero16;
+  const u32x4 a0 = *reinterpret_cast<const u32x4*>(asrc);
+  const u32x4 a1 = *reinterpret_cast<const u32x4*>(asrc + 16);
+  const u32x4 one = ones_chunk<VB>();
+  float4_t d1 = mfma_f16_k32(a0, one, float4_t{0.0f, 0.0f, 0.0f, 0.0f});
+  d1 = mfma_f16_k32(a1, one, d1);
+  const bool live = (g4 >> 1) < nblk;  // the lane's block holds body tokens
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {
-    if (jj < nblk) {
-      float4_t acc[D / 64], acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int nb = 0; nb < NB; ++nb) {
+    const int base = (nb >> 1) * VB, c0 = 2 * (nb & 1);  // stream, first chunk (kk = 0)
+    const u32x2 p0 = unpack_step_v<VB>(t.w, base, 2 * c0), p1 = unpack_step_v<VB>(t.w, base, 2 * c0 + 1);
+    const u32x2 p2 = unpack_step_v<VB>(t.w, base, 2 * c0 + 2), p3 = unpack_step_v<VB>(t.w, base, 2 * c0 + 3);
+    float4_t d = mfma_f16_k32(a0, u32x4{p0.x, p0.y, p1.x, p1.y}, float4_t{0.0f, 0.0f, 0.0f, 0.0f});
+    d = mfma_f16_k32(a1, u32x4{p2.x, p2.y, p3.x, p3.y}, d);
+    const uint32_t mw = live ? t.m[nb] : 0u;
+    const float sv = h2f(mw & 0xFFFFu) * kV, zv = h2f(mw >> 16) * kV1;
 #pragma unroll
-      for (int h = 0; h < D / 64; ++h) acc[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const u32x2 ahi = *reinterpret_cast<const u32x2*>(&sm.pw[wave][0][qi][16 * jj + 2 * s]);
-        const u32x2 alo = *reinterpret_cast<const u32x2*>(&sm.pw[wave][1][qi][16 * jj + 2 * s]);
-#pragma unroll
-        for (int h = 0; h < D / 64; ++h) {
-          const u32x2 b = unpack_step<VB>(t.w[h], jj * VB, s);
-          acc[h] = mfma_f16(ahi, b, acc[h]);
-          acc[h] = mfma_f16(alo, b, acc[h]);
-        }
-        const u32x2 one = ones_step<VB>(s);
-        acc1 = mfma_f16(ahi, one, acc1);
-        acc1 = mfma_f16(alo, one, acc1);
-      }
-#pragma unroll
-      for (int h = 0; h < D / 64; ++h) {
-        const float sv = h2f(t.m[h][jj] & 0xFFFFu) * kV, zv = h2f(t.m[h][jj] >> 16) * kV1;
-#pragma unroll
-        for (int i = 0; i < kMaxG; ++i) o[i][h] = __builtin_fmaf(sv, acc[h][i], __builtin_fmaf(zv, acc1[i], o[i][h]));
-      }
-#pragma unroll
-      for (int i = 0; i < kMaxG; ++i) st.l[i] = __builtin_fmaf(acc1[i], kV1, st.l[i]);
-    }
+    for (int i = 0; i < kMaxG; ++i) st.ob[nb][i] = __builtin_fmaf(sv, d[i], __builtin_fmaf(zv, d1[i], st.ob[nb][i]));
   }
+#pragma unroll
+  for (int i = 0; i < kMaxG; ++i) st.lb[i] = __builtin_fmaf(d1[i], kV1, st.lb[i]);
 }
 
-// value slot (and its exponent) that holds token tb (0..31) of a block
+// Factor of the softmax weight of body token tb (0..31 of its block): 2^(kEp - e) with e the
+// exponent of the token's value slot (token u = tb % 8 of its chunk)
 template <int VB>
-__device__ __forceinline__ void value_slot(int tb, int& ppos, int& pe) {
-  ppos = 0;
-  pe = 0;
+__device__ __forceinline__ float value_pscale(int tb) {
+  float f = 1.0f;
 #pragma unroll
-  for (int s = 0; s < 8; ++s)
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (Slots<VB>::chan(s, k) == tb) {
-        ppos = 4 * s + k;
-        pe = Slots<VB>::exp(s, k);
-      }
+  for (int u = 0; u < 8; ++u)
+    if ((tb & 7) == u) f = (float)(1 << kEp) / (float)(1 << VSlots<VB>::exp(u >> 2, u & 3));
+  return f;
 }
 
 // ---------------------------------------------------------------------------------------
 // 16-bit rows (sink and recent windows; heads kept unquantized)
 // ---------------------------------------------------------------------------------------
+// q.K^T of 16-bit rows: lane = token, its key row x (D values, 16-byte pieces) in registers
 template <int D, bool BF16>
-__device__ __forceinline__ void key_phase_16(const Smem<D>& sm, const uint16_t* row, int lane,
-                                             float scale_log2, float (&sc)[kMaxG]) {
+__device__ __forceinline__ void key_phase_16(const Smem<D>& sm, const uint4 (&x)[D / 8], int lane, float scale_log2,
+                                             float (&sc)[kMaxG]) {
   const int qi = lane & 3;
   float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  const uint4* r4 = reinterpret_cast<const uint4*>(row);
-#pragma unroll 1
-  for (int part = 0; part < D / 64; ++part) {
-    uint4 x[8];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) x[v] = r4[part * 8 + v];
-    issue_barrier();  // all eight loads in flight before the first is used
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int vv = part * 8 + v;
-      const u32x2 a0 = *reinterpret_cast<const u32x2*>(&sm.qW[qi][4 * vv]);
-      const u32x2 a1 = *reinterpret_cast<const u32x2*>(&sm.qW[qi][4 * vv + 2]);
-      acc = mfma16<BF16>(a0, u32x2{x[v].x, x[v].y}, acc);
-      acc = mfma16<BF16>(a1, u32x2{x[v].z, x[v].w}, acc);
-    }
+  for (int v = 0; v < D / 8; ++v) {
+    const u32x2 a0 = *reinterpret_cast<const u32x2*>(&sm.qW[qi][4 * v]);
+    const u32x2 a1 = *reinterpret_cast<const u32x2*>(&sm.qW[qi][4 * v + 2]);
+    acc = mfma16<BF16>(a0, u32x2{x[v].x, x[v].y}, acc);
+    acc = mfma16<BF16>(a1, u32x2{x[v].z, x[v].w}, acc);
   }
 #pragma unroll
   for (int i = 0; i < kMaxG; ++i) sc[i] = acc[i] * scale_log2;
@@ -501,8 +399,7 @@ __device__ __forceinline__ uint32_t pair16(uint32_t a, uint32_t b) {
 // lane = channel; P.V of one tile of 16-bit rows from the operands load_v16 fetched
 template <int D, bool BF16>
 __device__ __forceinline__ void value_phase_16(const Smem<D>& sm, int wave, int lane, int n_valid,
-                                               const uint32_t (&vr)[2][32], float (&o)[kMaxG][D / 64],
-                                               WaveState& st) {
+                                               const uint32_t (&vr)[2][32], WaveState<D>& st) {
   const int qi = lane & 3;
   const uint32_t one1 = BF16 ? 0x3F80u : 0x3C00u;
   const u32x2 one = u32x2{one1 | (one1 << 16), one1 | (one1 << 16)};
@@ -533,7 +430,7 @@ __device__ __forceinline__ void value_phase_16(const Smem<D>& sm, int wave, int 
 #pragma unroll
   for (int h = 0; h < D / 64; ++h)
 #pragma unroll
-    for (int i = 0; i < kMaxG; ++i) o[i][h] += acc[h][i];
+    for (int i = 0; i < kMaxG; ++i) st.o[i][h] += acc[h][i];
 #pragma unroll
   for (int i = 0; i < kMaxG; ++i) st.l[i] += acc1[i];
 }
@@ -542,53 +439,81 @@ __device__ __forceinline__ void value_phase_16(const Smem<D>& sm, int wave, int 
 // Tile loops
 // ---------------------------------------------------------------------------------------
 
-// Quantized keys and values, both widths fixed: the loads of the tile two steps ahead are
-// issued before the current tile is computed.
-template <int D, int KB, int VB, class Prologue, class Window>
+// One 64-token tile of 16-bit rows: for every token, the lane's value channel(s) (loaded
+// ahead, possibly before the query prologue); the key rows are loaded when it is computed.
+template <int D>
+struct Rows16 {
+  uint32_t v[2][32];
+};
+template <int D, class VRowOf>
+__device__ __forceinline__ void rows16_issue(Rows16<D>& r, int base, int n_tok, int lane, VRowOf vrow) {
+  load_v16<D>(r.v, lane, min(kTile, n_tok - base), [&](int k) { return vrow(base + k); });
+}
+template <int D, class KRowOf>
+__device__ __forceinline__ void rows16_compute(Smem<D>& sm, const DecodePlan& p, const Rows16<D>& r, int base,
+                                               int n_tok, int lane, int wave, WaveState<D>& st, KRowOf krow) {
+  const int u = base + lane;
+  const bool valid = u < n_tok;
+  const int n_valid = min(kTile, n_tok - base);
+  uint4 x[D / 8];  // the lane's key row, all loads in flight together
+  const uint4* r4 = reinterpret_cast<const uint4*>(krow(valid ? u : base));
+#pragma unroll
+  for (int v = 0; v < D / 8; ++v) x[v] = r4[v];
+  issue_barrier();
+  float sc[kMaxG];
+  if (p.dtype == KVQ_BF16) {
+    key_phase_16<D, true>(sm, x, lane, p.scale_log2, sc);
+    softmax_rows16<D>(sm, wave, lane, valid, sc, st, lane & 31, 1.0f, true);
+    value_phase_16<D, true>(sm, wave, lane, n_valid, r.v, st);
+  } else {
+    key_phase_16<D, false>(sm, x, lane, p.scale_log2, sc);
+    softmax_rows16<D>(sm, wave, lane, valid, sc, st, lane & 31, 1.0f, false);
+    value_phase_16<D, false>(sm, wave, lane, n_valid, r.v, st);
+  }
+  wave_lds_sync();
+}
+// Quantized keys and values, both widths fixed: the loads of the next tile are issued before
+// the current tile is computed.
+template <int D, int KB, int VB, class Prologue, class WindowIssue, class Window>
 __device__ __forceinline__ void body_loop(Smem<D>& sm, const DecodePlan& p, const uint64_t* off, int t0, int t1,
-                                          int lane, int wave, Prologue prologue, Window window, WaveState& st,
-                                          float (&o)[kMaxG][D / 64]) {
+                                          int lane, int wave, Prologue prologue, WindowIssue window_issue, Window window,
+                                          WaveState<D>& st) {
   const BodySrc src = body_src(p, off);
   int tile = t0 + wave;
   const bool any = tile < t1;
-  // three register buffers: while one tile is computed the next two are in flight
-  KTile<D, KB> kt[3];
-  VTile<D, VB> vt[3];
-  if (any) {  // the first tiles are in flight while the query operands are prepared
-    const int second = tile + kWaves < t1 ? tile + kWaves : tile;
+  // two register buffers: the next tile is in flight while this one is computed
+  KTile<D, KB> kt[2];
+  VTile<D, VB> vt[2];
+  Rows16<D> wt;
+  window_issue(wt);
+  if (any) {  // the first tile is in flight while the query operands are prepared
     load_k<D, KB>(kt[0], src, tile, lane);
     load_v<D, VB>(vt[0], src, tile, lane);
-    load_k<D, KB>(kt[1], src, second, lane);
-    load_v<D, VB>(vt[1], src, second, lane);
   }
   issue_barrier();
   const float kscale = prologue();
-  window();
+  window(wt);
   if (!any) return;
-  int ppos, pe;
-  value_slot<VB>(lane & 31, ppos, pe);
-  const float pscl = __builtin_ldexpf(1.0f, kEp - pe);
+  const float pscl = value_pscale<VB>(lane & 31);
   auto run = [&](const KTile<D, KB>& kcur, const VTile<D, VB>& vcur, KTile<D, KB>& kfree, VTile<D, VB>& vfree) {
-    // the tile two steps ahead (or, past the end, this one again) is always fetched, so the
-    // buffers keep fixed registers and the loads stay in flight while this tile is computed
-    const int ahead = tile + 2 * kWaves;
-    const int fetch = ahead < t1 ? ahead : tile;
+    // the next tile (or, past the end, this one again) is always fetched, so both buffers
+    // keep fixed registers and the loads stay in flight while this tile is computed
+    const int next = tile + kWaves;
+    const int fetch = next < t1 ? next : tile;
     load_k<D, KB>(kfree, src, fetch, lane);
     load_v<D, VB>(vfree, src, fetch, lane);
     issue_barrier();
     float sc[kMaxG];
     key_phase<D, KB>(sm, kcur, lane, kscale, sc);
-    softmax_tile<D>(sm, wave, lane, tile * kTile + lane < p.body, sc, st, o, ppos, pscl, false);
-    value_phase<D, VB>(sm, wave, vcur, lane, min(2, (p.body - tile * kTile) / 32), o, st);
+    softmax_body<D>(sm, wave, lane, tile * kTile + lane < p.body, sc, st, pscl);
+    value_phase<D, VB>(sm, wave, vcur, lane, min(2, (p.body - tile * kTile) / 32), st);
     wave_lds_sync();
-    tile += kWaves;
+    tile = next;
   };
   while (true) {
-    run(kt[0], vt[0], kt[2], vt[2]);
+    run(kt[0], vt[0], kt[1], vt[1]);
     if (tile >= t1) break;
     run(kt[1], vt[1], kt[0], vt[0]);
-    if (tile >= t1) break;
-    run(kt[2], vt[2], kt[1], vt[1]);
     if (tile >= t1) break;
   }
 }
@@ -603,21 +528,18 @@ __device__ __forceinline__ void key_tile_q(const Smem<D>& sm, const BodySrc& src
 
 template <int D, int VB>
 __device__ __forceinline__ void value_tile_q(Smem<D>& sm, int wave, const BodySrc& src, int tile,
-                                             int lane, bool valid, const float (&sc)[kMaxG], int nblk, WaveState& st,
-                                             float (&o)[kMaxG][D / 64]) {
-  int ppos, pe;
-  value_slot<VB>(lane & 31, ppos, pe);
-  softmax_tile<D>(sm, wave, lane, valid, sc, st, o, ppos, __builtin_ldexpf(1.0f, kEp - pe), false);
+                                             int lane, bool valid, const float (&sc)[kMaxG], int nblk, WaveState<D>& st) {
+  softmax_body<D>(sm, wave, lane, valid, sc, st, value_pscale<VB>(lane & 31));
   VTile<D, VB> t;
   load_v<D, VB>(t, src, tile, lane);
-  value_phase<D, VB>(sm, wave, t, lane, nblk, o, st);
+  value_phase<D, VB>(sm, wave, t, lane, nblk, st);
 }
 
 // Body tiles of heads with a 16-bit key or value side (one phase 16-bit, the other packed
 // or 16-bit); no prefetch.
 template <int D>
 __device__ __forceinline__ void mixed_body_loop(Smem<D>& sm, const DecodePlan& p, const uint64_t* off, int t0, int t1, int lane,
-                                int wave, float kscale, WaveState& st, float (&o)[kMaxG][D / 64]) {
+                                int wave, float kscale, WaveState<D>& st) {
   const int kb = p.k_bits[blockIdx.y], vb = p.v_bits[blockIdx.y];
   const bool bf16 = p.dtype == KVQ_BF16;
   const uint16_t* kr = reinterpret_cast<const uint16_t*>(p.blob + off[KC]);
@@ -637,29 +559,34 @@ __device__ __forceinline__ void mixed_body_loop(Smem<D>& sm, const DecodePlan& p
       case 7: key_tile_q<D, 7>(sm, src, tile, lane, kscale, sc); break;
       case 8: key_tile_q<D, 8>(sm, src, tile, lane, kscale, sc); break;
       default:
+        uint4 x[D / 8];
+        const uint4* r4 = reinterpret_cast<const uint4*>(kr + (size_t)(valid ? tok : tile * kTile) * D);
+#pragma unroll
+        for (int v = 0; v < D / 8; ++v) x[v] = r4[v];
+        issue_barrier();
         if (bf16)
-          key_phase_16<D, true>(sm, kr + (size_t)(valid ? tok : tile * kTile) * D, lane, p.scale_log2, sc);
+          key_phase_16<D, true>(sm, x, lane, p.scale_log2, sc);
         else
-          key_phase_16<D, false>(sm, kr + (size_t)(valid ? tok : tile * kTile) * D, lane, p.scale_log2, sc);
+          key_phase_16<D, false>(sm, x, lane, p.scale_log2, sc);
         break;
     }
     const int nblk = n_valid / 32;
     switch (vb) {
-      case 2: value_tile_q<D, 2>(sm, wave, src, tile, lane, valid, sc, nblk, st, o); break;
-      case 3: value_tile_q<D, 3>(sm, wave, src, tile, lane, valid, sc, nblk, st, o); break;
-      case 4: value_tile_q<D, 4>(sm, wave, src, tile, lane, valid, sc, nblk, st, o); break;
-      case 5: value_tile_q<D, 5>(sm, wave, src, tile, lane, valid, sc, nblk, st, o); break;
-      case 6: value_tile_q<D, 6>(sm, wave, src, tile, lane, valid, sc, nblk, st, o); break;
-      case 7: value_tile_q<D, 7>(sm, wave, src, tile, lane, valid, sc, nblk, st, o); break;
-      case 8: value_tile_q<D, 8>(sm, wave, src, tile, lane, valid, sc, nblk, st, o); break;
+      case 2: value_tile_q<D, 2>(sm, wave, src, tile, lane, valid, sc, nblk, st); break;
+      case 3: value_tile_q<D, 3>(sm, wave, src, tile, lane, valid, sc, nblk, st); break;
+      case 4: value_tile_q<D, 4>(sm, wave, src, tile, lane, valid, sc, nblk, st); break;
+      case 5: value_tile_q<D, 5>(sm, wave, src, tile, lane, valid, sc, nblk, st); break;
+      case 6: value_tile_q<D, 6>(sm, wave, src, tile, lane, valid, sc, nblk, st); break;
+      case 7: value_tile_q<D, 7>(sm, wave, src, tile, lane, valid, sc, nblk, st); break;
+      case 8: value_tile_q<D, 8>(sm, wave, src, tile, lane, valid, sc, nblk, st); break;
       default: {
         uint32_t rows[2][32];
         load_v16<D>(rows, lane, n_valid, [&](int k) { return vr + (size_t)(tile * kTile + k) * D; });
-        softmax_tile<D>(sm, wave, lane, valid, sc, st, o, lane & 31, 1.0f, bf16);
+        softmax_rows16<D>(sm, wave, lane, valid, sc, st, lane & 31, 1.0f, bf16);
         if (bf16)
-          value_phase_16<D, true>(sm, wave, lane, n_valid, rows, o, st);
+          value_phase_16<D, true>(sm, wave, lane, n_valid, rows, st);
         else
-          value_phase_16<D, false>(sm, wave, lane, n_valid, rows, o, st);
+          value_phase_16<D, false>(sm, wave, lane, n_valid, rows, st);
         break;
       }
     }
@@ -667,39 +594,23 @@ __device__ __forceinline__ void mixed_body_loop(Smem<D>& sm, const DecodePlan& p
   }
 }
 
-// 16-bit rows for tokens [first, n_tok) in 64-token tiles.
-template <int D, bool BF16, class KRowOf, class VRowOf>
-__device__ __forceinline__ void rows16_loop_t(Smem<D>& sm, const DecodePlan& p, int first, int n_tok, int lane,
-                                              int wave, WaveState& st, float (&o)[kMaxG][D / 64], KRowOf krow,
-                                              VRowOf vrow) {
-  for (int base = first + wave * kTile; base < n_tok; base += kWaves * kTile) {
-    const int u = base + lane;
-    const bool valid = u < n_tok;
-    const int n_valid = min(kTile, n_tok - base);
-    uint32_t vr[2][32];
-    load_v16<D>(vr, lane, n_valid, [&](int k) { return vrow(base + k); });
-    issue_barrier();
-    float sc[kMaxG];
-    key_phase_16<D, BF16>(sm, krow(valid ? u : base), lane, p.scale_log2, sc);
-    softmax_tile<D>(sm, wave, lane, valid, sc, st, o, lane & 31, 1.0f, BF16);
-    value_phase_16<D, BF16>(sm, wave, lane, n_valid, vr, o, st);
-    wave_lds_sync();
-  }
-}
+// 16-bit rows for tokens [first, n_tok) in 64-token tiles, round-robin over the wavefronts.
 template <int D, class KRowOf, class VRowOf>
 __device__ __forceinline__ void rows16_loop(Smem<D>& sm, const DecodePlan& p, int first, int n_tok, int lane, int wave,
-                                            WaveState& st, float (&o)[kMaxG][D / 64], KRowOf krow, VRowOf vrow) {
-  if (p.dtype == KVQ_BF16)
-    rows16_loop_t<D, true>(sm, p, first, n_tok, lane, wave, st, o, krow, vrow);
-  else
-    rows16_loop_t<D, false>(sm, p, first, n_tok, lane, wave, st, o, krow, vrow);
+                                            WaveState<D>& st, KRowOf krow, VRowOf vrow) {
+  for (int base = first + wave * kTile; base < n_tok; base += kWaves * kTile) {
+    Rows16<D> r;
+    rows16_issue<D>(r, base, n_tok, lane, vrow);
+    rows16_compute<D>(sm, p, r, base, n_tok, lane, wave, st, krow);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
 // Kernel
 // ---------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodePlan p) {
+// two wavefronts per SIMD (two workgroups per CU): the register budget is 256
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(const DecodePlan p) {
   __shared__ Smem<D> sm;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -728,6 +639,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodePlan p) {
 #pragma unroll
     for (int o2 = 16 / E; o2 >= 1; o2 >>= 1) qs += __shfl_xor(qs, o2, 64);
     if ((tid * E) % 32 == 0) sm.qsum[i0][((tid * E) % D) / 32] = qs * p.scale_log2;
+    if (tid < 32) sm.zero16[tid] = 0;
     qmax = wave_max(qmax);
     if (lane == 0) sm.qmax[wave] = qmax;
     __syncthreads();
@@ -753,54 +665,67 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodePlan p) {
     return __builtin_ldexpf(p.scale_log2, 24 - Eq);
   };
 
-  WaveState st;
-  float o[kMaxG][D / 64];
+  WaveState<D> st;
 #pragma unroll
   for (int i = 0; i < kMaxG; ++i) {
     st.m[i] = -INFINITY;
     st.l[i] = 0.0f;
+    st.lb[i] = 0.0f;
 #pragma unroll
-    for (int hh = 0; hh < D / 64; ++hh) o[i][hh] = 0.0f;
+    for (int hh = 0; hh < D / 64; ++hh) st.o[i][hh] = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) st.ob[nb][i] = 0.0f;
   }
   const uint64_t* off = p.off + ((size_t)b * p.H + h) * kRegions;
 
-  // ---- this workgroup's units: window tiles [w0, w1), then body tiles [t0, t1). A window
-  // tile (16-bit rows, loads not prefetched) counts as kWindowUnits units, a body tile as one.
-  const int wu = kWindowUnits * p.n_wtiles;
-  const int u0 = split * p.units_per_split, u1 = min(wu + p.n_tiles, u0 + p.units_per_split);
-  const int w0 = min((u0 + kWindowUnits - 1) / kWindowUnits, p.n_wtiles);
-  const int w1 = min((max(u1, 0) + kWindowUnits - 1) / kWindowUnits, p.n_wtiles);
-  const int t0 = max(u0, wu) - wu, t1 = max(u1, wu) - wu;
-
-  // 16-bit windows: window token u < n_sink_live is sink row u, else ring slot
-  // (ring0 + u - n_sink_live) mod ring, ring0 = body mod ring (the ring's oldest live slot)
-  auto window = [&]() {
-    if (w0 >= w1) return;
-    const uint16_t* sk = reinterpret_cast<const uint16_t*>(p.blob + off[SK]);
-    const uint16_t* sv = reinterpret_cast<const uint16_t*>(p.blob + off[SV]);
-    const uint16_t* rk = reinterpret_cast<const uint16_t*>(p.blob + off[RK]);
-    const uint16_t* rv = reinterpret_cast<const uint16_t*>(p.blob + off[RV]);
-    const int nsl = p.n_sink_live, ring0 = p.ring0, ring = p.ring;
-    auto slot = [=](int u) {
-      const int r = ring0 + (u - nsl);
-      return r >= ring ? r - ring : r;
-    };
-    auto krow = [=](int u) { return u < nsl ? sk + (size_t)u * D : rk + (size_t)slot(u) * D; };
-    auto vrow = [=](int u) { return u < nsl ? sv + (size_t)u * D : rv + (size_t)slot(u) * D; };
-    rows16_loop<D>(sm, p, w0 * kTile, min(p.n_sink_live + p.n_win, w1 * kTile), lane, wave, st, o, krow, vrow);
+  // ---- this workgroup's work: body tiles [t0, t1) round-robin over the wavefronts, and the
+  // window tiles w = split + n_splits * k (k = 0, 1, ...), tile k going to wavefront
+  // kWaves - 1 - k % kWaves (the last wavefronts have the fewest body tiles). A wavefront's
+  // first window tile is loaded before the query prologue, so its latency is hidden.
+  const int t0 = split * p.tiles_per_split, t1 = min(p.n_tiles, t0 + p.tiles_per_split);
+  const int n_wtok = p.n_sink_live + p.n_win;
+  const int w_first = split + p.n_splits * (kWaves - 1 - wave);  // k = kWaves - 1 - wave
+  const uint16_t* sk = reinterpret_cast<const uint16_t*>(p.blob + off[SK]);
+  const uint16_t* sv = reinterpret_cast<const uint16_t*>(p.blob + off[SV]);
+  const uint16_t* rk = reinterpret_cast<const uint16_t*>(p.blob + off[RK]);
+  const uint16_t* rv = reinterpret_cast<const uint16_t*>(p.blob + off[RV]);
+  // window token u < n_sink_live is sink row u, else ring slot (ring0 + u - n_sink_live) mod
+  // ring, ring0 = body mod ring (the ring's oldest live slot)
+  const int nsl = p.n_sink_live, ring0 = p.ring0, ring = p.ring;
+  auto slot = [=](int u) {
+    const int r = ring0 + (u - nsl);
+    return r >= ring ? r - ring : r;
+  };
+  auto krow = [=](int u) { return u < nsl ? sk + (size_t)u * D : rk + (size_t)slot(u) * D; };
+  auto vrow = [=](int u) { return u < nsl ? sv + (size_t)u * D : rv + (size_t)slot(u) * D; };
+  const bool has_w = w_first < p.n_wtiles;
+  // issue the value loads of the first window tile (before the prologue); compute the window
+  auto window_issue = [&](Rows16<D>& wt) {
+    if (has_w) rows16_issue<D>(wt, w_first * kTile, n_wtok, lane, vrow);
+  };
+  auto window = [&](const Rows16<D>& wt) {
+    if (!has_w) return;
+    rows16_compute<D>(sm, p, wt, w_first * kTile, n_wtok, lane, wave, st, krow);
+    for (int w = w_first + kWaves * p.n_splits; w < p.n_wtiles; w += kWaves * p.n_splits) {
+      Rows16<D> r;
+      rows16_issue<D>(r, w * kTile, n_wtok, lane, vrow);
+      rows16_compute<D>(sm, p, r, w * kTile, n_wtok, lane, wave, st, krow);
+    }
   };
 
   if (kb == 16 && vb == 16) {
+    Rows16<D> wt;
+    window_issue(wt);
     (void)prologue();
-    window();
+    window(wt);
     const uint16_t* kr = reinterpret_cast<const uint16_t*>(p.blob + off[KC]);
     const uint16_t* vr = reinterpret_cast<const uint16_t*>(p.blob + off[VC]);
-    rows16_loop<D>(sm, p, t0 * kTile, min(p.body, t1 * kTile), lane, wave, st, o,
+    rows16_loop<D>(sm, p, t0 * kTile, min(p.body, t1 * kTile), lane, wave, st,
                    [&](int u) { return kr + (size_t)u * D; }, [&](int u) { return vr + (size_t)u * D; });
   } else if (kb <= 4 && vb <= 4) {
     // the widths the allocator hands out in {2,3,4}: prefetching loop per combination
 #define KVQ_BODY(KB_, VB_) \
-  case KB_ * 16 + VB_: body_loop<D, KB_, VB_>(sm, p, off, t0, t1, lane, wave, prologue, window, st, o); break;
+  case KB_ * 16 + VB_: body_loop<D, KB_, VB_>(sm, p, off, t0, t1, lane, wave, prologue, window_issue, window, st); break;
     switch (kb * 16 + vb) {
       KVQ_BODY(2, 2) KVQ_BODY(2, 3) KVQ_BODY(2, 4) KVQ_BODY(3, 2) KVQ_BODY(3, 3) KVQ_BODY(3, 4)
       KVQ_BODY(4, 2) KVQ_BODY(4, 3) KVQ_BODY(4, 4)
@@ -809,20 +734,43 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodePlan p) {
 #undef KVQ_BODY
   } else {
     // wider codes or a 16-bit side: one phase at a time
+    Rows16<D> wt;
+    window_issue(wt);
     const float kscale = prologue();
-    window();
-    mixed_body_loop<D>(sm, p, off, t0, t1, lane, wave, kscale, st, o);
+    window(wt);
+    mixed_body_loop<D>(sm, p, off, t0, t1, lane, wave, kscale, st);
   }
 
-  // ---- combine the wavefronts of this workgroup into one partial (m, l, o)
+  // ---- combine the wavefronts of this workgroup into one partial (m, l, o). The packed-body
+  // sums of the four lane groups (block, hi/lo) are added first; lane (g4, n) then owns
+  // query g4 of channels 16 nb + n.
+#pragma unroll
+  for (int i = 0; i < kMaxG; ++i) {
+    st.lb[i] += __shfl_xor(st.lb[i], 16, 64);
+    st.lb[i] += __shfl_xor(st.lb[i], 32, 64);
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) {
+      st.ob[nb][i] += __shfl_xor(st.ob[nb][i], 16, 64);
+      st.ob[nb][i] += __shfl_xor(st.ob[nb][i], 32, 64);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < kMaxG; ++i) {
     if (lane == 0) {
       sm.red_m[wave][i] = st.m[i];
-      sm.red_l[wave][i] = st.l[i];
+      sm.red_l[wave][i] = st.l[i] + st.lb[i];
     }
 #pragma unroll
-    for (int hh = 0; hh < D / 64; ++hh) sm.red_o[wave][i][(D / 64) * lane + hh] = o[i][hh];
+    for (int hh = 0; hh < D / 64; ++hh) sm.red_o[wave][i][(D / 64) * lane + hh] = st.o[i][hh];
+  }
+  wave_lds_sync();
+  {
+    const int g4 = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) {
+      const float v = g4 == 0 ? st.ob[nb][0] : g4 == 1 ? st.ob[nb][1] : g4 == 2 ? st.ob[nb][2] : st.ob[nb][3];
+      sm.red_o[wave][g4][16 * nb + n] += v;
+    }
   }
   __syncthreads();
   const size_t rows = (size_t)p.B * p.Hq;

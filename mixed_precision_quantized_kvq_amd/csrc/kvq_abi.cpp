@@ -213,8 +213,7 @@ kvq_status decode_plan(const kvq_cache* cache, const void* q_dev, float* out_dev
   p.ring0 = p.body % p.ring;
   p.n_tiles = (p.body + kTile - 1) / kTile;
   p.n_wtiles = (p.n_sink_live + p.n_win + kTile - 1) / kTile;
-  // a window tile weighs kWindowUnits body tiles (16-bit rows, not prefetched)
-  p.units_per_split = (p.n_tiles + kWindowUnits * p.n_wtiles + n_splits - 1) / n_splits;
+  p.tiles_per_split = (p.n_tiles + n_splits - 1) / n_splits;
   p.dtype = c.dtype;
   const float s = scale > 0.0f ? scale : 1.0f / std::sqrt((float)c.head_dim);
   p.scale_log2 = s * 1.4426950408889634f;

@@ -13,7 +13,6 @@ namespace kvq {
 
 constexpr int kGroup = 32;        // quantization group size (keys: channels, values: tokens)
 constexpr int kTile = 64;         // body tokens per key tile (one wavefront, one token per lane)
-constexpr int kWindowUnits = 2;   // decode work units of a 16-bit window tile (a body tile is one)
 constexpr int kRegions = 9;
 constexpr uint64_t kAlign = 256;  // every region starts on a 256-byte boundary
 constexpr uint64_t kHeaderBytes = 256;
@@ -101,7 +100,7 @@ struct DecodePlan {
   int B, H, Hq, G, D, T, body, n_sink_live, n_win, n_sink_cfg, ring;
   int ring0;             // ring slot of the oldest live window token (body mod ring)
   int n_splits, n_tiles, n_wtiles;  // partials, 64-token body tiles, 64-token window tiles
-  int units_per_split;   // work units (window tiles first, then body tiles) per split
+  int tiles_per_split;   // body tiles per split (the window tiles are dealt out separately)
   int dtype;
   float scale_log2;      // softmax scale times log2(e)
   uint8_t k_bits[KVQ_MAX_KV_HEADS];

@@ -573,6 +573,25 @@ REG_KC, REG_KM, REG_VC, REG_VM, REG_FL, REG_SK, REG_SV, REG_RK, REG_RV = range(N
 TILE = 64  # body tokens per key tile
 
 
+def value_stream_position(b: int, s: int, k: int) -> int:
+    """Position, inside a 32-code value stream of width b, of the code that step s (0..7), slot
+    k (0..3) of the device's value plan reads. Step s covers chunk s // 2 (8 tokens of one
+    channel), token u = 4 (s % 2) + k of it. This is the library's storage order (a format
+    choice, restated here from its definition): pairs of codes that one shift and one mask
+    separate for the device sit at fixed distances in the stream."""
+    if b == 2:
+        return 16 * (s // 4) + 2 * (s % 4) + k // 2 + 8 * (k % 2)
+    if b == 3:
+        low = [4, 9, 20, 21, 22, 23, 24, 25] if s % 2 else [0, 1, 2, 3, 11, 12, 13, 14]
+        a = low[2 * (s // 2) + k // 2]
+        return a + (0 if k % 2 == 0 else (6 if s % 2 else 5))
+    if b == 4:
+        return 8 * (s // 2) + 2 * (s % 2) + k // 2 + 4 * (k % 2)
+    if b == 8:
+        return 4 * s + k // 2 + 2 * (k % 2)
+    return 4 * s + k
+
+
 def _align(x, a=256):
     return (x + a - 1) // a * a
 
@@ -658,25 +677,44 @@ def expected_regions(oc: OracleCache, b: int, h: int):
         data[REG_VC][:raw.size] = raw
         mask[REG_VC][:raw.size] = True
     elif body:
-        words = pack(e["v_codes"][b], vb)                             # [j][c][vb]
+        # value tile (2 blocks of 32 tokens): decode lane l = 16 g4 + n (g4 = 2 * block + jp)
+        # holds D/32 streams of 32 codes; stream vg, step s, slot k is token 16 kk + 8 jp + u of
+        # channel 16 nb + n, with chunk c = s // 2, nb = 2 vg + c // 2, kk = c % 2,
+        # u = 4 (s % 2) + k; the stream sits at words (tile * 64 + l) * (D/32) * vb + vg * vb
+        codes = e["v_codes"][b]                                           # [j][c][32 tokens]
+        nv = D // GROUP
+        streams = np.zeros((nblk, 2, 16, nv, GROUP), dtype=np.int64)      # [j][jp][n][vg][pos]
+        jp_i = np.arange(2)[:, None, None]
+        n_i = np.arange(16)[None, :, None]
+        vg_i = np.arange(nv)[None, None, :]
+        for s_ in range(8):
+            for k_ in range(4):
+                c_ = s_ // 2
+                nb, kk, u = 2 * vg_i + c_ // 2, c_ % 2, 4 * (s_ % 2) + k_
+                ch = 16 * nb + n_i                                          # [1][16][nv]
+                tok = 16 * kk + 8 * jp_i + u                                # [2][1][1]
+                streams[..., value_stream_position(vb, s_, k_)] = codes[:, ch, tok]
+        words = pack(streams, vb)                                           # [j][jp][n][vg][vb]
         vc = np.zeros(sz[REG_VC] // 4, dtype=np.uint32)
         vm = np.zeros(sz[REG_VC] // 4, dtype=bool)
-        j = np.arange(nblk)
-        for c in range(D):
-            for k in range(vb):
-                idx = (j // 2) * (2 * D * vb) + (c * 2 + (j % 2)) * vb + k
-                vc[idx] = words[:, c, k]
-                vm[idx] = True
+        jb = np.arange(nblk)[:, None, None, None]
+        tile, blk = jb // 2, jb % 2
+        lane = (2 * blk + jp_i[None]) * 16 + n_i[None]                      # [j][2][16][1]
+        base = tile * 2 * D * vb + (lane * nv + vg_i[None]) * vb            # [j][2][16][nv]
+        for w in range(vb):
+            vc[(base + w).reshape(-1)] = words[..., w].reshape(-1)
+            vm[(base + w).reshape(-1)] = True
         data[REG_VC] = vc.view(np.uint8)
         mask[REG_VC] = np.repeat(vm, 4)
         meta = (e["v_s"][b].view(np.uint16).astype(np.uint32)
                 | (e["v_z"][b].view(np.uint16).astype(np.uint32) << np.uint32(16)))   # [j][c]
         m = np.zeros(sz[REG_VM] // 4, dtype=np.uint32)
         mm = np.zeros(sz[REG_VM] // 4, dtype=bool)
-        for c in range(D):
-            idx = (j // 2) * (2 * D) + c * 2 + (j % 2)
-            m[idx] = meta[:, c]
-            mm[idx] = True
+        jb = np.arange(nblk)[:, None]
+        c = np.arange(D)[None, :]
+        idx = (jb // 2) * 2 * D + (jb % 2) * D + (c % 16) * (D // 16) + c // 16
+        m[idx.reshape(-1)] = meta.reshape(-1)
+        mm[idx.reshape(-1)] = True
         data[REG_VM] = m.view(np.uint8)
         mask[REG_VM] = np.repeat(mm, 4)
     if cfg.quant == "hybrid" and nblk:

@@ -1,10 +1,11 @@
 """CPU check of the decode kernel's code-unpack plans (host logic, no GPU).
 
 The decode kernel feeds b-bit codes to the MFMA as fp16 subnormals cut out of the packed
-words with a shift and a mask per pair of codes. This compiles the kernel's own
-unpack_step / Slots templates for the host and checks, for every width 2..8, that slot k
-of step s holds code[chan(s, k)] << exp(s, k), inside the 10-bit mantissa, and that every
-element of a group is used exactly once.
+words with a shift and a mask per pair of codes. This compiles the kernel's own key and
+value plans (code_plans.h) for the host and checks, for every width 2..8, that slot k of
+step s holds code[chan(s, k)] << exp(s, k), inside the 10-bit mantissa, that every element
+of a group is used exactly once, and that the value plans' exponents repeat every two steps
+(one weight operand serves every chunk).
 """
 import os
 import subprocess
@@ -25,4 +26,4 @@ def test_unpack_plans(tmp_path):
     subprocess.run(cmd, check=True, capture_output=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
-    assert r.stdout.count("0 mismatches") == 7, r.stdout
+    assert r.stdout.count(": 0 mismatches") == 14, r.stdout

@@ -1,7 +1,8 @@
 // Host check of the slot plans: for every width, the fp16 bits that unpack_step puts in
 // slot k of step s equal code[chan(s,k)] << exp(s,k), stay inside the 10-bit subnormal
-// mantissa, and chan(., .) is a permutation of the group.
-#include "decode.hip"
+// mantissa, and chan(., .) is a permutation of the group. The value plans (unpack_step_v,
+// VSlots) must also give every chunk the same exponents: exp(s, k) depends on (s % 2, k) only.
+#include "code_plans.h"
 #include <cstdio>
 #include <random>
 using namespace kvq;
@@ -33,8 +34,41 @@ int check(std::mt19937& g) {
   printf("B=%d: %d mismatches\n", B, bad);
   return bad;
 }
+template <int B>
+int check_v(std::mt19937& g) {
+  int bad = 0;
+  for (int s = 2; s < 8; ++s)
+    for (int k = 0; k < 4; ++k)
+      if (VSlots<B>::exp(s, k) != VSlots<B>::exp(s & 1, k)) ++bad;
+  for (int trial = 0; trial < 2000; ++trial) {
+    uint32_t codes[32], w[B] = {};
+    for (int i = 0; i < 32; ++i) codes[i] = g() & ((1u << B) - 1);
+    if (trial == 0) for (int i = 0; i < 32; ++i) codes[i] = (1u << B) - 1;
+    for (int i = 0; i < 32; ++i)
+      for (int j = 0; j < B; ++j) {
+        const int k = i * B + j;
+        w[k / 32] |= ((codes[i] >> j) & 1u) << (k % 32);
+      }
+    int seen[32] = {};
+    for (int s = 0; s < 8; ++s) {
+      const u32x2 r = unpack_step_v<B>(w, 0, s);
+      const uint32_t halves[4] = {r[0] & 0xFFFF, r[0] >> 16, r[1] & 0xFFFF, r[1] >> 16};
+      for (int k = 0; k < 4; ++k) {
+        const int ch = VSlots<B>::chan(s, k), e = VSlots<B>::exp(s, k);
+        seen[ch]++;
+        const uint32_t want = codes[ch] << e;
+        if (halves[k] != want || want >= 1024u || e < 2) ++bad;
+      }
+    }
+    for (int i = 0; i < 32; ++i) if (seen[i] != 1) ++bad;
+  }
+  printf("value plan B=%d: %d mismatches\n", B, bad);
+  return bad;
+}
 int main() {
   std::mt19937 g(7);
   int bad = check<2>(g) + check<3>(g) + check<4>(g) + check<5>(g) + check<6>(g) + check<7>(g) + check<8>(g);
+  bad += check_v<2>(g) + check_v<3>(g) + check_v<4>(g) + check_v<5>(g) + check_v<6>(g) + check_v<7>(g) +
+         check_v<8>(g);
   return bad ? 1 : 0;
 }
