@@ -289,20 +289,31 @@ template <int D, int KB>
 __device__ __forceinline__ void key_phase(const Smem<D>& sm, const KTile<D, KB>& t, int lane, float kscale,
                                           float (&sc)[kMaxG]) {
   const int qi = lane & 3;
+  constexpr int NG = D / 32;
+  // the groups' MFMA chains are interleaved so that no MFMA waits for the one before it
+  float4_t acc[NG];
 #pragma unroll
-  for (int g = 0; g < D / 32; ++g) {
-    float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int g = 0; g < NG; ++g) acc[g] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+  for (int s = 0; s < 8; ++s)
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
       const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.qA[qi][(g * 8 + s) * 2]);
-      acc = mfma_f16(a, unpack_step<KB>(t.w, g * KB, s), acc);
+      acc[g] = mfma_f16(a, unpack_step<KB>(t.w, g * KB, s), acc[g]);
     }
-    const float sg = h2f(t.m[g] & 0xFFFFu) * kscale;
-    const float zg = h2f(t.m[g] >> 16);
+  // fp16 s, z straight into mixed-precision FMAs: sum_g s_g acc_g and sum_g z_g qsum_g
+  float t1[kMaxG], t2[kMaxG];
 #pragma unroll
-    for (int i = 0; i < kMaxG; ++i)
-      sc[i] = __builtin_fmaf(sg, acc[i], g == 0 ? zg * sm.qsum[i][0] : __builtin_fmaf(zg, sm.qsum[i][g], sc[i]));
+  for (int g = 0; g < NG; ++g) {
+    const float sg = h2f(t.m[g] & 0xFFFFu), zg = h2f(t.m[g] >> 16);
+#pragma unroll
+    for (int i = 0; i < kMaxG; ++i) {
+      t1[i] = g == 0 ? sg * acc[g][i] : __builtin_fmaf(sg, acc[g][i], t1[i]);
+      t2[i] = g == 0 ? zg * sm.qsum[i][0] : __builtin_fmaf(zg, sm.qsum[i][g], t2[i]);
+    }
   }
+#pragma unroll
+  for (int i = 0; i < kMaxG; ++i) sc[i] = __builtin_fmaf(kscale, t1[i], t2[i]);
 }
 
 // P.V of one packed tile on the 16x16x32 MFMA. Rows m = (block, hi/lo, query) = 8 blk + 4 hl
@@ -324,21 +335,37 @@ __device__ __forceinline__ void value_phase(const Smem<D>& sm, int wave, const V
   const u32x4 one = ones_chunk<VB>();
   float4_t d1 = mfma_f16_k32(a0, one, float4_t{0.0f, 0.0f, 0.0f, 0.0f});
   d1 = mfma_f16_k32(a1, one, d1);
+  // the body accumulators hold sum s D + z D1 2^-10 and sum D1; the code products carry
+  // 2^(kEp - 24) and the weight sums 2^(kEp - 14), so ob * kV and lb * kV1 are the sums
+  float4_t d1s;
+#pragma unroll
+  for (int i = 0; i < kMaxG; ++i) d1s[i] = d1[i] * (kV1 / kV);
   const bool live = (g4 >> 1) < nblk;  // the lane's block holds body tokens
+  // all MFMAs first (the kk = 1 step of a column block is issued after every kk = 0 one, so no
+  // MFMA waits for its accumulator), then the scale and zero of every column block
+  float4_t d[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int base = (nb >> 1) * VB, c0 = 2 * (nb & 1);  // stream, first chunk (kk = 0)
+    const int base = (nb >> 1) * VB, c0 = 2 * (nb & 1);  // stream, chunk of kk = 0
     const u32x2 p0 = unpack_step_v<VB>(t.w, base, 2 * c0), p1 = unpack_step_v<VB>(t.w, base, 2 * c0 + 1);
-    const u32x2 p2 = unpack_step_v<VB>(t.w, base, 2 * c0 + 2), p3 = unpack_step_v<VB>(t.w, base, 2 * c0 + 3);
-    float4_t d = mfma_f16_k32(a0, u32x4{p0.x, p0.y, p1.x, p1.y}, float4_t{0.0f, 0.0f, 0.0f, 0.0f});
-    d = mfma_f16_k32(a1, u32x4{p2.x, p2.y, p3.x, p3.y}, d);
-    const uint32_t mw = live ? t.m[nb] : 0u;
-    const float sv = h2f(mw & 0xFFFFu) * kV, zv = h2f(mw >> 16) * kV1;
-#pragma unroll
-    for (int i = 0; i < kMaxG; ++i) st.ob[nb][i] = __builtin_fmaf(sv, d[i], __builtin_fmaf(zv, d1[i], st.ob[nb][i]));
+    d[nb] = mfma_f16_k32(a0, u32x4{p0.x, p0.y, p1.x, p1.y}, float4_t{0.0f, 0.0f, 0.0f, 0.0f});
   }
 #pragma unroll
-  for (int i = 0; i < kMaxG; ++i) st.lb[i] = __builtin_fmaf(d1[i], kV1, st.lb[i]);
+  for (int nb = 0; nb < NB; ++nb) {
+    const int base = (nb >> 1) * VB, c1 = 2 * (nb & 1) + 1;  // chunk of kk = 1
+    const u32x2 p2 = unpack_step_v<VB>(t.w, base, 2 * c1), p3 = unpack_step_v<VB>(t.w, base, 2 * c1 + 1);
+    d[nb] = mfma_f16_k32(a1, u32x4{p2.x, p2.y, p3.x, p3.y}, d[nb]);
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const uint32_t mw = live ? t.m[nb] : 0u;
+    const float sv = h2f(mw & 0xFFFFu), zv = h2f(mw >> 16);
+#pragma unroll
+    for (int i = 0; i < kMaxG; ++i)
+      st.ob[nb][i] = __builtin_fmaf(sv, d[nb][i], __builtin_fmaf(zv, d1s[i], st.ob[nb][i]));
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxG; ++i) st.lb[i] += d1[i];
 }
 
 // Factor of the softmax weight of body token tb (0..31 of its block): 2^(kEp - e) with e the
@@ -758,7 +785,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int i = 0; i < kMaxG; ++i) {
     if (lane == 0) {
       sm.red_m[wave][i] = st.m[i];
-      sm.red_l[wave][i] = st.l[i] + st.lb[i];
+      sm.red_l[wave][i] = __builtin_fmaf(st.lb[i], (float)(1 << (14 - kEp)), st.l[i]);
     }
 #pragma unroll
     for (int hh = 0; hh < D / 64; ++hh) sm.red_o[wave][i][(D / 64) * lane + hh] = st.o[i][hh];
@@ -769,7 +796,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) {
       const float v = g4 == 0 ? st.ob[nb][0] : g4 == 1 ? st.ob[nb][1] : g4 == 2 ? st.ob[nb][2] : st.ob[nb][3];
-      sm.red_o[wave][g4][16 * nb + n] += v;
+      sm.red_o[wave][g4][16 * nb + n] += v * (float)(1 << (24 - kEp));
     }
   }
   __syncthreads();
