@@ -804,14 +804,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const size_t row0 = (size_t)b * p.Hq + (size_t)h * G;
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int i = idx / D, c = idx % D;
-    float ms = -INFINITY;
-    for (int w = 0; w < kWaves; ++w) ms = fmaxf(ms, sm.red_m[w][i]);
+    float mw[kWaves], ms = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      mw[w] = sm.red_m[w][i];
+      ms = fmaxf(ms, mw[w]);
+    }
     float oo = 0.0f, ll = 0.0f;
     if (ms != -INFINITY) {
+#pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float f = exp2f(sm.red_m[w][i] - ms);
-        oo += f * sm.red_o[w][i][c];
-        ll += f * sm.red_l[w][i];
+        const float f = __builtin_amdgcn_exp2f(mw[w] - ms);  // 0 for an empty wavefront (-inf)
+        oo = __builtin_fmaf(f, sm.red_o[w][i][c], oo);
+        ll = __builtin_fmaf(f, sm.red_l[w][i], ll);
       }
     }
     p.ws_o[((size_t)split * rows + row0 + i) * D + c] = oo;
@@ -820,7 +825,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       p.ws_ml[((size_t)split * rows + row0 + i) * 2 + 1] = ll;
     }
   }
-
 }
 
 // ---------------------------------------------------------------------------------------
