@@ -152,6 +152,19 @@ kvq_status kvq_decode_splitk(const kvq_cache* cache, const void* q_dev, int32_t 
 kvq_status kvq_decode_merge(const kvq_cache* cache, float* out_dev, int32_t n_splits,
                             void* workspace_dev, size_t ws_bytes, void* stream);
 
+/* One decode step (InnerQ Algorithm 1 with techniques (i)-(ii)): append n_new tokens (exactly
+ * as kvq_append) and run decode attention for the query over all len + n_new tokens (exactly
+ * as kvq_decode_attention), in one call. With n_new == 1 and the token past the sink, the
+ * split-K launch reads the window as it stands and takes the new token straight from
+ * k_dev / v_dev as one more softmax term, and the merge launch copies it into its recent-ring
+ * slot; the step is then those two launches, plus the quantize launch when a 32-token block
+ * leaves the window. Same arguments, ownership and rules as the two calls; arguments are
+ * checked before anything is enqueued. Asynchronous on stream; cache->len grows by n_new.
+ * k_dev / v_dev must stay valid until the merge launch has run. */
+kvq_status kvq_decode_step(kvq_cache* cache, const void* k_dev, const void* v_dev, int32_t n_new,
+                           const void* q_dev, float* out_dev, int32_t n_splits, float scale,
+                           void* workspace_dev, size_t ws_bytes, void* stream);
+
 /* Synchronize `stream`, read the sticky range flag; KVQ_ERR_RANGE if it is set. */
 kvq_status kvq_cache_check(const kvq_cache* cache, void* stream);
 

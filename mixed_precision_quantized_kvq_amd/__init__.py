@@ -18,7 +18,8 @@ import os
 __all__ = [
     "KvqError", "Config", "KVCache", "lib", "lib_path", "cache_bytes", "cache_init",
     "calibrate_fit", "calibrate_workspace_bytes", "allocate_bits", "append",
-    "decode_workspace_bytes", "decode_attention", "decode_splitk", "decode_merge", "cache_check",
+    "decode_workspace_bytes", "decode_attention", "decode_splitk", "decode_merge", "decode_step",
+    "cache_check",
     "region_offset", "last_error",
     "F16", "BF16", "QUANT_ASYM", "QUANT_HYBRID", "AXIS_KEY", "AXIS_VALUE", "ALLOC_CAP_W",
     "EXPORTS",
@@ -37,7 +38,8 @@ STATUS = {0: "OK", -1: "ERR_ARG", -2: "ERR_BUDGET", -3: "ERR_CAPACITY", -4: "ERR
 
 EXPORTS = ("kvq_cache_bytes", "kvq_cache_init", "kvq_calibrate_workspace_bytes",
            "kvq_calibrate_fit", "kvq_allocate_bits", "kvq_append", "kvq_decode_workspace_bytes",
-           "kvq_decode_attention", "kvq_decode_splitk", "kvq_decode_merge", "kvq_cache_check",
+           "kvq_decode_attention", "kvq_decode_splitk", "kvq_decode_merge", "kvq_decode_step",
+           "kvq_cache_check",
            "kvq_region_offset", "kvq_last_error")
 
 
@@ -108,6 +110,7 @@ def lib():
             "kvq_decode_attention": (I32, [KP, P, P, I32, ctypes.c_float, P, SZ, P]),
             "kvq_decode_splitk": (I32, [KP, P, I32, ctypes.c_float, P, SZ, P]),
             "kvq_decode_merge": (I32, [KP, P, I32, P, SZ, P]),
+            "kvq_decode_step": (I32, [KP, P, P, I32, P, P, I32, ctypes.c_float, P, SZ, P]),
             "kvq_cache_check": (I32, [KP, P]),
             "kvq_region_offset": (U64, [CP, I32, I32, I32, ctypes.POINTER(U64)]),
             "kvq_last_error": (ctypes.c_char_p, []),
@@ -227,6 +230,21 @@ def decode_attention(cache: KVCache, q, out, n_splits: int, workspace, scale: fl
     _check(lib().kvq_decode_attention(ctypes.byref(cache.handle), _dptr(q), _dptr(out), int(n_splits),
                                       float(scale), _dptr(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream)))
+
+
+def decode_step(cache: KVCache, k, v, q, out, n_splits: int, workspace, scale: float = 0.0, stream=None):
+    """Append k, v ([batch][n_kv_heads][n_new][head_dim] 16-bit) and decode q into out
+    (float32 [batch][n_q_heads][head_dim]) in one call."""
+    import torch
+    c = cache.cfg
+    assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape and k.dim() == 4
+    assert tuple(k.shape[:2]) == (c.batch, c.n_kv_heads) and k.shape[3] == c.head_dim
+    assert k.element_size() == 2 and v.element_size() == 2
+    assert q.is_contiguous() and out.is_contiguous() and out.dtype == torch.float32
+    assert tuple(q.shape) == (c.batch, c.n_q_heads, c.head_dim) and tuple(out.shape) == tuple(q.shape)
+    _check(lib().kvq_decode_step(ctypes.byref(cache.handle), _dptr(k), _dptr(v), int(k.shape[2]), _dptr(q),
+                                 _dptr(out), int(n_splits), float(scale), _dptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def decode_splitk(cache: KVCache, q, n_splits: int, workspace, scale: float = 0.0, stream=None):

@@ -133,6 +133,7 @@ struct Smem {
   float red_o[kWaves][kMaxG][D];
   float red_m[kWaves][kMaxG];
   float red_l[kWaves][kMaxG];
+  float new_s[kMaxG];  // fused decode step: scores of the appended token (log2 units)
   float qmax[kWaves];
 };
 
@@ -799,6 +800,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       sm.red_o[wave][g4][16 * nb + n] += v * (float)(1 << (24 - kEp));
     }
   }
+  // fused decode step: the token being appended is not in the cache yet (the merge launch
+  // writes it there). The last split adds it as one more softmax term (m = its score, l = 1,
+  // o = its value row); wavefront i scores it against query i
+  const bool fresh = p.new_k != nullptr && split == p.n_splits - 1;
+  const size_t kv_row = ((size_t)b * p.H + h) * D;
+  if (fresh && wave < G) {
+    const uint16_t* nk = reinterpret_cast<const uint16_t*>(p.new_k) + kv_row;
+    float acc = 0.0f;
+#pragma unroll
+    for (int hh = 0; hh < D / 64; ++hh) {
+      const int c = (D / 64) * lane + hh;
+      acc = __builtin_fmaf(widen(reinterpret_cast<const uint16_t*>(sm.qW[wave])[c], p.dtype),
+                           widen(nk[c], p.dtype), acc);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (lane == 0) sm.new_s[wave] = acc * p.scale_log2;
+  }
   __syncthreads();
   const size_t rows = (size_t)p.B * p.Hq;
   const size_t row0 = (size_t)b * p.Hq + (size_t)h * G;
@@ -810,6 +829,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       mw[w] = sm.red_m[w][i];
       ms = fmaxf(ms, mw[w]);
     }
+    const float sn = fresh ? sm.new_s[i] : -INFINITY;
+    ms = fmaxf(ms, sn);
     float oo = 0.0f, ll = 0.0f;
     if (ms != -INFINITY) {
 #pragma unroll
@@ -817,6 +838,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const float f = __builtin_amdgcn_exp2f(mw[w] - ms);  // 0 for an empty wavefront (-inf)
         oo = __builtin_fmaf(f, sm.red_o[w][i][c], oo);
         ll = __builtin_fmaf(f, sm.red_l[w][i], ll);
+      }
+      if (fresh) {
+        const float f = __builtin_amdgcn_exp2f(sn - ms);
+        oo = __builtin_fmaf(f, widen(reinterpret_cast<const uint16_t*>(p.new_v)[kv_row + c], p.dtype), oo);
+        ll += f;
       }
     }
     p.ws_o[((size_t)split * rows + row0 + i) * D + c] = oo;
@@ -841,6 +867,17 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const DecodePlan p) {
   const size_t rows = (size_t)p.B * p.Hq;
   const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (p.new_k != nullptr && idx < (size_t)p.B * p.H * (D / 4)) {
+    // fused decode step: the appended token enters its ring slot once every read of the ring
+    // by the decode launch is done (one 16-byte piece of its key or value row per thread)
+    const size_t bh = idx / (D / 4);
+    const int piece = (int)(idx % (D / 4));
+    const bool kv = piece >= D / 8;
+    const uint4 x = reinterpret_cast<const uint4*>(kv ? p.new_v : p.new_k)[bh * (D / 8) + piece % (D / 8)];
+    const uint64_t ring_off = p.off[bh * kRegions + (kv ? RV : RK)];
+    uint4* dst = reinterpret_cast<uint4*>(const_cast<char*>(p.blob) + ring_off + (size_t)p.new_slot * D * 2);
+    dst[piece % (D / 8)] = x;
+  }
   if (idx >= rows * D) return;
   const size_t r = idx / D;
   const int parts = p.n_splits;

@@ -244,6 +244,70 @@ kvq_status kvq_decode_merge(const kvq_cache* cache, float* out_dev, int32_t n_sp
   return check_launch(launch_decode_merge(p, stream), "merge launch");
 }
 
+kvq_status kvq_decode_step(kvq_cache* cache, const void* k_dev, const void* v_dev, int32_t n_new,
+                           const void* q_dev, float* out_dev, int32_t n_splits, float scale, void* ws,
+                           size_t ws_bytes, void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (!q_dev || !out_dev) return fail(KVQ_ERR_ARG, "NULL pointer");
+  const kvq_config& c = cache->cfg;
+  const int len0 = cache->len, len1 = len0 + n_new;
+  const bool fused = n_new == 1 && len0 >= c.n_sink;
+  if (!fused) {
+    st = kvq_append(cache, k_dev, v_dev, n_new, stream);
+    if (st != KVQ_OK) return st;
+    return kvq_decode_attention(cache, q_dev, out_dev, n_splits, scale, ws, ws_bytes, stream);
+  }
+  if (!k_dev || !v_dev) return fail(KVQ_ERR_ARG, "NULL input");
+  if (!aligned(k_dev, 16) || !aligned(v_dev, 16)) return fail(KVQ_ERR_ARG, "inputs must be 16-byte aligned");
+  if ((int64_t)len1 > c.capacity) return fail(KVQ_ERR_CAPACITY, "append exceeds capacity");
+  // validate the decode arguments on the cache as it will be after the append (nothing has
+  // been enqueued yet, and cache->len is restored if they are rejected)
+  kvq_cache after = *cache;
+  after.len = len1;
+  DecodePlan d;
+  st = decode_plan(&after, q_dev, out_dev, n_splits, scale, ws, ws_bytes, d);
+  if (st != KVQ_OK) return st;
+  AppendPlan a{};
+  a.k_in = k_dev;
+  a.v_in = v_dev;
+  a.blob = static_cast<char*>(cache->dev);
+  a.off = table_ptr(cache);
+  a.range_flag = flag_ptr(cache);
+  a.B = c.batch;
+  a.H = c.n_kv_heads;
+  a.D = c.head_dim;
+  a.n_new = 1;
+  a.len0 = len0;
+  a.len1 = len1;
+  a.body0 = (int)body_len(len0, c.n_sink, c.n_recent);
+  a.body1 = (int)body_len(len1, c.n_sink, c.n_recent);
+  a.n_sink = c.n_sink;
+  a.n_recent = c.n_recent;
+  a.dtype = c.dtype;
+  a.hybrid = c.quant == KVQ_QUANT_HYBRID;
+  std::memcpy(a.k_bits, c.k_bits, sizeof(a.k_bits));
+  std::memcpy(a.v_bits, c.v_bits, sizeof(a.v_bits));
+  if (a.body1 > a.body0) {  // a block leaves the window: quantize it first
+    st = check_launch(launch_append_flush(a, stream), "append flush launch");
+    if (st != KVQ_OK) return st;
+  }
+  if (d.n_win > 0) {
+    // the new token is the last window token: the decode kernel takes it from the inputs as
+    // one more softmax term, reads the window as it stands before the append, and writes the
+    // token into its ring slot
+    d.new_k = k_dev;
+    d.new_v = v_dev;
+    d.new_slot = (len1 - 1 - c.n_sink) % ring_slots(c.n_recent);
+    d.n_win -= 1;
+    d.n_wtiles = (d.n_sink_live + d.n_win + kTile - 1) / kTile;
+  }
+  cache->len = len1;
+  st = check_launch(launch_decode_splitk(d, stream), "decode launch");
+  if (st != KVQ_OK) return st;
+  return check_launch(launch_decode_merge(d, stream), "merge launch");
+}
+
 kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q_dev, float* out_dev,
                                 int32_t n_splits, float scale, void* ws, size_t ws_bytes,
                                 void* stream) {

@@ -103,6 +103,13 @@ struct DecodePlan {
   int tiles_per_split;   // body tiles per split (the window tiles are dealt out separately)
   int dtype;
   float scale_log2;      // softmax scale times log2(e)
+  // fused decode step: the token being appended ([B][H][1][D], 16-bit), not counted in n_win.
+  // The last split of each (row, head) attends to it; the merge launch writes it into ring
+  // slot new_slot.
+  // Null when not fused.
+  const void* new_k;
+  const void* new_v;
+  int new_slot;
   uint8_t k_bits[KVQ_MAX_KV_HEADS];
   uint8_t v_bits[KVQ_MAX_KV_HEADS];
 };

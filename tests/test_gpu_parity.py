@@ -197,6 +197,64 @@ def test_long_window_across_splits(T):
     check_decode(cache, oc, q, splits=(1, 2, 3, 6, 40))
 
 
+@pytest.mark.parametrize("n_recent,n_sink", [(40, 3), (0, 0), (64, 5)])
+def test_decode_step_sequence(n_recent, n_sink):
+    # token-by-token decode steps (append + decode in one call): every step's output against
+    # the oracle on the whole prefix, crossing several 32-token flushes and the sink; at the end
+    # the cache bytes equal a bulk-built cache's
+    say(f"case: decode_step sequence n_recent={n_recent} n_sink={n_sink}")
+    rng = np.random.default_rng(80 + n_recent)
+    T0, steps = 90, 75
+    T = T0 + steps
+    ocfg = O.CacheConfig(2, 2, 4, 128, T + 8, n_sink, n_recent, "bf16", "hybrid", (3, 2), (2, 4))
+    k = workloads.random_raw16(rng, (2, 2, T, 128), "bf16", 2.0)
+    v = workloads.random_raw16(rng, (2, 2, T, 128), "bf16")
+    qs = workloads.random_raw16(rng, (steps, 2, 4, 128), "bf16")
+    cache = kvq.KVCache(lib_cfg(kvq, ocfg), device=DEV)
+    if T0:
+        kvq.append(cache, to_dev(np.ascontiguousarray(k[:, :, :T0])), to_dev(np.ascontiguousarray(v[:, :, :T0])))
+    out = torch.empty((2, 4, 128), dtype=torch.float32, device=DEV)
+    ws = torch.zeros(kvq.decode_workspace_bytes(cache, 3), dtype=torch.uint8, device=DEV)
+    worst = 0.0
+    for s in range(steps):
+        t = T0 + s
+        kvq.decode_step(cache, to_dev(np.ascontiguousarray(k[:, :, t:t + 1])),
+                        to_dev(np.ascontiguousarray(v[:, :, t:t + 1])), to_dev(np.ascontiguousarray(qs[s])),
+                        out, 3, ws)
+        assert cache.len == t + 1
+        if s % 4 == 0 or s == steps - 1:
+            ocfg_t = O.CacheConfig(2, 2, 4, 128, T + 8, n_sink, n_recent, "bf16", "hybrid", (3, 2), (2, 4))
+            oc = O.build_cache(k[:, :, :t + 1], v[:, :, :t + 1], ocfg_t)
+            ok, err, bound = within_tol(out.cpu().numpy(), O.decode(oc, qs[s]))
+            worst = max(worst, err / bound)
+            assert ok, (s, err, bound)
+    say(f"    worst error / bound over the steps: {worst:.3e}")
+    kvq.cache_check(cache)
+    assert_regions_equal(cache, O.build_cache(k, v, ocfg))
+
+
+def test_decode_step_unfused_paths():
+    # several tokens at once, and tokens that land in the sink, take the append + decode path
+    say("case: decode_step with n_new > 1 and sink tokens")
+    rng = np.random.default_rng(90)
+    ocfg = O.CacheConfig(1, 2, 2, 64, 300, 6, 16, "fp16", "asym", (2, 4), (4, 2))
+    k = workloads.random_raw16(rng, (1, 2, 120, 64), "fp16")
+    v = workloads.random_raw16(rng, (1, 2, 120, 64), "fp16")
+    q = workloads.random_raw16(rng, (1, 2, 64), "fp16")
+    cache = kvq.KVCache(lib_cfg(kvq, ocfg), device=DEV)
+    out = torch.empty((1, 2, 64), dtype=torch.float32, device=DEV)
+    ws = torch.zeros(kvq.decode_workspace_bytes(cache, 2), dtype=torch.uint8, device=DEV)
+    t = 0
+    for n in (1, 1, 3, 1, 1, 1, 40, 1, 72):
+        kvq.decode_step(cache, to_dev(np.ascontiguousarray(k[:, :, t:t + n])),
+                        to_dev(np.ascontiguousarray(v[:, :, t:t + n])), to_dev(q), out, 2, ws)
+        t += n
+        oc = O.build_cache(k[:, :, :t], v[:, :, :t], ocfg)
+        ok, err, bound = within_tol(out.cpu().numpy(), O.decode(oc, q))
+        assert ok, (t, err, bound)
+    assert_regions_equal(cache, O.build_cache(k, v, ocfg))
+
+
 def test_explicit_scale():
     rng = np.random.default_rng(40)
     ocfg = O.CacheConfig(1, 1, 4, 128, 500, 4, 64, "bf16", "asym", (3,), (3,))
