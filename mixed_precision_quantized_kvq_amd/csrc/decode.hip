@@ -69,6 +69,13 @@ __device__ __forceinline__ float4_t mfma16(u32x2 a, u32x2 b, float4_t c) {
   else return mfma_f16(a, b, c);
 }
 
+// Width of head h from a word-aligned per-head byte table in the kernel arguments, read a
+// word at a time: a scalar load for uniform h, where a byte load would take the vector path.
+__device__ __forceinline__ int head_bits(const uint8_t* table, int h) {
+  const uint32_t w = reinterpret_cast<const uint32_t*>(table)[h >> 2];
+  return (int)((w >> (8 * (h & 3))) & 0xFFu);
+}
+
 __device__ __forceinline__ float h2f(uint32_t bits16) { return __half2float(__ushort_as_half((uint16_t)bits16)); }
 __device__ __forceinline__ uint32_t f2h(float x) { return (uint32_t)__half_as_ushort(__float2half_rn(x)); }
 __device__ __forceinline__ uint32_t f2bf(float x) {  // round to nearest even (finite x)
@@ -568,7 +575,7 @@ __device__ __forceinline__ void value_tile_q(Smem<D>& sm, int wave, const BodySr
 template <int D>
 __device__ __forceinline__ void mixed_body_loop(Smem<D>& sm, const DecodePlan& p, const uint64_t* off, int t0, int t1, int lane,
                                 int wave, float kscale, WaveState<D>& st) {
-  const int kb = p.k_bits[blockIdx.y], vb = p.v_bits[blockIdx.y];
+  const int kb = head_bits(p.k_bits, blockIdx.y), vb = head_bits(p.v_bits, blockIdx.y);
   const bool bf16 = p.dtype == KVQ_BF16;
   const uint16_t* kr = reinterpret_cast<const uint16_t*>(p.blob + off[KC]);
   const uint16_t* vr = reinterpret_cast<const uint16_t*>(p.blob + off[VC]);
@@ -644,7 +651,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.G;
-  const int kb = p.k_bits[h], vb = p.v_bits[h];
+  const int kb = head_bits(p.k_bits, h), vb = head_bits(p.v_bits, h);
   const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)b * p.Hq + (size_t)h * G) * D;
 
   // ---- q operands in LDS: raw 16-bit copy, the per-group sums of q, and the fp16 key
@@ -707,9 +714,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const uint64_t* off = p.off + ((size_t)b * p.H + h) * kRegions;
 
   // ---- this workgroup's work: body tiles [t0, t1) round-robin over the wavefronts, and the
-  // window tiles w = split + n_splits * k (k = 0, 1, ...), tile k going to wavefront
-  // kWaves - 1 - k % kWaves (the last wavefronts have the fewest body tiles). A wavefront's
-  // first window tile is loaded before the query prologue, so its latency is hidden.
+  // window units w = split + n_splits * k (k = 0, 1, ...) of kWinTile tokens, unit k going to
+  // wavefront kWaves - 1 - k % kWaves (the last wavefronts have the fewest body tiles). Small
+  // units spread the 16-bit window over many wavefronts instead of loading a few of them
+  // with several body tiles' worth of bytes. A wavefront's first window unit is loaded
+  // before the query prologue, so its latency is hidden.
   const int t0 = split * p.tiles_per_split, t1 = min(p.n_tiles, t0 + p.tiles_per_split);
   const int n_wtok = p.n_sink_live + p.n_win;
   const int w_first = split + p.n_splits * (kWaves - 1 - wave);  // k = kWaves - 1 - wave
@@ -727,17 +736,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   auto krow = [=](int u) { return u < nsl ? sk + (size_t)u * D : rk + (size_t)slot(u) * D; };
   auto vrow = [=](int u) { return u < nsl ? sv + (size_t)u * D : rv + (size_t)slot(u) * D; };
   const bool has_w = w_first < p.n_wtiles;
+  auto wlim = [=](int w) { return min(n_wtok, (w + 1) * kWinTile); };  // end of window unit w
   // issue the value loads of the first window tile (before the prologue); compute the window
   auto window_issue = [&](Rows16<D>& wt) {
-    if (has_w) rows16_issue<D>(wt, w_first * kTile, n_wtok, lane, vrow);
+    if (has_w) rows16_issue<D>(wt, w_first * kWinTile, wlim(w_first), lane, vrow);
   };
   auto window = [&](const Rows16<D>& wt) {
     if (!has_w) return;
-    rows16_compute<D>(sm, p, wt, w_first * kTile, n_wtok, lane, wave, st, krow);
+    rows16_compute<D>(sm, p, wt, w_first * kWinTile, wlim(w_first), lane, wave, st, krow);
     for (int w = w_first + kWaves * p.n_splits; w < p.n_wtiles; w += kWaves * p.n_splits) {
       Rows16<D> r;
-      rows16_issue<D>(r, w * kTile, n_wtok, lane, vrow);
-      rows16_compute<D>(sm, p, r, w * kTile, n_wtok, lane, wave, st, krow);
+      rows16_issue<D>(r, w * kWinTile, wlim(w), lane, vrow);
+      rows16_compute<D>(sm, p, r, w * kWinTile, wlim(w), lane, wave, st, krow);
     }
   };
 

@@ -212,7 +212,7 @@ kvq_status decode_plan(const kvq_cache* cache, const void* q_dev, float* out_dev
   p.n_splits = n_splits;
   p.ring0 = p.body % p.ring;
   p.n_tiles = (p.body + kTile - 1) / kTile;
-  p.n_wtiles = (p.n_sink_live + p.n_win + kTile - 1) / kTile;
+  p.n_wtiles = (p.n_sink_live + p.n_win + kWinTile - 1) / kWinTile;
   p.tiles_per_split = (p.n_tiles + n_splits - 1) / n_splits;
   p.dtype = c.dtype;
   const float s = scale > 0.0f ? scale : 1.0f / std::sqrt((float)c.head_dim);
@@ -300,7 +300,7 @@ kvq_status kvq_decode_step(kvq_cache* cache, const void* k_dev, const void* v_de
     d.new_v = v_dev;
     d.new_slot = (len1 - 1 - c.n_sink) % ring_slots(c.n_recent);
     d.n_win -= 1;
-    d.n_wtiles = (d.n_sink_live + d.n_win + kTile - 1) / kTile;
+    d.n_wtiles = (d.n_sink_live + d.n_win + kWinTile - 1) / kWinTile;
   }
   cache->len = len1;
   st = check_launch(launch_decode_splitk(d, stream), "decode launch");

@@ -13,6 +13,12 @@ namespace kvq {
 
 constexpr int kGroup = 32;        // quantization group size (keys: channels, values: tokens)
 constexpr int kTile = 64;         // body tokens per key tile (one wavefront, one token per lane)
+// 16-bit window tokens per unit of decode work (a unit is dealt to one wavefront; units
+// smaller than a body tile spread the window's bytes over many wavefronts)
+#ifndef KVQ_WIN_TILE
+#define KVQ_WIN_TILE 16
+#endif
+constexpr int kWinTile = KVQ_WIN_TILE;
 constexpr int kRegions = 9;
 constexpr uint64_t kAlign = 256;  // every region starts on a 256-byte boundary
 constexpr uint64_t kHeaderBytes = 256;
@@ -75,8 +81,8 @@ struct AppendPlan {
   int body0, body1;      // body lengths before / after
   int n_sink, n_recent;
   int dtype, hybrid;
-  uint8_t k_bits[KVQ_MAX_KV_HEADS];
-  uint8_t v_bits[KVQ_MAX_KV_HEADS];
+  alignas(4) uint8_t k_bits[KVQ_MAX_KV_HEADS];  // word-aligned: kernels read them a word at a time
+  alignas(4) uint8_t v_bits[KVQ_MAX_KV_HEADS];
 };
 int launch_append_flush(const AppendPlan& p, void* stream);
 int launch_append_window(const AppendPlan& p, void* stream);
@@ -99,7 +105,7 @@ struct DecodePlan {
   float* ws_ml;          // [P][B][Hq][2]
   int B, H, Hq, G, D, T, body, n_sink_live, n_win, n_sink_cfg, ring;
   int ring0;             // ring slot of the oldest live window token (body mod ring)
-  int n_splits, n_tiles, n_wtiles;  // partials, 64-token body tiles, 64-token window tiles
+  int n_splits, n_tiles, n_wtiles;  // partials, 64-token body tiles, kWinTile-token window units
   int tiles_per_split;   // body tiles per split (the window tiles are dealt out separately)
   int dtype;
   float scale_log2;      // softmax scale times log2(e)
@@ -110,10 +116,11 @@ struct DecodePlan {
   const void* new_k;
   const void* new_v;
   int new_slot;
-  uint8_t k_bits[KVQ_MAX_KV_HEADS];
-  uint8_t v_bits[KVQ_MAX_KV_HEADS];
+  alignas(4) uint8_t k_bits[KVQ_MAX_KV_HEADS];  // word-aligned: kernels read them a word at a time
+  alignas(4) uint8_t v_bits[KVQ_MAX_KV_HEADS];
 };
 int launch_decode_splitk(const DecodePlan& p, void* stream);
+
 int launch_decode_merge(const DecodePlan& p, void* stream);
 
 }  // namespace kvq
