@@ -104,6 +104,18 @@ __device__ __forceinline__ float wave_max(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Sums over the four 16-lane rows of a, b, c, d at once: lane (r, n) of the result holds
+// a, c, b, d summed over the rows at lane n, for r = 0, 1, 2, 3 (two 32-lane swaps fold the
+// halves, one 16-lane swap folds the rows; all VALU, no LDS).
+__device__ __forceinline__ float sum4(float a, float b, float c, float d) {
+  const auto ab = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const auto cd = __builtin_amdgcn_permlane32_swap(__float_as_uint(c), __float_as_uint(d), false, false);
+  const float z = __uint_as_float(ab[0]) + __uint_as_float(ab[1]);  // rows: a0+a2, a1+a3, b0+b2, b1+b3
+  const float w = __uint_as_float(cd[0]) + __uint_as_float(cd[1]);
+  const auto zw = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(w), false, false);
+  return __uint_as_float(zw[0]) + __uint_as_float(zw[1]);
+}
+
 // LDS traffic of one wavefront is executed in issue order, so a wavefront reading back what
 // it wrote only needs the compiler not to reorder the accesses.
 __device__ __forceinline__ void wave_lds_sync() { __asm__ __volatile__("" ::: "memory"); }
@@ -780,35 +792,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 
   // ---- combine the wavefronts of this workgroup into one partial (m, l, o). The packed-body
-  // sums of the four lane groups (block, hi/lo) are added first; lane (g4, n) then owns
-  // query g4 of channels 16 nb + n.
+  // sums of the four lane groups (block, hi/lo) are added with lane swaps (sum4), after which
+  // lane (r, n) holds query qr of channels 16 nb + n; the 16-bit-row sums (lane = channel
+  // pair) are added on top in LDS by the wavefronts that have any.
+  const int r4 = lane >> 4, n16 = lane & 15;
+  const int qr = ((r4 & 1) << 1) | (r4 >> 1);
+  const float lbr = sum4(st.lb[0], st.lb[1], st.lb[2], st.lb[3]);
 #pragma unroll
-  for (int i = 0; i < kMaxG; ++i) {
-    st.lb[i] += __shfl_xor(st.lb[i], 16, 64);
-    st.lb[i] += __shfl_xor(st.lb[i], 32, 64);
-#pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) {
-      st.ob[nb][i] += __shfl_xor(st.ob[nb][i], 16, 64);
-      st.ob[nb][i] += __shfl_xor(st.ob[nb][i], 32, 64);
-    }
+  for (int nb = 0; nb < D / 16; ++nb) {
+    const float v = sum4(st.ob[nb][0], st.ob[nb][1], st.ob[nb][2], st.ob[nb][3]);
+    sm.red_o[wave][qr][16 * nb + n16] = v * (float)(1 << (24 - kEp));
   }
-#pragma unroll
-  for (int i = 0; i < kMaxG; ++i) {
-    if (lane == 0) {
-      sm.red_m[wave][i] = st.m[i];
-      sm.red_l[wave][i] = __builtin_fmaf(st.lb[i], (float)(1 << (14 - kEp)), st.l[i]);
-    }
-#pragma unroll
-    for (int hh = 0; hh < D / 64; ++hh) sm.red_o[wave][i][(D / 64) * lane + hh] = st.o[i][hh];
+  if (n16 == 0) {
+    const float mq = qr == 0 ? st.m[0] : qr == 1 ? st.m[1] : qr == 2 ? st.m[2] : st.m[3];
+    const float lq = qr == 0 ? st.l[0] : qr == 1 ? st.l[1] : qr == 2 ? st.l[2] : st.l[3];
+    sm.red_m[wave][qr] = mq;
+    sm.red_l[wave][qr] = __builtin_fmaf(lbr, (float)(1 << (14 - kEp)), lq);
   }
-  wave_lds_sync();
-  {
-    const int g4 = lane >> 4, n = lane & 15;
+  if (has_w || !(kb <= 4 && vb <= 4)) {  // 16-bit rows seen: st.o holds sums
+    wave_lds_sync();
 #pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) {
-      const float v = g4 == 0 ? st.ob[nb][0] : g4 == 1 ? st.ob[nb][1] : g4 == 2 ? st.ob[nb][2] : st.ob[nb][3];
-      sm.red_o[wave][g4][16 * nb + n] += v * (float)(1 << (24 - kEp));
-    }
+    for (int i = 0; i < kMaxG; ++i)
+#pragma unroll
+      for (int hh = 0; hh < D / 64; ++hh) sm.red_o[wave][i][(D / 64) * lane + hh] += st.o[i][hh];
   }
   // fused decode step: the token being appended is not in the cache yet (the merge launch
   // writes it there). The last split adds it as one more softmax term (m = its score, l = 1,
