@@ -63,6 +63,15 @@ __device__ __forceinline__ float4_t mfma_f16_k32(u32x4 a, u32x4 b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0,
                                                 0, 0);
 }
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+template <bool BF16>
+__device__ __forceinline__ float4_t mfma_k32(u32x4 a, u32x4 b, float4_t c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                   0, 0, 0);
+  else
+    return mfma_f16_k32(a, b, c);
+}
 template <bool BF16>
 __device__ __forceinline__ float4_t mfma16(u32x2 a, u32x2 b, float4_t c) {
   if constexpr (BF16) return mfma_bf16(a, b, c);
@@ -519,6 +528,85 @@ __device__ __forceinline__ void rows16_compute(Smem<D>& sm, const DecodePlan& p,
   }
   wave_lds_sync();
 }
+// One window unit: kWinTile = 16 tokens of 16-bit rows, all of its loads in 32 registers.
+// Keys are read cooperatively (lane (t, j): token t = lane % 16, channels 32 s + 8 j .. +7 of
+// step s), which is the B operand of a 16x16x32 MFMA whose rows 0..3 are the queries; values
+// are whole rows, lane = channel pair (D = 128) or channel (D = 64), as for 16-bit tiles.
+template <int D>
+struct WinUnit {
+  u32x4 k[D / 32];
+  uint32_t v[kWinTile];
+};
+template <int D, class KRowOf, class VRowOf>
+__device__ __forceinline__ void win_issue(WinUnit<D>& w, int base, int n_valid, int lane, KRowOf krow, VRowOf vrow) {
+  static_assert(kWinTile == 16, "window units are 16 tokens (one MFMA column block)");
+  const uint16_t* kr = krow(base + min(lane & 15, n_valid - 1)) + 8 * (lane >> 4);
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) w.k[s] = *reinterpret_cast<const u32x4*>(kr + 32 * s);
+#pragma unroll
+  for (int k = 0; k < kWinTile; ++k) {
+    const uint16_t* r = vrow(base + min(k, n_valid - 1));
+    if constexpr (D == 128)
+      w.v[k] = *reinterpret_cast<const uint32_t*>(r + 2 * lane);
+    else
+      w.v[k] = r[lane];
+  }
+}
+template <int D, bool BF16>
+__device__ __forceinline__ void win_compute_t(Smem<D>& sm, const DecodePlan& p, const WinUnit<D>& w, int n_valid,
+                                              int lane, int wave, WaveState<D>& st) {
+  // scores: lane t < 16 ends with q_i . k_t for the queries i = 0..3 of rows 0..3
+  const int i = lane & 15, j = lane >> 4;
+  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) {
+    const u32x4 a = i < kMaxG ? *reinterpret_cast<const u32x4*>(&sm.qW[i][16 * s + 4 * j]) : u32x4{0u, 0u, 0u, 0u};
+    acc = mfma_k32<BF16>(a, w.k[s], acc);
+  }
+  float sc[kMaxG];
+#pragma unroll
+  for (int r = 0; r < kMaxG; ++r) sc[r] = acc[r] * p.scale_log2;
+  softmax_rows16<D>(sm, wave, lane, lane < n_valid, sc, st, lane & 31, 1.0f, BF16);
+  // P.V over the unit's 16 rows: 4 steps of 4 tokens on the 4x4x4 MFMA (lane = channel)
+  const int qi = lane & 3;
+  const uint32_t one1 = BF16 ? 0x3F80u : 0x3C00u;
+  const u32x2 one = u32x2{one1 | (one1 << 16), one1 | (one1 << 16)};
+  float4_t o[D / 64], l1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h) o[h] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < kWinTile / 4; ++s) {
+    const u32x2 ahi = *reinterpret_cast<const u32x2*>(&sm.pw[wave][0][qi][2 * s]);
+    const u32x2 alo = *reinterpret_cast<const u32x2*>(&sm.pw[wave][1][qi][2 * s]);
+    const uint32_t* r = &w.v[4 * s];
+    const u32x2 b0 = u32x2{pair16<0>(r[0], r[1]), pair16<0>(r[2], r[3])};
+    o[0] = mfma16<BF16>(ahi, b0, o[0]);
+    o[0] = mfma16<BF16>(alo, b0, o[0]);
+    if constexpr (D == 128) {
+      const u32x2 b1 = u32x2{pair16<1>(r[0], r[1]), pair16<1>(r[2], r[3])};
+      o[1] = mfma16<BF16>(ahi, b1, o[1]);
+      o[1] = mfma16<BF16>(alo, b1, o[1]);
+    }
+    l1 = mfma16<BF16>(ahi, one, l1);
+    l1 = mfma16<BF16>(alo, one, l1);
+  }
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h)
+#pragma unroll
+    for (int r = 0; r < kMaxG; ++r) st.o[r][h] += o[h][r];
+#pragma unroll
+  for (int r = 0; r < kMaxG; ++r) st.l[r] += l1[r];
+  wave_lds_sync();
+}
+template <int D>
+__device__ __forceinline__ void win_compute(Smem<D>& sm, const DecodePlan& p, const WinUnit<D>& w, int n_valid,
+                                            int lane, int wave, WaveState<D>& st) {
+  if (p.dtype == KVQ_BF16)
+    win_compute_t<D, true>(sm, p, w, n_valid, lane, wave, st);
+  else
+    win_compute_t<D, false>(sm, p, w, n_valid, lane, wave, st);
+}
+
 // Quantized keys and values, both widths fixed: the loads of the next tile are issued before
 // the current tile is computed.
 template <int D, int KB, int VB, class Prologue, class WindowIssue, class Window>
@@ -531,7 +619,7 @@ __device__ __forceinline__ void body_loop(Smem<D>& sm, const DecodePlan& p, cons
   // two register buffers: the next tile is in flight while this one is computed
   KTile<D, KB> kt[2];
   VTile<D, VB> vt[2];
-  Rows16<D> wt;
+  WinUnit<D> wt;
   window_issue(wt);
   if (any) {  // the first tile is in flight while the query operands are prepared
     load_k<D, KB>(kt[0], src, tile, lane);
@@ -669,14 +757,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // ---- q operands in LDS: raw 16-bit copy, the per-group sums of q, and the fp16 key
   // operand in slot order with q scaled by 2^Eq so that max|q| * 2^Eq lies in [2^14, 2^15).
   // Returns the key-score factor scale_log2 * 2^(24 - Eq). Every wavefront calls it once.
+  // the region table of this (row, head), read once into scalar registers ahead of anything
+  // the compiler must treat as a possible store
+  const uint64_t* tab = p.off + ((size_t)b * p.H + h) * kRegions;
+  uint64_t off[kRegions];
+#pragma unroll
+  for (int r = 0; r < kRegions; ++r) off[r] = tab[r];
+  // the query loads are issued first, so they return ahead of the window and body loads
+  // issued next and the prologue does not wait for those
+  constexpr int E = kMaxG * D / kThreads;  // consecutive elements per thread (2 or 1)
+  const int i0 = (tid * E) / D;
+  uint32_t qraw[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) qraw[e] = i0 < G ? q[(size_t)i0 * D + (tid * E + e) % D] : 0u;
+  issue_barrier();
   auto prologue = [&]() -> float {
-    constexpr int E = kMaxG * D / kThreads;  // consecutive elements per thread (2 or 1)
     float qmax = 0.0f, qs = 0.0f;
-    const int i0 = (tid * E) / D;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int c = (tid * E + e) % D;
-      const uint32_t raw = i0 < G ? q[(size_t)i0 * D + c] : 0u;
+      const uint32_t raw = qraw[e];
       reinterpret_cast<uint16_t*>(sm.qW[i0])[c] = (uint16_t)raw;
       const float v = widen(raw, p.dtype);
       qmax = fmaxf(qmax, fabsf(v));
@@ -723,7 +823,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) st.ob[nb][i] = 0.0f;
   }
-  const uint64_t* off = p.off + ((size_t)b * p.H + h) * kRegions;
 
   // ---- this workgroup's work: body tiles [t0, t1) round-robin over the wavefronts, and the
   // window units w = split + n_splits * k (k = 0, 1, ...) of kWinTile tokens, unit k going to
@@ -750,21 +849,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const bool has_w = w_first < p.n_wtiles;
   auto wlim = [=](int w) { return min(n_wtok, (w + 1) * kWinTile); };  // end of window unit w
   // issue the value loads of the first window tile (before the prologue); compute the window
-  auto window_issue = [&](Rows16<D>& wt) {
-    if (has_w) rows16_issue<D>(wt, w_first * kWinTile, wlim(w_first), lane, vrow);
+  auto window_issue = [&](WinUnit<D>& wt) {
+    if (has_w) win_issue<D>(wt, w_first * kWinTile, wlim(w_first) - w_first * kWinTile, lane, krow, vrow);
   };
-  auto window = [&](const Rows16<D>& wt) {
+  auto window = [&](const WinUnit<D>& wt) {
     if (!has_w) return;
-    rows16_compute<D>(sm, p, wt, w_first * kWinTile, wlim(w_first), lane, wave, st, krow);
+    win_compute<D>(sm, p, wt, wlim(w_first) - w_first * kWinTile, lane, wave, st);
     for (int w = w_first + kWaves * p.n_splits; w < p.n_wtiles; w += kWaves * p.n_splits) {
-      Rows16<D> r;
-      rows16_issue<D>(r, w * kWinTile, wlim(w), lane, vrow);
-      rows16_compute<D>(sm, p, r, w * kWinTile, wlim(w), lane, wave, st, krow);
+      WinUnit<D> r;
+      win_issue<D>(r, w * kWinTile, wlim(w) - w * kWinTile, lane, krow, vrow);
+      win_compute<D>(sm, p, r, wlim(w) - w * kWinTile, lane, wave, st);
     }
   };
 
   if (kb == 16 && vb == 16) {
-    Rows16<D> wt;
+    WinUnit<D> wt;
     window_issue(wt);
     (void)prologue();
     window(wt);
@@ -784,7 +883,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #undef KVQ_BODY
   } else {
     // wider codes or a 16-bit side: one phase at a time
-    Rows16<D> wt;
+    WinUnit<D> wt;
     window_issue(wt);
     const float kscale = prologue();
     window(wt);
