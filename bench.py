@@ -186,7 +186,7 @@ def main():
 
     # ---- caches: prefill T-1 tokens into each instance, then one token per step
     T0 = s.tokens - 1
-    steps_per_inst = (args.steps + args.warmup + args.instances - 1) // args.instances + 1
+    steps_per_inst = (args.steps + args.warmup + 160 + args.instances - 1) // args.instances + 1
     capacity = T0 + steps_per_inst + 64
     cfg = kvq.Config.make(B, H, Hq, D, capacity, s.n_sink, s.n_recent, s.dtype, s.quant, k_bits, v_bits)
     kd = torch.from_numpy(w["k"][:, :, :T0].view(np.int16)).to(dev)
@@ -216,35 +216,40 @@ def main():
     ws = torch.zeros(kvq.decode_workspace_bytes(caches[0], s.n_splits) * 2, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(i, evs=None):
-        # one decode step = append the new token + split-K decode + merge (the two launches of
-        # decode_attention, called apart so that events bracket the split-K kernel alone)
+    def step(i):
+        # one decode step = append the new token + split-K decode + merge, in one call (the
+        # split-K launch attends to the new token from the inputs, the merge launch stores it
+        # in the recent window; a 32-token block leaving the window is quantized first)
         c = caches[i % len(caches)]
-        kvq.append(c, newk[i % n_new], newv[i % n_new], stream=stream)
-        if evs is not None:
-            evs[0].record(stream)
-        kvq.decode_splitk(c, q, s.n_splits, ws, stream=stream)
-        if evs is not None:
-            evs[1].record(stream)
-        kvq.decode_merge(c, out, s.n_splits, ws, stream=stream)
+        kvq.decode_step(c, newk[i % n_new], newv[i % n_new], q, out, s.n_splits, ws, stream=stream)
         return c.len
 
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
     toks = 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        toks += step(args.warmup + i, evs[i]) * B * H
+        toks += step(args.warmup + i) * B * H
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+    done = args.warmup + args.steps
+    T_mean = toks / (args.steps * B * H)
+
+    # ---- GPU time of a step without host gaps: steps queued behind a spin kernel, events on
+    # the launch stream around the batch (a 160-step batch holds the 5 flushes per 160 steps
+    # that the rotation over 5 caches gives)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_gpu_steps = 160
+    torch.cuda._sleep(50_000_000)
+    e0.record(stream)
+    for i in range(n_gpu_steps):
+        step(done + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_gpu_us = e0.elapsed_time(e1) * 1e3 / n_gpu_steps
     for c in caches:
         kvq.cache_check(c)
-    step_dec_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
-    T_mean = toks / (args.steps * B * H)
 
     # ---- the split-K kernel alone, for the roofline: launches queued back to back behind a
     # spin kernel (so the host is ahead and no launch gap enters the events), rotating over
@@ -286,8 +291,8 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "decode_kernel (split-K fused-dequant decode), HIP events around "
                                f"{n_batch}x{per_batch} back-to-back launches",
-                     "bytes_per_launch": nbytes, "avg_us": dec_us, "context": T_now,
-                     "in_step_avg_us": step_dec_us},
+                     "bytes_per_launch": nbytes, "avg_us": dec_us, "context": T_now},
+        "step_gpu_us": step_gpu_us,
         "offline": {"allocate_bits_us": alloc_us, "calibrate_fit_ms_k_plus_v": calib_ms,
                     "prefill_append_ms": float(np.median(prefill_ms)),
                     "prefill_append_gbs": (B * H * T0 * D * 4) / (float(np.median(prefill_ms)) * 1e-3) / 1e9},
