@@ -76,3 +76,49 @@ def test_full_size_sampled(name):
     say(f"    decode n_splits={s.n_splits}: max err {err:.3e} (bound {bound:.3e})")
     assert ok
     assert np.all(np.isfinite(out))
+
+
+def test_full_size_decode_steps():
+    # the benchmark's step: prefill T - 1 tokens of the 32k workload, then one-token decode
+    # steps (append + decode + merge in one call) up to and across the next block flush;
+    # sampled slices against the oracle on the whole prefix after the first and the flush step
+    name = "qwen8b_t32k"
+    say(f"case: full-size fused decode steps on {name}")
+    w = workloads.make(name)
+    s = w["spec"]
+    kb, vb, _ = _bits(w)
+    rng = np.random.default_rng(7)
+    T0 = s.tokens - 1
+    n_steps = 6
+    extra_k = workloads.random_raw16(rng, (s.batch, s.n_kv, n_steps - 1, s.head_dim), s.dtype)
+    extra_v = workloads.random_raw16(rng, (s.batch, s.n_kv, n_steps - 1, s.head_dim), s.dtype)
+    k_all = np.concatenate([w["k"], extra_k], axis=2)
+    v_all = np.concatenate([w["v"], extra_v], axis=2)
+    ocfg = oracle_cfg(w, kb, vb, capacity=T0 + n_steps)
+    cache = kvq.KVCache(lib_cfg(kvq, ocfg), device=DEV)
+    kvq.append(cache, to_dev(np.ascontiguousarray(k_all[:, :, :T0])), to_dev(np.ascontiguousarray(v_all[:, :, :T0])))
+    out = torch.empty((s.batch, s.n_q, s.head_dim), dtype=torch.float32, device=DEV)
+    ws = torch.zeros(kvq.decode_workspace_bytes(cache, s.n_splits), dtype=torch.uint8, device=DEV)
+    q = to_dev(w["q"])
+    B, H, G = s.batch, s.n_kv, s.n_q // s.n_kv
+    body = lambda t: O.body_len(t, s.n_sink, s.n_recent)
+    flush_step = next(i for i in range(n_steps) if body(T0 + i + 1) > body(T0 + i))
+    samples = sorted({(0, 0), (B - 1, H - 1), (B // 2, H // 2)})
+    for i in range(n_steps):
+        t = T0 + i
+        kvq.decode_step(cache, to_dev(np.ascontiguousarray(k_all[:, :, t:t + 1])),
+                        to_dev(np.ascontiguousarray(v_all[:, :, t:t + 1])), q, out, s.n_splits, ws)
+        if i not in (0, flush_step):
+            continue
+        got = out.cpu().numpy()
+        gots, wants = [], []
+        for b, h in samples:
+            cfg1 = O.CacheConfig(1, 1, G, s.head_dim, t + 1, s.n_sink, s.n_recent, s.dtype, s.quant,
+                                 (kb[h],), (vb[h],))
+            oc1 = O.build_cache(k_all[b:b + 1, h:h + 1, :t + 1], v_all[b:b + 1, h:h + 1, :t + 1], cfg1)
+            wants.append(O.decode(oc1, w["q"][b:b + 1, h * G:(h + 1) * G])[0])
+            gots.append(got[b, h * G:(h + 1) * G])
+        ok, err, bound = within_tol(np.stack(gots), np.stack(wants))
+        say(f"    step {i} (T = {t + 1}, flush {i == flush_step}): max err {err:.3e} (bound {bound:.3e})")
+        assert ok
+    kvq.cache_check(cache)
