@@ -12,30 +12,44 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------------------
 // Slot plans: MFMA step s (0..7) of a 32-element group takes 4 codes; slot k of step s
-// holds group element chan(s, k) as the fp16 subnormal c * 2^(exp(s, k) - 24).
-// Codes sit at the TOP of the 10-bit subnormal mantissa (exp = 10 - b or close to it): the
-// 4x4x4 f16 MFMA keeps fp32 accuracy in its sums only when the subnormal operands are not
-// deeply denormalized (codes at the bottom bits lose up to ~2^-16 of relative accuracy).
-// Each pair of codes is cut out of the packed words with one shift/funnel shift and one AND:
-//   b = 2: codes k, k+8 of a word; k even at bits 8-9, k odd at bits 6-7 (exp 8 / 6)
-//   b = 3: pairs (a, a+5) or (a, a+6): code a at bits 5-7, code b at high-half bits 4-6 / 7-9
-//   b = 4: codes k, k+4 of a word at bits 6-9 (exp 6)
+// holds group element chan(s, k) as the fp16 subnormal c * 2^(exp(s, k) - 24). The 2^exp of
+// each slot is divided out of the other operand, so a code may sit anywhere in the 10-bit
+// mantissa: both MFMA shapes sum such subnormals to within 5e-5 relative at exp 0 and 2e-7
+// at exp 8 (measured on gfx950), far inside the decode tolerance.
+// Each register (slots 2h, 2h + 1) is one AND of a "window" of the group's code stream (the
+// stream shifted right by sh bits): the low code in bits 0-9, the high code in bits 16-25.
+// One window serves several registers, so a group costs 16 ANDs plus one shift per window
+// that is not a raw word:
+//   b = 2: per word, codes (i, i + 8) from the word (i < 4) or the word >> 8 (i >= 4), at
+//          bits 2 (i % 4): 2 shifts per group
+//   b = 3: the 16 pairs of pair3() from 7 windows (raw words at 0, 32, 64; shifted at 4, 10,
+//          41, 71): 4 shifts per group
+//   b = 4: per word, codes (i, i + 4) from the word (i < 2) or the word >> 8 (i >= 2), at
+//          bits 4 (i % 2): 4 shifts per group
 //   b = 8: codes k, k+2 of a word at bits 2-9 (exp 2)
 //   b = 5, 6, 7: codes 4s .. 4s+3 in order, each field extracted and placed at exp 10 - b
 // ---------------------------------------------------------------------------------------
-__host__ __device__ constexpr int pair3_a(int j) { return j < 5 ? j : (j < 10 ? j + 5 : j + 10); }
-__host__ __device__ constexpr int pair3_b(int j) { return j < 10 ? pair3_a(j) + 5 : pair3_a(j) + 6; }
+struct Pair3 {
+  int lo, hi, sh, el, eh;  // low code, high code, window shift, their bit positions in the halves
+};
+__host__ __device__ constexpr Pair3 pair3(int j) {
+  constexpr Pair3 t[16] = {{0, 6, 0, 0, 2},    {1, 7, 0, 3, 5},    {2, 8, 4, 2, 4},    {3, 9, 4, 5, 7},
+                           {4, 10, 10, 2, 4},  {5, 11, 10, 5, 7},  {12, 17, 32, 4, 3}, {13, 18, 32, 7, 6},
+                           {14, 19, 41, 1, 0}, {15, 20, 41, 4, 3}, {16, 21, 41, 7, 6}, {22, 27, 64, 2, 1},
+                           {23, 28, 64, 5, 4}, {24, 29, 71, 1, 0}, {25, 30, 71, 4, 3}, {26, 31, 71, 7, 6}};
+  return t[j];
+}
 
 template <int B>
 struct Slots {
   __host__ __device__ static constexpr int chan(int s, int k) {
+    const int j = 2 * s + (k >> 1);  // register (pair) index in the group
     if constexpr (B == 2) {
-      return 16 * (s >> 2) + 2 * (s & 3) + (k >> 1) + 8 * (k & 1);
+      return 16 * (j >> 3) + (j & 7) + 8 * (k & 1);
     } else if constexpr (B == 3) {
-      const int j = 2 * s + (k >> 1);
-      return (k & 1) ? pair3_b(j) : pair3_a(j);
+      return (k & 1) ? pair3(j).hi : pair3(j).lo;
     } else if constexpr (B == 4) {
-      return 8 * (s >> 1) + 2 * (s & 1) + (k >> 1) + 4 * (k & 1);
+      return 8 * (j >> 2) + (j & 3) + 4 * (k & 1);
     } else if constexpr (B == 8) {
       return 4 * s + (k >> 1) + 2 * (k & 1);
     } else {
@@ -43,13 +57,13 @@ struct Slots {
     }
   }
   __host__ __device__ static constexpr int exp(int s, int k) {
+    const int j = 2 * s + (k >> 1);
     if constexpr (B == 2) {
-      return ((2 * (s & 3) + (k >> 1)) & 1) ? 6 : 8;
+      return 2 * (j & 3);
     } else if constexpr (B == 3) {
-      const int j = 2 * s + (k >> 1);
-      return (k & 1) ? (j < 10 ? 4 : 7) : 5;
+      return (k & 1) ? pair3(j).eh : pair3(j).el;
     } else if constexpr (B == 4) {
-      return 6;
+      return 4 * (j & 1);
     } else if constexpr (B == 8) {
       return 2;
     } else {
@@ -94,20 +108,18 @@ __host__ __device__ __forceinline__ u32x2 unpack_step(const uint32_t (&w)[N], in
     uint32_t r[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int k = 2 * (s & 3) + h;            // pair (k, k + 8) of this word
-      const int sh = (k & 1) ? 2 * k - 6 : 2 * k - 8;
-      const uint32_t y = sh >= 0 ? (x >> sh) : (x << -sh);
-      r[h] = y & ((k & 1) ? 0x00C000C0u : 0x03000300u);
+      const int i = (2 * s + h) & 7;  // pair (i, i + 8) of this word
+      const uint32_t y = i < 4 ? x : x >> 8;
+      const int e = 2 * (i & 3);
+      r[h] = y & ((3u << e) | (3u << (16 + e)));
     }
     return u32x2{r[0], r[1]};
   } else if constexpr (B == 3) {
     uint32_t r[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int j = 2 * s + h;
-      const int a = pair3_a(j);
-      const uint32_t y = window<3>(w, base, 3 * a - 5);
-      r[h] = y & ((7u << 5) | (7u << (16 + (j < 10 ? 4 : 7))));
+      const Pair3 q = pair3(2 * s + h);
+      r[h] = window<3>(w, base, q.sh) & ((7u << q.el) | (7u << (16 + q.eh)));
     }
     return u32x2{r[0], r[1]};
   } else if constexpr (B == 4) {
@@ -115,10 +127,10 @@ __host__ __device__ __forceinline__ u32x2 unpack_step(const uint32_t (&w)[N], in
     uint32_t r[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int k = 2 * (s & 1) + h;            // pair (k, k + 4) of this word
-      const int sh = 4 * k - 6;
-      const uint32_t y = sh >= 0 ? (x >> sh) : (x << -sh);
-      r[h] = y & 0x03C003C0u;
+      const int i = (2 * s + h) & 3;  // pair (i, i + 4) of this word
+      const uint32_t y = i < 2 ? x : x >> 8;
+      const int e = 4 * (i & 1);
+      r[h] = y & ((15u << e) | (15u << (16 + e)));
     }
     return u32x2{r[0], r[1]};
   } else if constexpr (B == 8) {

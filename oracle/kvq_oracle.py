@@ -579,14 +579,15 @@ def value_stream_position(b: int, s: int, k: int) -> int:
     channel), token u = 4 (s % 2) + k of it. This is the library's storage order (a format
     choice, restated here from its definition): pairs of codes that one shift and one mask
     separate for the device sit at fixed distances in the stream."""
+    j = 2 * s + k // 2  # the step's register (pair of codes) k // 2
     if b == 2:
-        return 16 * (s // 4) + 2 * (s % 4) + k // 2 + 8 * (k % 2)
+        return 16 * (j // 8) + j % 8 + 8 * (k % 2)
     if b == 3:
         low = [4, 9, 20, 21, 22, 23, 24, 25] if s % 2 else [0, 1, 2, 3, 11, 12, 13, 14]
         a = low[2 * (s // 2) + k // 2]
         return a + (0 if k % 2 == 0 else (6 if s % 2 else 5))
     if b == 4:
-        return 8 * (s // 2) + 2 * (s % 2) + k // 2 + 4 * (k % 2)
+        return 8 * (j // 4) + j % 4 + 4 * (k % 2)
     if b == 8:
         return 4 * s + k // 2 + 2 * (k % 2)
     return 4 * s + k

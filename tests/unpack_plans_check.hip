@@ -57,7 +57,7 @@ int check_v(std::mt19937& g) {
         const int ch = VSlots<B>::chan(s, k), e = VSlots<B>::exp(s, k);
         seen[ch]++;
         const uint32_t want = codes[ch] << e;
-        if (halves[k] != want || want >= 1024u || e < 2) ++bad;
+        if (halves[k] != want || want >= 1024u) ++bad;
       }
     }
     for (int i = 0; i < 32; ++i) if (seen[i] != 1) ++bad;
