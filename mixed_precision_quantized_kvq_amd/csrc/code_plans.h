@@ -150,33 +150,39 @@ __host__ __device__ __forceinline__ u32x2 unpack_step(const uint32_t (&w)[N], in
 // ---------------------------------------------------------------------------------------
 // Value slot plans. The value product runs on the 16x16x32 MFMA: a lane's B operand is 8
 // consecutive tokens u = 0..7 of one channel ("chunk"), two steps s of a 32-code stream:
-// u = 4 (s % 2) + k. The weight operand is shared by every chunk of the tile, so the
-// exponent of a slot may depend on (s % 2, k) only. The key plans have that property for
-// b != 3; for b = 3 the values pair codes (a, a + 5) on even steps (high code at bits 4-6)
-// and (a, a + 6) on odd steps (bits 7-9), low code at bits 5-7.
+// u = 4 (s % 2) + k. Chunks 2 c' + kk of a stream (steps 4 c' + 2 kk, +1) take the weight
+// operand of K-step kk, shared with every other chunk of that K-step, so the exponent of a
+// slot may depend on (s % 4, k) only. The key plans for b = 2 and 4 have that property; for
+// b = 3 the values use vpair3(): 8 pair types (bit positions), each used by two registers of
+// the same (s % 4, register), cut from 8 windows (raw words at 0, 32, 64; shifted at -2, 8,
+// 18, 41, 71): 5 shifts per stream.
 // ---------------------------------------------------------------------------------------
-__host__ __device__ constexpr int vpair3_a(int s, int h) {
-  // low codes of the 8 even-step pairs (distance 5), then of the 8 odd-step pairs (distance 6)
-  constexpr int even_a[8] = {0, 1, 2, 3, 11, 12, 13, 14};
-  constexpr int odd_a[8] = {4, 9, 20, 21, 22, 23, 24, 25};
-  return (s & 1) ? odd_a[2 * (s >> 1) + h] : even_a[2 * (s >> 1) + h];
+__host__ __device__ constexpr Pair3 vpair3(int j) {
+  // register j = 2 s + h; steps s and s + 4 hold pairs of the same type
+  constexpr Pair3 t[16] = {{0, 5, -2, 2, 1},   {1, 6, -2, 5, 4},   {2, 7, 0, 6, 5},    {3, 9, 8, 1, 3},
+                           {4, 10, 8, 4, 6},   {14, 19, 41, 1, 0}, {15, 20, 41, 4, 3}, {16, 21, 41, 7, 6},
+                           {22, 27, 64, 2, 1}, {23, 28, 64, 5, 4}, {8, 13, 18, 6, 5},  {11, 17, 32, 1, 3},
+                           {12, 18, 32, 4, 6}, {24, 29, 71, 1, 0}, {25, 30, 71, 4, 3}, {26, 31, 71, 7, 6}};
+  return t[j];
 }
 
 template <int B>
 struct VSlots {
   __host__ __device__ static constexpr int chan(int s, int k) {
     if constexpr (B == 3) {
-      const int a = vpair3_a(s, k >> 1);
-      return (k & 1) ? a + ((s & 1) ? 6 : 5) : a;
+      const Pair3 q = vpair3(2 * s + (k >> 1));
+      return (k & 1) ? q.hi : q.lo;
     } else {
       return Slots<B>::chan(s, k);
     }
   }
   __host__ __device__ static constexpr int exp(int s, int k) {
-    if constexpr (B == 3)
-      return (k & 1) ? ((s & 1) ? 7 : 4) : 5;
-    else
+    if constexpr (B == 3) {
+      const Pair3 q = vpair3(2 * s + (k >> 1));
+      return (k & 1) ? q.eh : q.el;
+    } else {
       return Slots<B>::exp(s, k);
+    }
   }
 };
 
@@ -186,9 +192,8 @@ __host__ __device__ __forceinline__ u32x2 unpack_step_v(const uint32_t (&w)[N], 
     uint32_t r[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int a = vpair3_a(s, h);
-      const uint32_t y = window<3>(w, base, 3 * a - 5);
-      r[h] = y & ((7u << 5) | (7u << (16 + ((s & 1) ? 7 : 4))));
+      const Pair3 q = vpair3(2 * s + h);
+      r[h] = window<3>(w, base, q.sh) & ((7u << q.el) | (7u << (16 + q.eh)));
     }
     return u32x2{r[0], r[1]};
   } else {

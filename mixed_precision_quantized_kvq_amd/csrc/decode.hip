@@ -138,9 +138,10 @@ __device__ __forceinline__ u32x2 ones_step(int s) {
   return u32x2{one(0) | (one(1) << 16), one(2) | (one(3) << 16)};
 }
 
+// fp16 2^(exp - 14) in the slot of token u = 0..7 of a chunk of K-step kk
 template <int B>
-__device__ __forceinline__ u32x4 ones_chunk() {
-  auto one = [](int u) { return (uint32_t)(VSlots<B>::exp(u >> 2, u & 3) + 1) << 10; };
+__device__ __forceinline__ u32x4 ones_chunk(int kk) {
+  auto one = [&](int u) { return (uint32_t)(VSlots<B>::exp(2 * kk + (u >> 2), u & 3) + 1) << 10; };
   return u32x4{one(0) | (one(1) << 16), one(2) | (one(3) << 16), one(4) | (one(5) << 16),
                one(6) | (one(7) << 16)};
 }
@@ -361,9 +362,8 @@ __device__ __forceinline__ void value_phase(const Smem<D>& sm, int wave, const V
   const uint16_t* asrc = (m >> 3) == (g4 >> 1) ? &sm.pv[wave][m >> 3][(m >> 2) & 1][m & 3][8 * (g4 & 1)] : sm.zero16;
   const u32x4 a0 = *reinterpret_cast<const u32x4*>(asrc);
   const u32x4 a1 = *reinterpret_cast<const u32x4*>(asrc + 16);
-  const u32x4 one = ones_chunk<VB>();
-  float4_t d1 = mfma_f16_k32(a0, one, float4_t{0.0f, 0.0f, 0.0f, 0.0f});
-  d1 = mfma_f16_k32(a1, one, d1);
+  float4_t d1 = mfma_f16_k32(a0, ones_chunk<VB>(0), float4_t{0.0f, 0.0f, 0.0f, 0.0f});
+  d1 = mfma_f16_k32(a1, ones_chunk<VB>(1), d1);
   // the body accumulators hold sum s D + z D1 2^-10 and sum D1; the code products carry
   // 2^(kEp - 24) and the weight sums 2^(kEp - 14), so ob * kV and lb * kV1 are the sums
   float4_t d1s;
@@ -404,7 +404,9 @@ __device__ __forceinline__ float value_pscale(int tb) {
   float f = 1.0f;
 #pragma unroll
   for (int u = 0; u < 8; ++u)
-    if ((tb & 7) == u) f = (float)(1 << kEp) / (float)(1 << VSlots<VB>::exp(u >> 2, u & 3));
+    if ((tb & 7) == u)
+      f = (tb & 16) ? (float)(1 << kEp) / (float)(1 << VSlots<VB>::exp(2 + (u >> 2), u & 3))
+                    : (float)(1 << kEp) / (float)(1 << VSlots<VB>::exp(u >> 2, u & 3));
   return f;
 }
 

@@ -583,9 +583,9 @@ def value_stream_position(b: int, s: int, k: int) -> int:
     if b == 2:
         return 16 * (j // 8) + j % 8 + 8 * (k % 2)
     if b == 3:
-        low = [4, 9, 20, 21, 22, 23, 24, 25] if s % 2 else [0, 1, 2, 3, 11, 12, 13, 14]
-        a = low[2 * (s // 2) + k // 2]
-        return a + (0 if k % 2 == 0 else (6 if s % 2 else 5))
+        lo_hi = [(0, 5), (1, 6), (2, 7), (3, 9), (4, 10), (14, 19), (15, 20), (16, 21),
+                 (22, 27), (23, 28), (8, 13), (11, 17), (12, 18), (24, 29), (25, 30), (26, 31)]
+        return lo_hi[j][k % 2]
     if b == 4:
         return 8 * (j // 4) + j % 4 + 4 * (k % 2)
     if b == 8:

@@ -1,7 +1,8 @@
 // Host check of the slot plans: for every width, the fp16 bits that unpack_step puts in
 // slot k of step s equal code[chan(s,k)] << exp(s,k), stay inside the 10-bit subnormal
 // mantissa, and chan(., .) is a permutation of the group. The value plans (unpack_step_v,
-// VSlots) must also give every chunk the same exponents: exp(s, k) depends on (s % 2, k) only.
+// VSlots) must also give the chunks of one K-step the same exponents: exp(s, k) depends on
+// (s % 4, k) only.
 #include "code_plans.h"
 #include <cstdio>
 #include <random>
@@ -39,7 +40,7 @@ int check_v(std::mt19937& g) {
   int bad = 0;
   for (int s = 2; s < 8; ++s)
     for (int k = 0; k < 4; ++k)
-      if (VSlots<B>::exp(s, k) != VSlots<B>::exp(s & 1, k)) ++bad;
+      if (VSlots<B>::exp(s, k) != VSlots<B>::exp(s & 3, k)) ++bad;
   for (int trial = 0; trial < 2000; ++trial) {
     uint32_t codes[32], w[B] = {};
     for (int i = 0; i < 32; ++i) codes[i] = g() & ((1u << B) - 1);
