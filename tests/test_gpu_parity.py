@@ -167,6 +167,40 @@ def test_16bit_heads_and_mixed_widths():
     check_decode(cache, oc, q, splits=(1, 5))
 
 
+def test_full_grid_all_body_paths():
+    # a grid of 4 rows x 8 KV heads x 15..32 chunks (more workgroups than CUs) with every body
+    # path in one launch (widths 2-4, wider widths, 16-bit sides), window units, and fused
+    # decode steps across a block flush
+    say("case: B=4 x 8 KV heads, all body paths, 15-32 splits, fused steps")
+    rng = np.random.default_rng(33)
+    T0, steps = 1100, 40
+    T = T0 + steps
+    kb = (2, 3, 4, 16, 5, 2, 3, 4)
+    vb = (2, 3, 4, 16, 2, 8, 4, 3)
+    ocfg = O.CacheConfig(4, 8, 32, 128, T, 4, 64, "bf16", "hybrid", kb, vb)
+    k = workloads.random_raw16(rng, (4, 8, T, 128), "bf16", 2.0)
+    v = workloads.random_raw16(rng, (4, 8, T, 128), "bf16")
+    q = workloads.random_raw16(rng, (4, 32, 128), "bf16")
+    ocfg0 = O.CacheConfig(4, 8, 32, 128, T, 4, 64, "bf16", "hybrid", kb, vb)
+    oc = O.build_cache(k[:, :, :T0], v[:, :, :T0], ocfg0)
+    cache = gpu_cache(ocfg, k[:, :, :T0], v[:, :, :T0])
+    assert_regions_equal(cache, oc)
+    check_decode(cache, oc, q, splits=(15, 16, 32))
+    out = torch.empty((4, 32, 128), dtype=torch.float32, device=DEV)
+    ws = torch.zeros(kvq.decode_workspace_bytes(cache, 16), dtype=torch.uint8, device=DEV)
+    qd = to_dev(q)
+    for s_ in range(steps):
+        t = T0 + s_
+        kvq.decode_step(cache, to_dev(np.ascontiguousarray(k[:, :, t:t + 1])),
+                        to_dev(np.ascontiguousarray(v[:, :, t:t + 1])), qd, out, 16, ws)
+        if s_ % 8 == 7:
+            oc_t = O.build_cache(k[:, :, :t + 1], v[:, :, :t + 1], ocfg0)
+            ok, err, bound = within_tol(out.cpu().numpy(), O.decode(oc_t, q))
+            say(f"    step {s_}: max err {err:.3e} (bound {bound:.3e})")
+            assert ok, (s_, err, bound)
+    assert_regions_equal(cache, O.build_cache(k, v, ocfg))
+
+
 @pytest.mark.parametrize("T", [1, 3, 4 + 32, 4 + 32 + 31, 4 + 32 + 32, 4 + 32 + 95, 200])
 def test_decode_edge_lengths(T):
     say(f"case: edge length T={T}")
