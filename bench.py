@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--instances", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the decode timings of the other full-size workloads and the prefill ingest")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run only the launches the HBM-counter passes measure: a 256 MiB "
@@ -146,6 +148,101 @@ def cpu_baseline(w, k_bits, v_bits, seconds):
             "kind": "oracle",
             "sample": f"{len(pairs)} of {s.batch * s.n_kv} (row, KV head) slices of {WORKLOAD}, "
                       f"{done} float64 decodes in {el:.1f} s (unpack codes, dequantize, attention)"}
+
+
+def workload_bits(kvq, w, xk=None, xv=None):
+    """Per-KV-head (K, V) widths of a workload: fixed, one joint or two separate allocations,
+    or calibration (on device) followed by allocation."""
+    s = w["spec"]
+    if s.alloc == "fixed":
+        return list(s.fixed_bits), list(s.fixed_bits)
+    if s.alloc == "joint":
+        b, _ = kvq.allocate_bits(w["alpha"], w["beta"], w["w"], s.k_total, s.b_lo, s.b_hi)
+        return list(b), list(b)
+    if s.alloc == "separate":
+        kb, _ = kvq.allocate_bits(w["alpha_k"], w["beta_k"], w["w_k"], s.k_total, s.b_lo, s.b_hi)
+        vb, _ = kvq.allocate_bits(w["alpha_v"], w["beta_v"], w["w_v"], s.v_total, s.b_lo, s.b_hi)
+        return list(kb), list(vb)
+    fk = kvq.calibrate_fit(xk, s.dtype, kvq.AXIS_KEY, kvq.QUANT_ASYM, 2, 8)
+    fv = kvq.calibrate_fit(xv, s.dtype, kvq.AXIS_VALUE, kvq.QUANT_ASYM, 2, 8)
+    kb, _ = kvq.allocate_bits(fk[0], fk[1], w["w_k"], s.k_total, s.b_lo, s.b_hi)
+    vb, _ = kvq.allocate_bits(fv[0], fv[1], w["w_v"], s.v_total, s.b_lo, s.b_hi)
+    return list(kb), list(vb)
+
+
+def other_configs():
+    """The other full-size workloads, one GPU: split-K decode time of the 8k-token Llama-shaped
+    layer and of the 128k-token context (caches rotated so their reads come from HBM, launches
+    back to back behind a spin kernel, HIP events on the launch stream), and the ingest rate of
+    the 16 x 4096-token prefill (calibration, allocation, then one append of every token)."""
+    import torch
+
+    import mixed_precision_quantized_kvq_amd as kvq
+    import workloads
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, n_inst in (("llama8b_t8k", 5), ("long_t128k", 3)):
+        w = workloads.make(name)
+        s = w["spec"]
+        kb, vb = workload_bits(kvq, w)
+        cfg = kvq.Config.make(s.batch, s.n_kv, s.n_q, s.head_dim, s.tokens, s.n_sink, s.n_recent, s.dtype,
+                              s.quant, kb, vb)
+        kd = torch.from_numpy(w["k"].view(np.int16)).to(dev)
+        vd = torch.from_numpy(w["v"].view(np.int16)).to(dev)
+        caches = []
+        for _ in range(n_inst):
+            c = kvq.KVCache(cfg, device=dev)
+            kvq.append(c, kd, vd)
+            caches.append(c)
+        del kd, vd
+        q = torch.from_numpy(w["q"].view(np.int16)).to(dev)
+        ws = torch.zeros(kvq.decode_workspace_bytes(caches[0], s.n_splits), dtype=torch.uint8, device=dev)
+        for i in range(10):
+            kvq.decode_splitk(caches[i % n_inst], q, s.n_splits, ws, stream=stream)
+        t_us = []
+        for _ in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(20_000_000)
+            e0.record(stream)
+            for i in range(50):
+                kvq.decode_splitk(caches[i % n_inst], q, s.n_splits, ws, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t_us.append(e0.elapsed_time(e1) * 1e3 / 50)
+        us = float(np.median(t_us))
+        nbytes = decode_bytes(s, kb, vb, s.tokens, s.n_splits)
+        res[name] = {"decode_us": us, "bytes_per_launch": nbytes, "achieved_gbs": nbytes / (us * 1e-6) / 1e9,
+                     "frac_of_8tbs": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "k_bits": kb, "v_bits": vb,
+                     "n_splits": s.n_splits, "kv_tokens_heads_per_s": s.batch * s.n_kv * s.tokens / (us * 1e-6)}
+        del caches, ws, q
+        torch.cuda.empty_cache()
+    # prefill ingest
+    w = workloads.make("prefill_t4k")
+    s = w["spec"]
+    xk = torch.from_numpy(np.ascontiguousarray(w["k"][0, :, :s.calib_tokens]).view(np.int16)).to(dev)
+    xv = torch.from_numpy(np.ascontiguousarray(w["v"][0, :, :s.calib_tokens]).view(np.int16)).to(dev)
+    kb, vb = workload_bits(kvq, w, xk, xv)
+    cfg = kvq.Config.make(s.batch, s.n_kv, s.n_q, s.head_dim, s.tokens, s.n_sink, s.n_recent, s.dtype, s.quant,
+                          kb, vb)
+    kd = torch.from_numpy(w["k"].view(np.int16)).to(dev)
+    vd = torch.from_numpy(w["v"].view(np.int16)).to(dev)
+    ms = []
+    for _ in range(4):
+        c = kvq.KVCache(cfg, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        kvq.append(c, kd, vd, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        kvq.cache_check(c)
+        ms.append(e0.elapsed_time(e1))
+        del c
+    in_bytes = 2 * kd.numel() * 2
+    t = float(np.median(ms[1:]))
+    res["prefill_t4k"] = {"append_ms": t, "input_bytes": in_bytes, "ingest_gbs": in_bytes / (t * 1e-3) / 1e9,
+                          "tokens_per_s": s.batch * s.tokens / (t * 1e-3), "k_bits": kb, "v_bits": vb}
+    return res
 
 
 def main():
@@ -297,6 +394,8 @@ def main():
                     "prefill_append_ms": float(np.median(prefill_ms)),
                     "prefill_append_gbs": (B * H * T0 * D * 4) / (float(np.median(prefill_ms)) * 1e-3) / 1e9},
     }
+    if not args.no_other_configs:
+        res["other_configs"] = other_configs()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, k_bits, v_bits, args.cpu_seconds)
     print(json.dumps(res), flush=True)

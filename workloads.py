@@ -50,8 +50,10 @@ WORKLOADS = {
     "tiny_t256": Workload("tiny_t256", 1, 2, 4, 64, 256, "fp16", 1, 32, "asym", 4,
                           "fixed", fixed_bits=(2, 4)),
     # Llama-3-8B-shaped layer: 8 rows, 32/8 heads, d 128, 8192 tokens, bf16, per-channel
-    # log-normal(0, 0.5) key scales; one joint per-KV-head allocation, 2.5 average bits.
-    "llama8b_t8k": Workload("llama8b_t8k", 8, 8, 32, 128, 8192, "bf16", 4, 128, "asym", 16,
+    # log-normal(0, 0.5) key scales; one joint per-KV-head allocation, 2.5 average bits. The
+    # description fixes no chunk count; 4 chunks give 256 workgroups, one per CU (measured
+    # fastest of 1..16 on MI355X).
+    "llama8b_t8k": Workload("llama8b_t8k", 8, 8, 32, 128, 8192, "bf16", 4, 128, "asym", 4,
                             "joint", k_total=20, v_total=20),
     # Qwen3-8B-shaped long context: 4 rows, 32768 tokens, separate K (3.0) / V (2.0)
     # budgets, hybrid symmetric/asymmetric groups, 16 split-K chunks.
