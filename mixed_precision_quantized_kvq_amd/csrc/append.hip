@@ -3,6 +3,8 @@
 // Built with -ffp-contract=off: the quantizer must round exactly as quant_device.h states.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "code_plans.h"
 #include "kvq_internal.h"
 #include "quant_device.h"
@@ -40,7 +42,7 @@ __device__ __forceinline__ void load_row32(const uint16_t* src, int dtype, float
 // code of token 16 kk + 8 jp + u of channel 16 nb + n, with chunk c = s / 2, nb = 2 vg + c / 2,
 // kk = c % 2, u = 4 (s % 2) + k: the order the decode kernel's value plan reads.
 template <int B>
-__device__ __forceinline__ void pack_value_stream(const uint8_t (*codes)[kGroup + 1], int vg, int jp, int n,
+__device__ __forceinline__ void pack_value_stream(const uint8_t (*codes)[36], int vg, int jp, int n,
                                                   uint32_t* dst) {
   uint64_t acc = 0;
   int nbits = 0, w = 0;
@@ -71,7 +73,7 @@ __device__ __forceinline__ void pack_value_stream(const uint8_t (*codes)[kGroup 
 // Value codes are staged in LDS and then written, one (decode lane, stream) per thread, in the
 // decode kernel's value order.
 __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
-  __shared__ uint8_t vcodes[128][kGroup + 1];   // [channel][token of the block]
+  __shared__ alignas(4) uint8_t vcodes[128][36];  // [channel][token of the block], rows padded to 36 bytes
   const int j = p.body0 / kGroup + blockIdx.x;  // body block index
   const int h = blockIdx.y, b = blockIdx.z;
   const int D = p.D, Gd = D / kGroup;
@@ -112,27 +114,53 @@ __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
         x[k] = widen16(token_row(p, p.blob + off[RV], vin, p.n_sink + j * kGroup + k)[c], p.dtype);
     }
     if (out_of_range(x)) atomicOr(p.range_flag, 1u);
-    const GroupQ q = choose_quant(x, bits, p.hybrid != 0);
-    sym = q.sym;
-    const uint32_t meta = (uint32_t)q.s_bits | ((uint32_t)q.z_bits << 16);
-    if (is_key) {
-      const int tt = tid / Gd, g = tid % Gd;
-      const int W = Gd * bits;  // words per token
-      const int t_in_tile = jj * kGroup + tt;
-      uint32_t* kc = reinterpret_cast<uint32_t*>(p.blob + off[KC]) + (size_t)tile * kTile * W;
-      pack_group(x, q, bits, [&](int k, uint32_t word) {
-        const int w = g * bits + k;
-        const int qc = w >> 2, nq = min(4, W - 4 * qc);
-        kc[256 * qc + t_in_tile * nq + (w - 4 * qc)] = word;
-      });
-      reinterpret_cast<uint32_t*>(p.blob + off[KM])[(size_t)(j * kGroup + tt) * Gd + g] = meta;
-    } else {
-      const int c = tid - D;
+    // the width is uniform over each wavefront (keys: wavefronts 0, 1; values: 2, 3)
+    auto group = [&](auto bc) {
+      constexpr int B = decltype(bc)::value;
+      uint32_t w[B];
+      const GroupQ q = quantize_pack<B>(x, p.hybrid != 0, w);
+      sym = q.sym;
+      const uint32_t meta = (uint32_t)q.s_bits | ((uint32_t)q.z_bits << 16);
+      if (is_key) {
+        const int tt = tid / Gd, g = tid % Gd;
+        const int W = Gd * B;  // words per token
+        const int t_in_tile = jj * kGroup + tt;
+        uint32_t* kc = reinterpret_cast<uint32_t*>(p.blob + off[KC]) + (size_t)tile * kTile * W;
 #pragma unroll
-      for (int k = 0; k < 32; ++k) vcodes[c][k] = (uint8_t)code_of(x[k], q);
-      // (s|z) of channel c = 16 nb + n for this block, at [tile][block][n][nb]
-      reinterpret_cast<uint32_t*>(p.blob + off[VM])[(size_t)tile * 2 * D + jj * D + (c & 15) * (D / 16) + (c >> 4)] =
-          meta;
+        for (int k = 0; k < B; ++k) {
+          const int wi = g * B + k;
+          const int qc = wi >> 2, nq = min(4, W - 4 * qc);
+          kc[256 * qc + t_in_tile * nq + (wi - 4 * qc)] = w[k];
+        }
+        reinterpret_cast<uint32_t*>(p.blob + off[KM])[(size_t)(j * kGroup + tt) * Gd + g] = meta;
+      } else {
+        const int c = tid - D;
+        // codes of the 32 tokens, four to a word (the rows of vcodes are 36 bytes apart)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          uint32_t v4 = 0u;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int pos = (4 * m + u) * B, wi = pos >> 5, o = pos & 31;
+            uint32_t cd = w[wi] >> o;
+            if (o + B > 32) cd |= w[wi + 1] << (32 - o);
+            v4 |= (cd & ((1u << B) - 1u)) << (8 * u);
+          }
+          reinterpret_cast<uint32_t*>(vcodes[c])[m] = v4;
+        }
+        // (s|z) of channel c = 16 nb + n for this block, at [tile][block][n][nb]
+        reinterpret_cast<uint32_t*>(p.blob + off[VM])[(size_t)tile * 2 * D + jj * D + (c & 15) * (D / 16) + (c >> 4)] =
+            meta;
+      }
+    };
+    switch (bits) {
+      case 2: group(std::integral_constant<int, 2>{}); break;
+      case 3: group(std::integral_constant<int, 3>{}); break;
+      case 4: group(std::integral_constant<int, 4>{}); break;
+      case 5: group(std::integral_constant<int, 5>{}); break;
+      case 6: group(std::integral_constant<int, 6>{}); break;
+      case 7: group(std::integral_constant<int, 7>{}); break;
+      default: group(std::integral_constant<int, 8>{}); break;
     }
   }
   if (p.hybrid && bits != 16) {

@@ -117,6 +117,51 @@ __device__ __forceinline__ bool out_of_range(const float (&x)[32]) {
   return bad;
 }
 
+// Codes of one variant for the 32 elements, packed at stream bits [i*B, i*B+B) of w, and
+// (when SSE) the float64 squared error of group_sse, computed with the same operations in
+// the same order.
+template <int B, bool SSE>
+__device__ __forceinline__ double codes_sse(const float (&x)[32], const GroupQ& q, uint32_t (&w)[B]) {
+#pragma unroll
+  for (int k = 0; k < B; ++k) w[k] = 0u;
+  const double s = (double)q.s, z = (double)q.z;
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int c = code_of(x[i], q);
+    const int pos = i * B, wi = pos >> 5, off = pos & 31;
+    w[wi] |= (uint32_t)c << off;
+    if (off + B > 32) w[wi + 1] |= (uint32_t)c >> (32 - off);
+    if constexpr (SSE) {
+      const double xh = (double)c * s + z;
+      const double d = (double)x[i] - xh;
+      const double sq = d * d;
+      acc = acc + sq;
+    }
+  }
+  return acc;
+}
+
+// choose_quant with the codes of the chosen variant packed into w (one code pass per variant).
+template <int B>
+__device__ __forceinline__ GroupQ quantize_pack(const float (&x)[32], bool hybrid, uint32_t (&w)[B]) {
+  const GroupQ a = asym_params(x, B);
+  if (!hybrid) {
+    (void)codes_sse<B, false>(x, a, w);
+    return a;
+  }
+  const double ea = codes_sse<B, true>(x, a, w);
+  const GroupQ s = sym_params(x, B);
+  uint32_t ws[B];
+  const double es = codes_sse<B, true>(x, s, ws);
+  if (es < ea) {
+#pragma unroll
+    for (int k = 0; k < B; ++k) w[k] = ws[k];
+    return s;
+  }
+  return a;
+}
+
 // Pack the 32 codes of a group into b little-endian words (code i at stream bits
 // [i*b, i*b+b)) and hand each finished word to store(word_index, word).
 template <class Store>
