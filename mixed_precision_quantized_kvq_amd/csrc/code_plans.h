@@ -14,18 +14,20 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Slot plans: MFMA step s (0..7) of a 32-element group takes 4 codes; slot k of step s
 // holds group element chan(s, k) as the fp16 subnormal c * 2^(exp(s, k) - 24). The 2^exp of
 // each slot is divided out of the other operand, so a code may sit anywhere in the 10-bit
-// mantissa: both MFMA shapes sum such subnormals to within 5e-5 relative at exp 0 and 2e-7
-// at exp 8 (measured on gfx950), far inside the decode tolerance.
+// mantissa. Both MFMA shapes sum such subnormals to within 5e-5 relative at exp 0 and 2e-7 at
+// exp 8 (measured on gfx950): the error halves per bit that a code sits higher. Over 128k
+// tokens that floor reaches a quarter of the decode tolerance, so the plans keep codes high
+// where that costs at most one more shift per code word.
 // Each register (slots 2h, 2h + 1) is one AND of a "window" of the group's code stream (the
 // stream shifted right by sh bits): the low code in bits 0-9, the high code in bits 16-25.
 // One window serves several registers, so a group costs 16 ANDs plus one shift per window
 // that is not a raw word:
-//   b = 2: per word, codes (i, i + 8) from the word (i < 4) or the word >> 8 (i >= 4), at
-//          bits 2 (i % 4): 2 shifts per group
+//   b = 2: per word, codes (i, i + 8) from the word << 2 (i < 4) or the word >> 6 (i >= 4),
+//          at bits 2 (i % 4) + 2: 4 shifts per group
 //   b = 3: the 16 pairs of pair3() from 7 windows (raw words at 0, 32, 64; shifted at 4, 10,
 //          41, 71): 4 shifts per group
-//   b = 4: per word, codes (i, i + 4) from the word (i < 2) or the word >> 8 (i >= 2), at
-//          bits 4 (i % 2): 4 shifts per group
+//   b = 4: per word, codes (i, i + 4) from the word << 2 (i < 2) or the word >> 6 (i >= 2),
+//          at bits 4 (i % 2) + 2: 8 shifts per group
 //   b = 8: codes k, k+2 of a word at bits 2-9 (exp 2)
 //   b = 5, 6, 7: codes 4s .. 4s+3 in order, each field extracted and placed at exp 10 - b
 // ---------------------------------------------------------------------------------------
@@ -59,11 +61,11 @@ struct Slots {
   __host__ __device__ static constexpr int exp(int s, int k) {
     const int j = 2 * s + (k >> 1);
     if constexpr (B == 2) {
-      return 2 * (j & 3);
+      return 2 * (j & 3) + 2;
     } else if constexpr (B == 3) {
       return (k & 1) ? pair3(j).eh : pair3(j).el;
     } else if constexpr (B == 4) {
-      return 4 * (j & 1);
+      return 4 * (j & 1) + 2;
     } else if constexpr (B == 8) {
       return 2;
     } else {
@@ -109,8 +111,8 @@ __host__ __device__ __forceinline__ u32x2 unpack_step(const uint32_t (&w)[N], in
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int i = (2 * s + h) & 7;  // pair (i, i + 8) of this word
-      const uint32_t y = i < 4 ? x : x >> 8;
-      const int e = 2 * (i & 3);
+      const uint32_t y = i < 4 ? x << 2 : x >> 6;
+      const int e = 2 * (i & 3) + 2;
       r[h] = y & ((3u << e) | (3u << (16 + e)));
     }
     return u32x2{r[0], r[1]};
@@ -128,8 +130,8 @@ __host__ __device__ __forceinline__ u32x2 unpack_step(const uint32_t (&w)[N], in
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int i = (2 * s + h) & 3;  // pair (i, i + 4) of this word
-      const uint32_t y = i < 2 ? x : x >> 8;
-      const int e = 4 * (i & 1);
+      const uint32_t y = i < 2 ? x << 2 : x >> 6;
+      const int e = 4 * (i & 1) + 2;
       r[h] = y & ((15u << e) | (15u << (16 + e)));
     }
     return u32x2{r[0], r[1]};
