@@ -49,6 +49,14 @@ typedef enum {
 
 typedef enum { KVQ_F16 = 0, KVQ_BF16 = 1 } kvq_dtype;
 enum { KVQ_QUANT_ASYM = 0, KVQ_QUANT_HYBRID = 1 };
+/* Flag OR'ed into kvq_config.quant: per-channel key normalization (InnerQ technique (iii), its
+ * "Core claim" and abstract). The first kvq_append on an empty cache stores, per row, KV head
+ * and channel c, n_c = the smallest power of two >= max |k_c| over the tokens of that call
+ * (1 if that max is 0; fp32, region KN). From then on every quantized key group holds
+ * k_c / n_c instead of k_c, and decode scores the packed keys with q_c * n_c: the
+ * normalization is folded into the query. Both steps are exact because n_c is a power of two.
+ * 16-bit sink, window and unquantized-head keys are stored and used as they are. */
+enum { KVQ_KEY_NORM = 0x100 };
 enum { KVQ_AXIS_KEY = 0, KVQ_AXIS_VALUE = 1 };
 enum { KVQ_ALLOC_CAP_W = 1u }; /* w_i <- min(w_i, 5 * mean(w)) before allocating (RateQuant W.14) */
 
@@ -64,7 +72,7 @@ typedef struct {
   int32_t n_recent;     /* recent tokens kept in 16 bits, >= 0 (the window holds
                            n_recent..n_recent+31 once the body has started) */
   int32_t dtype;        /* kvq_dtype of keys, values and queries */
-  int32_t quant;        /* KVQ_QUANT_ASYM or KVQ_QUANT_HYBRID */
+  int32_t quant;        /* KVQ_QUANT_ASYM or KVQ_QUANT_HYBRID, optionally | KVQ_KEY_NORM */
   uint8_t k_bits[KVQ_MAX_KV_HEADS]; /* per KV head: 2..8, or 16 = unquantized */
   uint8_t v_bits[KVQ_MAX_KV_HEADS];
 } kvq_config;

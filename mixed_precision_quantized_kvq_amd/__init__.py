@@ -21,12 +21,13 @@ __all__ = [
     "decode_workspace_bytes", "decode_attention", "decode_splitk", "decode_merge", "decode_step",
     "cache_check",
     "region_offset", "last_error",
-    "F16", "BF16", "QUANT_ASYM", "QUANT_HYBRID", "AXIS_KEY", "AXIS_VALUE", "ALLOC_CAP_W",
+    "F16", "BF16", "QUANT_ASYM", "QUANT_HYBRID", "KEY_NORM", "AXIS_KEY", "AXIS_VALUE", "ALLOC_CAP_W",
     "EXPORTS",
 ]
 
 F16, BF16 = 0, 1
 QUANT_ASYM, QUANT_HYBRID = 0, 1
+KEY_NORM = 0x100  # OR'ed into the quant mode: per-channel key normalization
 AXIS_KEY, AXIS_VALUE = 0, 1
 ALLOC_CAP_W = 1
 MAX_KV_HEADS = 128
@@ -59,12 +60,14 @@ class Config(ctypes.Structure):
 
     @classmethod
     def make(cls, batch, n_kv_heads, n_q_heads, head_dim, capacity, n_sink, n_recent, dtype,
-             quant, k_bits, v_bits):
+             quant, k_bits, v_bits, key_norm=False):
         c = cls()
         c.batch, c.n_kv_heads, c.n_q_heads, c.head_dim = batch, n_kv_heads, n_q_heads, head_dim
         c.capacity, c.group, c.n_sink, c.n_recent = capacity, 32, n_sink, n_recent
         c.dtype = dtype if isinstance(dtype, int) else {"fp16": F16, "bf16": BF16}[dtype]
         c.quant = quant if isinstance(quant, int) else {"asym": QUANT_ASYM, "hybrid": QUANT_HYBRID}[quant]
+        if key_norm:
+            c.quant |= KEY_NORM
         for i, b in enumerate(k_bits):
             c.k_bits[i] = int(b)
         for i, b in enumerate(v_bits):

@@ -107,6 +107,11 @@ __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
     if (is_key) {
       const int tt = tid / Gd, g = tid % Gd;
       load_row32(token_row(p, p.blob + off[RK], kin, p.n_sink + j * kGroup + tt) + g * kGroup, p.dtype, x);
+      if (p.key_norm) {  // the group holds k_c / n_c (IEEE fp32 division)
+        const float* kn = reinterpret_cast<const float*>(p.blob + off[KN]) + g * kGroup;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) x[i] = x[i] / kn[i];
+      }
     } else {
       const int c = tid - D;
 #pragma unroll
@@ -195,6 +200,47 @@ __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
   }
 }
 
+// Per-channel key norms of the first append (InnerQ technique (iii)): n_c = the smallest power
+// of two >= max |k_c| over its tokens, 1 where that max is 0. One workgroup per (row, KV head):
+// thread (lane l, part r) reads 16-byte pieces l (8 channels) of tokens r, r + R, ...; the
+// maxima meet in LDS (as the bit patterns of non-negative floats, which order like the
+// floats). Heads kept in 16 bits have no norms.
+constexpr int kNormThreads = 1024;
+__global__ __launch_bounds__(kNormThreads) void key_norm_kernel(const AppendPlan p) {
+  __shared__ uint32_t nmax[128];
+  const int h = blockIdx.x % p.H, b = blockIdx.x / p.H, tid = threadIdx.x;
+  if (p.k_bits[h] == 16) return;  // uniform over the workgroup
+  if (tid < p.D) nmax[tid] = 0u;
+  __syncthreads();
+  const int pieces = p.D / 8, parts = kNormThreads / pieces;
+  const int l = tid % pieces, r = tid / pieces;
+  const uint4* k = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.k_in) +
+                                                  ((size_t)b * p.H + h) * p.n_new * p.D) + l;
+  float m[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t = r; t < p.n_new; t += parts) {
+    const uint4 u = k[(size_t)t * pieces];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m[2 * i] = fmaxf(m[2 * i], fabsf(widen16((uint16_t)(w[i] & 0xFFFFu), p.dtype)));
+      m[2 * i + 1] = fmaxf(m[2 * i + 1], fabsf(widen16((uint16_t)(w[i] >> 16), p.dtype)));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) atomicMax(&nmax[8 * l + i], __float_as_uint(m[i]));
+  __syncthreads();
+  if (tid < p.D) {
+    const uint64_t* off = p.off + ((size_t)b * p.H + h) * kRegions;
+    // the smallest power of two >= max |k_c| (1 if that is 0): dividing by it, and folding
+    // it into the query, is exact
+    const float m = __uint_as_float(nmax[tid]);
+    int e = 0;
+    const float f = frexpf(m, &e);  // m = f * 2^e, 0.5 <= f < 1
+    const float n = f == 0.5f ? m : ldexpf(1.0f, e);
+    reinterpret_cast<float*>(p.blob + off[KN])[tid] = m > 0.0f ? n : 1.0f;
+  }
+}
+
 // Copy new tokens that land in the sink or in the recent ring: one thread per 16 bytes of a
 // key or value row. Token index k < n_a is sink token len0 + k, else ring token t_b + k - n_a.
 __global__ __launch_bounds__(256) void append_window_kernel(const AppendPlan p, int n_a, int t_b, int n_tok) {
@@ -230,6 +276,11 @@ int launch_append_flush(const AppendPlan& p, void* stream) {
   if (nblk <= 0) return (int)hipSuccess;
   dim3 grid(nblk, p.H, p.B);
   hipLaunchKernelGGL(append_flush_kernel, grid, dim3(2 * p.D), 0, (hipStream_t)stream, p);
+  return (int)hipGetLastError();
+}
+
+int launch_key_norms(const AppendPlan& p, void* stream) {
+  hipLaunchKernelGGL(key_norm_kernel, dim3((unsigned)(p.B * p.H)), dim3(kNormThreads), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 

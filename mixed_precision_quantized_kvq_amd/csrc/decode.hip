@@ -154,6 +154,7 @@ struct Smem {
   alignas(16) uint32_t qA[kMaxG][D / 2 + 4];      // key-MFMA A operand: fp16 q * 2^(Eq - e), slot order
   alignas(16) uint32_t qW[kMaxG][D / 2 + 4];      // 16-bit-row A operand: q in the cache dtype
   alignas(16) float qsum[kMaxG][D / 32];          // sum of q over each key group, times the softmax scale
+  float qn[kMaxG][D];                             // packed-key query: q, or q * n with key normalization
   alignas(16) uint32_t pw[kWaves][2][kMaxG][36];  // per wave: hi/lo, query, 2 blocks x 16 words (+4 pad)
   // packed-body weights per wave: [32-token block][hi/lo][query][token], fp16, rows padded to
   // 40 halves; plus 32 zero halves for the operand rows of the other block
@@ -761,7 +762,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)b * p.Hq + (size_t)h * G) * D;
 
   // ---- q operands in LDS: raw 16-bit copy, the per-group sums of q, and the fp16 key
-  // operand in slot order with q scaled by 2^Eq so that max|q| * 2^Eq lies in [2^14, 2^15).
+  // operand in slot order with q scaled by 2^Eq so that max|q| * 2^Eq lies in [2^14, 2^15)
+  // (q means q * n for the packed keys of a cache with key normalization).
   // Returns the key-score factor scale_log2 * 2^(24 - Eq). Every wavefront calls it once.
   // the region table of this (row, head), read once into scalar registers ahead of anything
   // the compiler must treat as a possible store
@@ -776,6 +778,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   uint32_t qraw[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) qraw[e] = i0 < G ? q[(size_t)i0 * D + (tid * E + e) % D] : 0u;
+  // per-channel key norms (caches with key normalization, packed key heads): the packed keys
+  // hold k / n, so the packed-key operand is built from q * n
+  const bool use_norm = p.key_norm && kb != 16;
+  float knv[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    knv[e] = use_norm ? reinterpret_cast<const float*>(p.blob + off[KN])[(tid * E + e) % D] : 1.0f;
   issue_barrier();
   auto prologue = [&]() -> float {
     float qmax = 0.0f, qs = 0.0f;
@@ -784,7 +793,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const int c = (tid * E + e) % D;
       const uint32_t raw = qraw[e];
       reinterpret_cast<uint16_t*>(sm.qW[i0])[c] = (uint16_t)raw;
-      const float v = widen(raw, p.dtype);
+      const float v = widen(raw, p.dtype) * knv[e];
+      sm.qn[i0][c] = v;
       qmax = fmaxf(qmax, fabsf(v));
       qs += v;
     }
@@ -811,7 +821,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #undef KVQ_SLOT
         default: break;
       }
-      const float qv = widen(reinterpret_cast<const uint16_t*>(sm.qW[i])[g * 32 + ch], p.dtype);
+      const float qv = sm.qn[i][g * 32 + ch];
       reinterpret_cast<uint16_t*>(sm.qA[i])[slot] = (uint16_t)f2h(__builtin_ldexpf(qv, Eq - e));
     }
     __syncthreads();

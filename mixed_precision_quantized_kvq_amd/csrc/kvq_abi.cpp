@@ -84,7 +84,7 @@ kvq_status kvq_cache_init(kvq_cache* cache, const kvq_config* cfg, void* dev_mem
   if (bytes < total) return fail(KVQ_ERR_ARG, "dev_mem smaller than kvq_cache_bytes()");
   BlobHeader hdr{};
   hdr.magic = kMagic;
-  hdr.version = 1;
+  hdr.version = kVersion;
   hdr.range_flag = 0;
   hdr.n_regions = kRegions;
   hdr.batch = cfg->batch;
@@ -144,9 +144,15 @@ kvq_status kvq_append(kvq_cache* cache, const void* k_dev, const void* v_dev, in
   p.n_sink = c.n_sink;
   p.n_recent = c.n_recent;
   p.dtype = c.dtype;
-  p.hybrid = c.quant == KVQ_QUANT_HYBRID;
+  p.hybrid = quant_mode(c) == KVQ_QUANT_HYBRID;
+  p.key_norm = key_norm(c);
   std::memcpy(p.k_bits, c.k_bits, sizeof(p.k_bits));
   std::memcpy(p.v_bits, c.v_bits, sizeof(p.v_bits));
+  // The key norms come from the first append, before any block of it is quantized.
+  if (p.key_norm && p.len0 == 0) {
+    st = check_launch(launch_key_norms(p, stream), "key norm launch");
+    if (st != KVQ_OK) return st;
+  }
   // Blocks leaving the ring are quantized first; the window copy runs after it on the same
   // stream, so new ring tokens never overwrite ring slots that a flushed block still reads.
   if (p.body1 > p.body0) {
@@ -215,6 +221,7 @@ kvq_status decode_plan(const kvq_cache* cache, const void* q_dev, float* out_dev
   p.n_wtiles = (p.n_sink_live + p.n_win + kWinTile - 1) / kWinTile;
   p.tiles_per_split = (p.n_tiles + n_splits - 1) / n_splits;
   p.dtype = c.dtype;
+  p.key_norm = key_norm(c);
   const float s = scale > 0.0f ? scale : 1.0f / std::sqrt((float)c.head_dim);
   p.scale_log2 = s * 1.4426950408889634f;
   std::memcpy(p.k_bits, c.k_bits, sizeof(p.k_bits));
@@ -252,7 +259,8 @@ kvq_status kvq_decode_step(kvq_cache* cache, const void* k_dev, const void* v_de
   if (!q_dev || !out_dev) return fail(KVQ_ERR_ARG, "NULL pointer");
   const kvq_config& c = cache->cfg;
   const int len0 = cache->len, len1 = len0 + n_new;
-  const bool fused = n_new == 1 && len0 >= c.n_sink;
+  // (with key normalization the norms come from the first append: that one is not fused)
+  const bool fused = n_new == 1 && len0 >= c.n_sink && !(key_norm(c) && len0 == 0);
   if (!fused) {
     st = kvq_append(cache, k_dev, v_dev, n_new, stream);
     if (st != KVQ_OK) return st;
@@ -285,7 +293,8 @@ kvq_status kvq_decode_step(kvq_cache* cache, const void* k_dev, const void* v_de
   a.n_sink = c.n_sink;
   a.n_recent = c.n_recent;
   a.dtype = c.dtype;
-  a.hybrid = c.quant == KVQ_QUANT_HYBRID;
+  a.hybrid = quant_mode(c) == KVQ_QUANT_HYBRID;
+  a.key_norm = key_norm(c);
   std::memcpy(a.k_bits, c.k_bits, sizeof(a.k_bits));
   std::memcpy(a.v_bits, c.v_bits, sizeof(a.v_bits));
   if (a.body1 > a.body0) {  // a block leaves the window: quantize it first

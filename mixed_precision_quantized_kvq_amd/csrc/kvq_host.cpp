@@ -34,6 +34,7 @@ const char* last_error() { return g_last_error.c_str(); }
 //   FL hybrid flags [block][D/32 key words | D/32 value words] (hybrid caches only)
 //   SK, SV sink    [n_sink][D] 16-bit
 //   RK, RV ring    [n_recent + 32][D] 16-bit; token t >= n_sink sits in slot (t-n_sink) mod R
+//   KN key norms   [D] fp32 (caches with KVQ_KEY_NORM, quantized key heads only)
 void region_sizes(const kvq_config& cfg, int h, uint64_t sz[kRegions]) {
   const uint64_t D = (uint64_t)cfg.head_dim;
   const uint64_t bmax = (uint64_t)body_len(cfg.capacity, cfg.n_sink, cfg.n_recent);
@@ -44,9 +45,10 @@ void region_sizes(const kvq_config& cfg, int h, uint64_t sz[kRegions]) {
   sz[KM] = kb == 16 ? 0 : ntile * kTile * (D / kGroup) * 4;
   sz[VC] = vb == 16 ? bmax * D * 2 : ntile * kTile * D * vb / 8;
   sz[VM] = vb == 16 ? 0 : ntile * 2 * D * 4;
-  sz[FL] = cfg.quant == KVQ_QUANT_HYBRID ? nblk * 2 * (D / kGroup) * 4 : 0;
+  sz[FL] = quant_mode(cfg) == KVQ_QUANT_HYBRID ? nblk * 2 * (D / kGroup) * 4 : 0;
   sz[SK] = sz[SV] = (uint64_t)cfg.n_sink * D * 2;
   sz[RK] = sz[RV] = (uint64_t)ring_slots(cfg.n_recent) * D * 2;
+  sz[KN] = key_norm(cfg) && kb != 16 ? D * 4 : 0;
 }
 
 uint64_t plan_layout(const kvq_config& cfg, uint64_t* off) {
@@ -83,7 +85,8 @@ kvq_status check_config(const kvq_config* c) {
   if (c->n_sink > (1 << 20) || c->n_recent > (1 << 20))
     return fail(KVQ_ERR_ARG, "window too large");
   if (c->dtype != KVQ_F16 && c->dtype != KVQ_BF16) return fail(KVQ_ERR_ARG, "bad dtype");
-  if (c->quant != KVQ_QUANT_ASYM && c->quant != KVQ_QUANT_HYBRID)
+  if ((quant_mode(*c) != KVQ_QUANT_ASYM && quant_mode(*c) != KVQ_QUANT_HYBRID) ||
+      (c->quant & ~(0xFF | KVQ_KEY_NORM)))
     return fail(KVQ_ERR_ARG, "bad quant mode");
   for (int h = 0; h < c->n_kv_heads; ++h)
     if (!bits_ok(c->k_bits[h]) || !bits_ok(c->v_bits[h]))

@@ -19,13 +19,18 @@ constexpr int kTile = 64;         // body tokens per key tile (one wavefront, on
 #define KVQ_WIN_TILE 16
 #endif
 constexpr int kWinTile = KVQ_WIN_TILE;
-constexpr int kRegions = 9;
+constexpr int kRegions = 10;
 constexpr uint64_t kAlign = 256;  // every region starts on a 256-byte boundary
 constexpr uint64_t kHeaderBytes = 256;
 constexpr uint32_t kMagic = 0x3151564Bu;  // "KVQ1"
+constexpr uint32_t kVersion = 2;        // 2: region KN (key norms) added
 constexpr float kRangeLimit = 16384.0f;   // |x| <= 2^14 for quantized heads
 
-enum Region { KC = 0, KM, VC, VM, FL, SK, SV, RK, RV };
+enum Region { KC = 0, KM, VC, VM, FL, SK, SV, RK, RV, KN };
+
+// Quantizer mode and flags packed in kvq_config.quant.
+inline int quant_mode(const kvq_config& c) { return c.quant & 0xFF; }
+inline bool key_norm(const kvq_config& c) { return (c.quant & KVQ_KEY_NORM) != 0; }
 
 // Blob header (first 256 bytes of every cache blob). The region table follows it.
 struct BlobHeader {
@@ -81,11 +86,13 @@ struct AppendPlan {
   int body0, body1;      // body lengths before / after
   int n_sink, n_recent;
   int dtype, hybrid;
+  int key_norm;          // keys of quantized heads are divided by the stored per-channel norms
   alignas(4) uint8_t k_bits[KVQ_MAX_KV_HEADS];  // word-aligned: kernels read them a word at a time
   alignas(4) uint8_t v_bits[KVQ_MAX_KV_HEADS];
 };
 int launch_append_flush(const AppendPlan& p, void* stream);
 int launch_append_window(const AppendPlan& p, void* stream);
+int launch_key_norms(const AppendPlan& p, void* stream);  // first append: per-channel key norms
 
 struct CalibPlan {
   const void* x;          // [n_heads][n_tokens][D]
@@ -108,6 +115,7 @@ struct DecodePlan {
   int n_splits, n_tiles, n_wtiles;  // partials, 64-token body tiles, kWinTile-token window units
   int tiles_per_split;   // body tiles per split (the window tiles are dealt out separately)
   int dtype;
+  int key_norm;          // packed keys are k / n: their scores use q * n
   float scale_log2;      // softmax scale times log2(e)
   // fused decode step: the token being appended ([B][H][1][D], 16-bit), not counted in n_win.
   // The last split of each (row, head) attends to it; the merge launch writes it into ring

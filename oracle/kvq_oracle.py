@@ -16,6 +16,14 @@ What it computes, and where the pages define it
   lower squared error wins, ties go to asymmetric.
 * 16-bit high-precision windows for attention-sink tokens and recent tokens (InnerQ page,
   abstract, technique (ii)).
+* Optional per-channel key normalization computed once at prefill and folded into the
+  query (InnerQ page, abstract, technique (iii), and "Core claim"). The pages give no
+  formula for n_c. Reading taken: n_c is the smallest power of two >= max |k_c| over the
+  tokens of the first append (1 if that max is 0). That brings every prefill channel into
+  [-1, 1], as dividing by the max would, to within a factor of 2. It also makes both k_c / n_c
+  and the query fold q_c * n_c exact in any binary format, so folding into the query costs
+  no precision. Quantized key groups hold k_c / n_c (IEEE float32 division), and their
+  attention uses n_c * (s c + z). 16-bit keys are used as they are.
 * Distortion model D(b) = alpha * beta^-b fitted per head by least squares in the log
   domain, with a beta fallback for poor fits (RateQuant page, TL;DR and sections 3.1,
   3.4, W.10).
@@ -210,6 +218,7 @@ class CacheConfig:
     quant: str                  # "asym" | "hybrid"
     k_bits: tuple
     v_bits: tuple
+    key_norm: bool = False      # per-channel key normalization (InnerQ technique (iii))
 
     @property
     def groups(self) -> int:
@@ -228,6 +237,8 @@ class OracleCache:
     win_v: np.ndarray
     # per head h: dict with quantized body (or raw 16-bit body for 16-bit heads)
     heads: list
+    # per-channel key norms float32 [B][H][D] (key normalization only, else None)
+    k_norm: np.ndarray | None = None
 
 
 def _check_range(x: np.ndarray):
@@ -235,16 +246,29 @@ def _check_range(x: np.ndarray):
         raise ValueError("quantized inputs must be finite with |x| <= 2^14")
 
 
-def build_cache(k_raw: np.ndarray, v_raw: np.ndarray, cfg: CacheConfig) -> OracleCache:
+def key_norms(k_raw: np.ndarray, dtype: str) -> np.ndarray:
+    """Per-channel key norms float32 [B][H][D]: the smallest power of two >= the max over
+    the given tokens (those of the first append) of |k_c|; 1 where that max is 0 (InnerQ
+    page, technique (iii); the power of two is this implementation's reading)."""
+    m = np.abs(widen16(k_raw, dtype)).max(axis=2) if k_raw.shape[2] else np.zeros(
+        (k_raw.shape[0], k_raw.shape[1], k_raw.shape[3]), dtype=np.float32)
+    f, e = np.frexp(m.astype(np.float64))            # m = f * 2^e, 0.5 <= f < 1
+    n = np.where(f == 0.5, m.astype(np.float64), np.ldexp(1.0, e))
+    return np.where(m > 0, n, 1.0).astype(np.float32)
+
+
+def build_cache(k_raw: np.ndarray, v_raw: np.ndarray, cfg: CacheConfig, norm_tokens: int | None = None) -> OracleCache:
     """State of the cache after appending tokens 0..T-1 (k_raw, v_raw [B][H][T][D] bits).
 
     Body keys: group (token t, channels 32g..32g+31); body values: group (channel c,
-    tokens 32j..32j+31).  Heads with 16 bits keep the body unquantized."""
+    tokens 32j..32j+31).  Heads with 16 bits keep the body unquantized. With key
+    normalization, norm_tokens is the token count of the first append (default: all T)."""
     B, H, T, D = k_raw.shape
     assert v_raw.shape == k_raw.shape and H == cfg.n_kv and D == cfg.head_dim
     ns = min(T, cfg.n_sink)
     body = body_len(T, cfg.n_sink, cfg.n_recent)
     hyb = cfg.quant == "hybrid"
+    kn = key_norms(k_raw[:, :, :T if norm_tokens is None else norm_tokens], cfg.dtype) if cfg.key_norm else None
     heads = []
     for h in range(H):
         e = {}
@@ -255,6 +279,8 @@ def build_cache(k_raw: np.ndarray, v_raw: np.ndarray, cfg: CacheConfig) -> Oracl
             e["k_raw"] = kbody.copy()
         else:
             x = widen16(kbody, cfg.dtype)
+            if kn is not None:
+                x = (x / kn[:, h, None, :]).astype(np.float32)   # IEEE float32 division
             _check_range(x)
             xg = x.reshape(B, body, cfg.groups, GROUP)
             c, s, z, f = quant_group(xg, kb, hyb)
@@ -272,7 +298,7 @@ def build_cache(k_raw: np.ndarray, v_raw: np.ndarray, cfg: CacheConfig) -> Oracl
     return OracleCache(cfg=cfg, T=T, body=body,
                        sink_k=k_raw[:, :, :ns].copy(), sink_v=v_raw[:, :, :ns].copy(),
                        win_k=k_raw[:, :, ns + body:].copy(), win_v=v_raw[:, :, ns + body:].copy(),
-                       heads=heads)
+                       heads=heads, k_norm=kn)
 
 
 def logical_kv(oc: OracleCache, b: int, h: int):
@@ -286,7 +312,10 @@ def logical_kv(oc: OracleCache, b: int, h: int):
     if "k_raw" in e:
         parts_k.append(widen16(e["k_raw"][b], cfg.dtype).astype(np.float64))
     else:
-        parts_k.append(dequant(e["k_codes"][b], e["k_s"][b], e["k_z"][b]).reshape(oc.body, D))
+        kh = dequant(e["k_codes"][b], e["k_s"][b], e["k_z"][b]).reshape(oc.body, D)
+        if oc.k_norm is not None:
+            kh = kh * oc.k_norm[b, h].astype(np.float64)[None, :]   # the normalization undone
+        parts_k.append(kh)
     if "v_raw" in e:
         parts_v.append(widen16(e["v_raw"][b], cfg.dtype).astype(np.float64))
     else:
@@ -568,8 +597,8 @@ def allocate_continuous(alpha, beta, w, total, b_lo, b_hi, cap=False, tol=1e-13)
 # ----------------------------------------------------------------------------------------
 
 HEADER_BYTES = 256
-N_REGIONS = 9
-REG_KC, REG_KM, REG_VC, REG_VM, REG_FL, REG_SK, REG_SV, REG_RK, REG_RV = range(N_REGIONS)
+N_REGIONS = 10
+REG_KC, REG_KM, REG_VC, REG_VM, REG_FL, REG_SK, REG_SV, REG_RK, REG_RV, REG_KN = range(N_REGIONS)
 TILE = 64  # body tokens per key tile
 
 
@@ -612,12 +641,13 @@ def region_sizes(cfg: CacheConfig, h: int):
     sz[REG_FL] = nblk * 2 * (D // GROUP) * 4 if cfg.quant == "hybrid" else 0
     sz[REG_SK] = sz[REG_SV] = cfg.n_sink * D * 2
     sz[REG_RK] = sz[REG_RV] = ring_slots(cfg.n_recent) * D * 2
+    sz[REG_KN] = D * 4 if cfg.key_norm and kb != 16 else 0
     return sz
 
 
 def layout(cfg: CacheConfig):
-    """Offsets (bytes from the blob start) [B][H][9] and the total blob size.
-    Header (256 B), then the offset table (uint64 [B][H][9]), then every region in
+    """Offsets (bytes from the blob start) [B][H][10] and the total blob size.
+    Header (256 B), then the offset table (uint64 [B][H][10]), then every region in
     (row, head, region) order, each starting on a 256-byte boundary."""
     B, H = cfg.batch, cfg.n_kv
     off = np.zeros((B, H, N_REGIONS), dtype=np.uint64)
@@ -753,4 +783,7 @@ def expected_regions(oc: OracleCache, b: int, h: int):
             slot = (tok - cfg.n_sink) % R
             buf[slot] = src[b, h, i]
             mk[slot] = True
+    if sz[REG_KN]:
+        data[REG_KN] = oc.k_norm[b, h].astype(np.float32).view(np.uint8).copy()
+        mask[REG_KN][:] = True
     return data, mask

@@ -35,20 +35,20 @@ def oracle_calibration(w):
     return res
 
 
-def oracle_cfg(w, k_bits, v_bits, capacity=None, batch=None, n_kv=None, n_q=None):
+def oracle_cfg(w, k_bits, v_bits, capacity=None, batch=None, n_kv=None, n_q=None, key_norm=False):
     s = w["spec"]
     return O.CacheConfig(batch=w["batch"] if batch is None else batch,
                          n_kv=s.n_kv if n_kv is None else n_kv,
                          n_q=s.n_q if n_q is None else n_q, head_dim=s.head_dim,
                          capacity=w["tokens"] if capacity is None else capacity,
                          n_sink=s.n_sink, n_recent=s.n_recent, dtype=s.dtype, quant=s.quant,
-                         k_bits=tuple(k_bits), v_bits=tuple(v_bits))
+                         k_bits=tuple(k_bits), v_bits=tuple(v_bits), key_norm=key_norm)
 
 
 def lib_cfg(kvq, ocfg):
     return kvq.Config.make(ocfg.batch, ocfg.n_kv, ocfg.n_q, ocfg.head_dim, ocfg.capacity,
                            ocfg.n_sink, ocfg.n_recent, ocfg.dtype, ocfg.quant, ocfg.k_bits,
-                           ocfg.v_bits)
+                           ocfg.v_bits, key_norm=ocfg.key_norm)
 
 
 def head_slice_cfg(ocfg, h):
@@ -56,7 +56,8 @@ def head_slice_cfg(ocfg, h):
     G = ocfg.n_q // ocfg.n_kv
     return O.CacheConfig(batch=1, n_kv=1, n_q=G, head_dim=ocfg.head_dim, capacity=ocfg.capacity,
                          n_sink=ocfg.n_sink, n_recent=ocfg.n_recent, dtype=ocfg.dtype,
-                         quant=ocfg.quant, k_bits=(ocfg.k_bits[h],), v_bits=(ocfg.v_bits[h],))
+                         quant=ocfg.quant, k_bits=(ocfg.k_bits[h],), v_bits=(ocfg.v_bits[h],),
+                         key_norm=ocfg.key_norm)
 
 
 def within_tol(got, want, rel=2e-3):

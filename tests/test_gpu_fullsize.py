@@ -40,7 +40,17 @@ def _bits(w):
 
 @pytest.mark.parametrize("name", list(workloads.WORKLOADS))
 def test_full_size_sampled(name):
-    say(f"case: full-size {name}")
+    _full_size_sampled(name, key_norm=False)
+
+
+@pytest.mark.parametrize("name", ["qwen8b_t32k", "long_t128k"])
+def test_full_size_key_norm(name):
+    # the same bulk append + decode with per-channel key normalization
+    _full_size_sampled(name, key_norm=True)
+
+
+def _full_size_sampled(name, key_norm):
+    say(f"case: full-size {name}, key normalization {key_norm}")
     w = workloads.make(name)
     s = w["spec"]
     kb, vb, fits = _bits(w)
@@ -54,7 +64,7 @@ def test_full_size_sampled(name):
     else:
         assert (kb, vb) == oracle_bits(w)
     say(f"    bits K={kb} V={vb}")
-    ocfg = oracle_cfg(w, kb, vb)
+    ocfg = oracle_cfg(w, kb, vb, key_norm=key_norm)
     cache = kvq.KVCache(lib_cfg(kvq, ocfg), device=DEV)
     kd, vd = to_dev(w["k"]), to_dev(w["v"])
     kvq.append(cache, kd, vd)

@@ -358,3 +358,98 @@ def test_abi_errors_enqueue_nothing():
     with pytest.raises(kvq.KvqError) as e:
         kvq.decode_attention(cache, q, out, 1, ws)       # empty cache
     assert e.value.status == -1
+
+
+# ------------------------------------------------------------------------------------------
+# Per-channel key normalization: norms from the first append, normalized body keys, the norms
+# folded into the query at decode
+
+def outlier_keys(rng, shape, dtype, n_out=4, factor=8.0):
+    """N(0, 1) keys with n_out channels per (row, head) scaled by factor."""
+    x = workloads.random_raw16(rng, shape, dtype)
+    xf = O.widen16(x, dtype).copy()
+    for b in range(shape[0]):
+        for h in range(shape[1]):
+            xf[b, h, :, rng.choice(shape[3], size=n_out, replace=False)] *= np.float32(factor)
+    return workloads.to_raw16(xf, dtype)
+
+
+@pytest.mark.parametrize("chunks", [[300], [37, 1, 100, 62, 100], [8] + [1] * 60 + [93]],
+                         ids=["bulk", "ragged", "one-token"])
+def test_key_norm_appends(chunks):
+    say(f"case: key norm, appends {chunks[:4]}...")
+    rng = np.random.default_rng(200 + len(chunks))
+    T = sum(chunks)
+    ocfg = O.CacheConfig(2, 2, 4, 64, T + 5, 3, 40, "bf16", "hybrid", (3, 2), (2, 4), key_norm=True)
+    k = outlier_keys(rng, (2, 2, T, 64), "bf16")
+    v = workloads.random_raw16(rng, (2, 2, T, 64), "bf16")
+    q = workloads.random_raw16(rng, (2, 4, 64), "bf16")
+    oc = O.build_cache(k, v, ocfg, norm_tokens=chunks[0])
+    cache = gpu_cache(ocfg, k, v, chunks=chunks)
+    assert_regions_equal(cache, oc)
+    check_decode(cache, oc, q, splits=(1, 3, 8))
+
+
+def test_key_norm_mixed_widths_d128():
+    say("case: key norm, 16-bit heads + every width 2..8, fp16 hybrid, D=128")
+    rng = np.random.default_rng(210)
+    T = 900
+    kb = (16, 2, 3, 4, 5, 6, 7, 8)
+    vb = (8, 7, 16, 5, 4, 3, 2, 16)
+    ocfg = O.CacheConfig(1, 8, 16, 128, T, 4, 64, "fp16", "hybrid", kb, vb, key_norm=True)
+    k = outlier_keys(rng, (1, 8, T, 128), "fp16")
+    v = workloads.random_raw16(rng, (1, 8, T, 128), "fp16")
+    q = workloads.random_raw16(rng, (1, 16, 128), "fp16")
+    oc = O.build_cache(k, v, ocfg, norm_tokens=500)
+    cache = gpu_cache(ocfg, k, v, chunks=[500, 1, 399])
+    assert_regions_equal(cache, oc)
+    check_decode(cache, oc, q, splits=(1, 5, 16))
+
+
+def test_key_norm_full_grid_asym():
+    # every body path in one launch with normalized keys, asymmetric quantizer, bf16
+    say("case: key norm, B=4 x 8 KV heads, all body paths, asym")
+    rng = np.random.default_rng(211)
+    T = 1100
+    kb = (2, 3, 4, 16, 5, 2, 3, 4)
+    vb = (2, 3, 4, 16, 2, 8, 4, 3)
+    ocfg = O.CacheConfig(4, 8, 32, 128, T, 4, 64, "bf16", "asym", kb, vb, key_norm=True)
+    k = outlier_keys(rng, (4, 8, T, 128), "bf16")
+    v = workloads.random_raw16(rng, (4, 8, T, 128), "bf16")
+    q = workloads.random_raw16(rng, (4, 32, 128), "bf16")
+    oc = O.build_cache(k, v, ocfg)
+    cache = gpu_cache(ocfg, k, v)
+    assert_regions_equal(cache, oc)
+    check_decode(cache, oc, q, splits=(15, 32))
+
+
+@pytest.mark.parametrize("first", [8, 90])
+def test_key_norm_decode_steps(first):
+    # decode_step from an empty cache: the first call (several tokens) sets the norms, the
+    # single-token steps after it take the fused path across several flushes
+    say(f"case: key norm decode_step sequence, first append {first}")
+    rng = np.random.default_rng(220 + first)
+    steps = 75
+    T = first + steps
+    ocfg = O.CacheConfig(2, 2, 4, 128, T + 8, 4, 40, "bf16", "hybrid", (3, 2), (2, 4), key_norm=True)
+    k = outlier_keys(rng, (2, 2, T, 128), "bf16")
+    v = workloads.random_raw16(rng, (2, 2, T, 128), "bf16")
+    qs = workloads.random_raw16(rng, (steps + 1, 2, 4, 128), "bf16")
+    cache = kvq.KVCache(lib_cfg(kvq, ocfg), device=DEV)
+    out = torch.empty((2, 4, 128), dtype=torch.float32, device=DEV)
+    ws = torch.zeros(kvq.decode_workspace_bytes(cache, 3), dtype=torch.uint8, device=DEV)
+    t, worst = 0, 0.0
+    for s, n in enumerate([first] + [1] * steps):
+        kvq.decode_step(cache, to_dev(np.ascontiguousarray(k[:, :, t:t + n])),
+                        to_dev(np.ascontiguousarray(v[:, :, t:t + n])), to_dev(np.ascontiguousarray(qs[s])),
+                        out, 3, ws)
+        t += n
+        assert cache.len == t
+        if s % 4 == 0 or t == T:
+            oc = O.build_cache(k[:, :, :t], v[:, :, :t], ocfg, norm_tokens=first)
+            ok, err, bound = within_tol(out.cpu().numpy(), O.decode(oc, qs[s]))
+            worst = max(worst, err / bound)
+            assert ok, (s, err, bound)
+    say(f"    worst error / bound over the steps: {worst:.3e}")
+    kvq.cache_check(cache)
+    assert_regions_equal(cache, O.build_cache(k, v, ocfg, norm_tokens=first))
