@@ -22,10 +22,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // stream shifted right by sh bits): the low code in bits 0-9, the high code in bits 16-25.
 // One window serves several registers, so a group costs 16 ANDs plus one shift per window
 // that is not a raw word:
-//   b = 2: per word, codes (i, i + 8) from the word << 2 (i < 4) or the word >> 6 (i >= 4),
-//          at bits 2 (i % 4) + 2: 4 shifts per group
-//   b = 3: the 16 pairs of pair3() from 7 windows (raw words at 0, 32, 64; shifted at 4, 10,
-//          41, 71): 4 shifts per group
+//   b = 2: per word, codes (i, i + 8) from the word << 4 (i < 3, at bits 2 i + 4), the word
+//          (i = 3, 4, at bits 2 i) or the word >> 6 (i > 4, at bits 2 i - 6): every code at
+//          bit 4, 6 or 8; 4 shifts per group
+//   b = 3: the 16 pairs of pair3() from 9 windows (raw words at 0, 32, 64; shifted at -4, 5,
+//          26, 35, 58, 70): every code at bit 2 or above; 6 shifts per group
 //   b = 4: per word, codes (i, i + 4) from the word << 2 (i < 2) or the word >> 6 (i >= 2),
 //          at bits 4 (i % 2) + 2: 8 shifts per group
 //   b = 8: codes k, k+2 of a word at bits 2-9 (exp 2)
@@ -35,10 +36,10 @@ struct Pair3 {
   int lo, hi, sh, el, eh;  // low code, high code, window shift, their bit positions in the halves
 };
 __host__ __device__ constexpr Pair3 pair3(int j) {
-  constexpr Pair3 t[16] = {{0, 6, 0, 0, 2},    {1, 7, 0, 3, 5},    {2, 8, 4, 2, 4},    {3, 9, 4, 5, 7},
-                           {4, 10, 10, 2, 4},  {5, 11, 10, 5, 7},  {12, 17, 32, 4, 3}, {13, 18, 32, 7, 6},
-                           {14, 19, 41, 1, 0}, {15, 20, 41, 4, 3}, {16, 21, 41, 7, 6}, {22, 27, 64, 2, 1},
-                           {23, 28, 64, 5, 4}, {24, 29, 71, 1, 0}, {25, 30, 71, 4, 3}, {26, 31, 71, 7, 6}};
+  constexpr Pair3 t[16] = {{0, 5, -4, 4, 3},   {1, 6, -4, 7, 6},   {2, 7, 0, 6, 5},    {3, 8, 5, 4, 3},
+                           {4, 9, 5, 7, 6},    {10, 15, 26, 4, 3}, {11, 16, 26, 7, 6}, {12, 17, 32, 4, 3},
+                           {13, 18, 32, 7, 6}, {14, 19, 35, 7, 6}, {20, 26, 58, 2, 4}, {21, 27, 58, 5, 7},
+                           {22, 28, 64, 2, 4}, {23, 29, 64, 5, 7}, {24, 30, 70, 2, 4}, {25, 31, 70, 5, 7}};
   return t[j];
 }
 
@@ -61,7 +62,8 @@ struct Slots {
   __host__ __device__ static constexpr int exp(int s, int k) {
     const int j = 2 * s + (k >> 1);
     if constexpr (B == 2) {
-      return 2 * (j & 3) + 2;
+      const int i = j & 7;
+      return i < 3 ? 2 * i + 4 : i < 5 ? 2 * i : 2 * i - 6;
     } else if constexpr (B == 3) {
       return (k & 1) ? pair3(j).eh : pair3(j).el;
     } else if constexpr (B == 4) {
@@ -111,8 +113,8 @@ __host__ __device__ __forceinline__ u32x2 unpack_step(const uint32_t (&w)[N], in
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int i = (2 * s + h) & 7;  // pair (i, i + 8) of this word
-      const uint32_t y = i < 4 ? x << 2 : x >> 6;
-      const int e = 2 * (i & 3) + 2;
+      const uint32_t y = i < 3 ? x << 4 : i < 5 ? x : x >> 6;
+      const int e = i < 3 ? 2 * i + 4 : i < 5 ? 2 * i : 2 * i - 6;
       r[h] = y & ((3u << e) | (3u << (16 + e)));
     }
     return u32x2{r[0], r[1]};
@@ -155,16 +157,16 @@ __host__ __device__ __forceinline__ u32x2 unpack_step(const uint32_t (&w)[N], in
 // u = 4 (s % 2) + k. Chunks 2 c' + kk of a stream (steps 4 c' + 2 kk, +1) take the weight
 // operand of K-step kk, shared with every other chunk of that K-step, so the exponent of a
 // slot may depend on (s % 4, k) only. The key plans for b = 2 and 4 have that property; for
-// b = 3 the values use vpair3(): 8 pair types (bit positions), each used by two registers of
-// the same (s % 4, register), cut from 8 windows (raw words at 0, 32, 64; shifted at -2, 8,
-// 18, 41, 71): 5 shifts per stream.
+// b = 3 the values use vpair3(): 8 pair types (bit positions), each used by registers j and
+// j + 8, cut from 10 windows (raw words at 0, 32, 64; shifted at -4, 5, 26, 36, 58, 67, 70),
+// every code at bit 2 or above: 7 shifts per stream.
 // ---------------------------------------------------------------------------------------
 __host__ __device__ constexpr Pair3 vpair3(int j) {
   // register j = 2 s + h; steps s and s + 4 hold pairs of the same type
-  constexpr Pair3 t[16] = {{0, 5, -2, 2, 1},   {1, 6, -2, 5, 4},   {2, 7, 0, 6, 5},    {3, 9, 8, 1, 3},
-                           {4, 10, 8, 4, 6},   {14, 19, 41, 1, 0}, {15, 20, 41, 4, 3}, {16, 21, 41, 7, 6},
-                           {22, 27, 64, 2, 1}, {23, 28, 64, 5, 4}, {8, 13, 18, 6, 5},  {11, 17, 32, 1, 3},
-                           {12, 18, 32, 4, 6}, {24, 29, 71, 1, 0}, {25, 30, 71, 4, 3}, {26, 31, 71, 7, 6}};
+  constexpr Pair3 t[16] = {{0, 5, -4, 4, 3},   {1, 6, -4, 7, 6},   {2, 7, 0, 6, 5},    {10, 15, 26, 4, 3},
+                           {11, 16, 26, 7, 6}, {20, 26, 58, 2, 4}, {21, 27, 58, 5, 7}, {24, 30, 67, 5, 7},
+                           {3, 8, 5, 4, 3},    {4, 9, 5, 7, 6},    {14, 19, 36, 6, 5}, {12, 17, 32, 4, 3},
+                           {13, 18, 32, 7, 6}, {22, 28, 64, 2, 4}, {23, 29, 64, 5, 7}, {25, 31, 70, 5, 7}};
   return t[j];
 }
 

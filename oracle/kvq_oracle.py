@@ -612,8 +612,8 @@ def value_stream_position(b: int, s: int, k: int) -> int:
     if b == 2:
         return 16 * (j // 8) + j % 8 + 8 * (k % 2)
     if b == 3:
-        lo_hi = [(0, 5), (1, 6), (2, 7), (3, 9), (4, 10), (14, 19), (15, 20), (16, 21),
-                 (22, 27), (23, 28), (8, 13), (11, 17), (12, 18), (24, 29), (25, 30), (26, 31)]
+        lo_hi = [(0, 5), (1, 6), (2, 7), (10, 15), (11, 16), (20, 26), (21, 27), (24, 30),
+                 (3, 8), (4, 9), (14, 19), (12, 17), (13, 18), (22, 28), (23, 29), (25, 31)]
         return lo_hi[j][k % 2]
     if b == 4:
         return 8 * (j // 4) + j % 4 + 4 * (k % 2)

@@ -4,8 +4,9 @@ The decode kernel feeds b-bit codes to the MFMA as fp16 subnormals cut out of th
 words with a shift and a mask per pair of codes. This compiles the kernel's own key and
 value plans (code_plans.h) for the host and checks, for every width 2..8, that slot k of
 step s holds code[chan(s, k)] << exp(s, k), inside the 10-bit mantissa, that every element
-of a group is used exactly once, and that the value plans' exponents repeat every two steps
-(one weight operand serves every chunk).
+of a group is used exactly once, that the value plans' exponents repeat every two steps
+(one weight operand serves every chunk), and that 2- to 4-bit codes sit at mantissa bit 2 or
+above (4 or above for 2 bits), where the MFMA sums them with little error.
 """
 import os
 import subprocess

@@ -2,14 +2,20 @@
 // slot k of step s equal code[chan(s,k)] << exp(s,k), stay inside the 10-bit subnormal
 // mantissa, and chan(., .) is a permutation of the group. The value plans (unpack_step_v,
 // VSlots) must also give the chunks of one K-step the same exponents: exp(s, k) depends on
-// (s % 4, k) only.
+// (s % 4, k) only. Codes of 2 to 4 bits sit at mantissa bit 2 or above (bit 4 or above for
+// 2 bits), where the MFMA sums them precisely.
 #include "code_plans.h"
 #include <cstdio>
 #include <random>
 using namespace kvq;
 template <int B>
+constexpr int min_exp() { return B == 2 ? 4 : B <= 4 ? 2 : 0; }
+template <int B>
 int check(std::mt19937& g) {
   int bad = 0;
+  for (int s = 0; s < 8; ++s)
+    for (int k = 0; k < 4; ++k)
+      if (Slots<B>::exp(s, k) < min_exp<B>()) ++bad;
   for (int trial = 0; trial < 2000; ++trial) {
     uint32_t codes[32], w[B] = {};
     for (int i = 0; i < 32; ++i) codes[i] = g() & ((1u << B) - 1);
@@ -41,6 +47,9 @@ int check_v(std::mt19937& g) {
   for (int s = 2; s < 8; ++s)
     for (int k = 0; k < 4; ++k)
       if (VSlots<B>::exp(s, k) != VSlots<B>::exp(s & 3, k)) ++bad;
+  for (int s = 0; s < 8; ++s)
+    for (int k = 0; k < 4; ++k)
+      if (VSlots<B>::exp(s, k) < min_exp<B>()) ++bad;
   for (int trial = 0; trial < 2000; ++trial) {
     uint32_t codes[32], w[B] = {};
     for (int i = 0; i < 32; ++i) codes[i] = g() & ((1u << B) - 1);
