@@ -100,19 +100,26 @@ def decode_bytes(spec, k_bits, v_bits, T, n_splits):
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "decode_kernel_qwen8b_t32k_traffic.txt")
-KERNEL_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "mixed_precision_quantized_kvq_amd",
-                          "csrc", "decode.hip")
+KERNEL_SRCS = [os.path.join(os.path.dirname(os.path.abspath(__file__)), "mixed_precision_quantized_kvq_amd",
+                            "csrc", f) for f in ("decode.hip", "code_plans.h", "kvq_internal.h")]
+
+
+def kernel_sources_sha256():
+    """sha256 over the decode kernel's sources, in a fixed order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic():
     """HBM bytes per decode launch from the committed FETCH_SIZE + WRITE_SIZE summary, or None
-    when that summary was taken on another version of the kernel source (sha256 mismatch)."""
-    import hashlib
+    when that summary was taken on another version of the kernel sources (sha256 mismatch)."""
     try:
         fields = dict(l.split("=", 1) for l in open(TRAFFIC_FILE).read().split()
                       if "=" in l and not l.startswith("#"))
-        src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-        if fields.get("decode_hip_sha256") != src_hash:
+        if fields.get("decode_sources_sha256") != kernel_sources_sha256():
             return None
         return float(fields["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -172,9 +179,11 @@ def workload_bits(kvq, w, xk=None, xv=None):
 
 def other_configs():
     """The other full-size workloads, one GPU: split-K decode time of the 8k-token Llama-shaped
-    layer and of the 128k-token context (caches rotated so their reads come from HBM, launches
-    back to back behind a spin kernel, HIP events on the launch stream), and the ingest rate of
-    the 16 x 4096-token prefill (calibration, allocation, then one append of every token)."""
+    layer, of the 128k-token context and of the 32k-token workload with per-channel key
+    normalization (caches rotated so their reads come from HBM, launches back to back behind
+    a spin kernel, HIP events on the launch stream), and the ingest rate of the 16 x 4096-token
+    prefill (calibration, allocation, then one append of every token), with and without key
+    normalization."""
     import torch
 
     import mixed_precision_quantized_kvq_amd as kvq
@@ -182,12 +191,13 @@ def other_configs():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     res = {}
-    for name, n_inst in (("llama8b_t8k", 5), ("long_t128k", 3)):
+    for name, n_inst, key_norm in (("llama8b_t8k", 5, False), ("long_t128k", 3, False),
+                                   ("qwen8b_t32k", 5, True)):
         w = workloads.make(name)
         s = w["spec"]
         kb, vb = workload_bits(kvq, w)
         cfg = kvq.Config.make(s.batch, s.n_kv, s.n_q, s.head_dim, s.tokens, s.n_sink, s.n_recent, s.dtype,
-                              s.quant, kb, vb)
+                              s.quant, kb, vb, key_norm=key_norm)
         kd = torch.from_numpy(w["k"].view(np.int16)).to(dev)
         vd = torch.from_numpy(w["v"].view(np.int16)).to(dev)
         caches = []
@@ -212,7 +222,7 @@ def other_configs():
             t_us.append(e0.elapsed_time(e1) * 1e3 / 50)
         us = float(np.median(t_us))
         nbytes = decode_bytes(s, kb, vb, s.tokens, s.n_splits)
-        res[name] = {"decode_us": us, "bytes_per_launch": nbytes, "achieved_gbs": nbytes / (us * 1e-6) / 1e9,
+        res[name + ("_key_norm" if key_norm else "")] = {"decode_us": us, "bytes_per_launch": nbytes, "achieved_gbs": nbytes / (us * 1e-6) / 1e9,
                      "frac_of_8tbs": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "k_bits": kb, "v_bits": vb,
                      "n_splits": s.n_splits, "kv_tokens_heads_per_s": s.batch * s.n_kv * s.tokens / (us * 1e-6)}
         del caches, ws, q
@@ -223,26 +233,67 @@ def other_configs():
     xk = torch.from_numpy(np.ascontiguousarray(w["k"][0, :, :s.calib_tokens]).view(np.int16)).to(dev)
     xv = torch.from_numpy(np.ascontiguousarray(w["v"][0, :, :s.calib_tokens]).view(np.int16)).to(dev)
     kb, vb = workload_bits(kvq, w, xk, xv)
-    cfg = kvq.Config.make(s.batch, s.n_kv, s.n_q, s.head_dim, s.tokens, s.n_sink, s.n_recent, s.dtype, s.quant,
-                          kb, vb)
     kd = torch.from_numpy(w["k"].view(np.int16)).to(dev)
     vd = torch.from_numpy(w["v"].view(np.int16)).to(dev)
-    ms = []
-    for _ in range(4):
-        c = kvq.KVCache(cfg, device=dev)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        kvq.append(c, kd, vd, stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        kvq.cache_check(c)
-        ms.append(e0.elapsed_time(e1))
-        del c
-    in_bytes = 2 * kd.numel() * 2
-    t = float(np.median(ms[1:]))
-    res["prefill_t4k"] = {"append_ms": t, "input_bytes": in_bytes, "ingest_gbs": in_bytes / (t * 1e-3) / 1e9,
-                          "tokens_per_s": s.batch * s.tokens / (t * 1e-3), "k_bits": kb, "v_bits": vb}
+    for key_norm in (False, True):
+        cfg = kvq.Config.make(s.batch, s.n_kv, s.n_q, s.head_dim, s.tokens, s.n_sink, s.n_recent, s.dtype,
+                              s.quant, kb, vb, key_norm=key_norm)
+        ms = []
+        for _ in range(4):
+            c = kvq.KVCache(cfg, device=dev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            kvq.append(c, kd, vd, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            kvq.cache_check(c)
+            ms.append(e0.elapsed_time(e1))
+            del c
+        in_bytes = 2 * kd.numel() * 2
+        t = float(np.median(ms[1:]))
+        res["prefill_t4k" + ("_key_norm" if key_norm else "")] = {
+            "append_ms": t, "input_bytes": in_bytes, "ingest_gbs": in_bytes / (t * 1e-3) / 1e9,
+            "tokens_per_s": s.batch * s.tokens / (t * 1e-3), "k_bits": kb, "v_bits": vb}
     return res
+
+
+def model_calibration():
+    """Whole-model offline stage on one GPU: calibration + fit of every (layer, KV head) pair
+    of a Qwen3-8B-shaped model (36 x 8 = 288 pairs, 16 x 512 tokens each, keys and values
+    separately, widths 2..8), then the K and V bit allocations over all 288 pairs. Inputs are
+    resident on the GPU; each call blocks until its result is on the host."""
+    import torch
+
+    import mixed_precision_quantized_kvq_amd as kvq
+    import workloads
+    dev = torch.device("cuda:0")
+    m = workloads.make_model_calib()
+    s = m["spec"]
+    P, T, D = s.pairs, s.tokens, s.head_dim
+    xk = torch.from_numpy(m["k"].view(np.int16)).to(dev)
+    xv = torch.from_numpy(m["v"].view(np.int16)).to(dev)
+    del m["k"], m["v"]
+    ws = torch.empty(kvq.calibrate_workspace_bytes(P, T, D, 2, 8), dtype=torch.uint8, device=dev)
+    q = kvq.QUANT_HYBRID if s.quant == "hybrid" else kvq.QUANT_ASYM
+    kvq.calibrate_fit(xk, s.dtype, kvq.AXIS_KEY, q, 2, 8, workspace=ws)  # warm-up
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        ak, bk, _ = kvq.calibrate_fit(xk, s.dtype, kvq.AXIS_KEY, q, 2, 8, workspace=ws)
+        t1 = time.perf_counter()
+        av, bv, _ = kvq.calibrate_fit(xv, s.dtype, kvq.AXIS_VALUE, q, 2, 8, workspace=ws)
+        t2 = time.perf_counter()
+        kb, _ = kvq.allocate_bits(ak, bk, m["w_k"], m["k_total"], s.b_lo, s.b_hi)
+        vb, _ = kvq.allocate_bits(av, bv, m["w_v"], m["v_total"], s.b_lo, s.b_hi)
+        t3 = time.perf_counter()
+        runs.append((t1 - t0, t2 - t1, t3 - t2, t3 - t0))
+    ck, cv, al, tot = (float(np.median([r[i] for r in runs])) * 1e3 for i in range(4))
+    in_bytes = 2 * P * T * D * 2
+    return {"workload": s.name, "pairs": P, "tokens_per_pair": T, "head_dim": D, "widths": "2..8",
+            "calibrate_k_ms": ck, "calibrate_v_ms": cv, "allocate_k_plus_v_ms": al, "total_ms": tot,
+            "input_bytes": in_bytes, "input_gbs": in_bytes / ((ck + cv) * 1e-3) / 1e9,
+            "k_bits_count": {b: kb.count(b) for b in (2, 3, 4)},
+            "v_bits_count": {b: vb.count(b) for b in (2, 3, 4)}}
 
 
 def main():
@@ -396,6 +447,7 @@ def main():
     }
     if not args.no_other_configs:
         res["other_configs"] = other_configs()
+        res["offline"]["model_calibrate_allocate"] = model_calibration()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, k_bits, v_bits, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -102,10 +102,12 @@ kvq_status kvq_cache_init(kvq_cache* cache, const kvq_config* cfg, void* dev_mem
  * axis KVQ_AXIS_KEY groups 32 channels of a token; KVQ_AXIS_VALUE groups 32 tokens of a
  * channel (n_tokens must then be a multiple of 32). For every head and b = b_lo..b_hi the
  * device computes each group's squared quantization error in float64 (quant = asym or
- * hybrid); the host adds them in group order, divides by n_tokens*head_dim to get D(b),
+ * hybrid) and adds them per 256 groups in a fixed order; the host adds those sums in
+ * order, divides by n_tokens*head_dim to get D(b),
  * fits ln D(b) = ln alpha - b ln beta by least squares and applies the beta fallback
  * (R^2 < 0.96: beta = min(beta, mean beta of the well-fitted heads)).
- * Outputs alpha, beta, r2: host arrays [n_heads]. Needs 2 <= b_lo, b_lo + 2 <= b_hi <= 8.
+ * Outputs alpha, beta, r2: host arrays [n_heads]. Needs 2 <= b_lo, b_lo + 2 <= b_hi <= 8 and
+ * 1 <= n_heads <= 65535 (a whole model's (layer, KV head) pairs fit in one call).
  * ws_dev: device scratch of at least kvq_calibrate_workspace_bytes(...) bytes.
  * BLOCKS until the result is on the host. A head whose inputs are out of range makes the
  * call return KVQ_ERR_RANGE. */

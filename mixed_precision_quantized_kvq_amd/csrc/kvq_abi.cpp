@@ -333,7 +333,8 @@ size_t kvq_calibrate_workspace_bytes(int32_t n_heads, int32_t n_tokens, int32_t 
                                      int32_t b_lo, int32_t b_hi) {
   if (n_heads < 1 || n_tokens < 1 || head_dim < 32 || head_dim % kGroup || b_hi < b_lo) return 0;
   const size_t groups = (size_t)n_tokens * head_dim / kGroup;
-  return align_up((size_t)n_heads * (b_hi - b_lo + 1) * groups * 8) + kAlign;
+  const size_t blocks = (groups + kCalibThreads - 1) / kCalibThreads;
+  return align_up((size_t)n_heads * (b_hi - b_lo + 1) * blocks * 8) + kAlign;
 }
 
 kvq_status kvq_calibrate_fit(const void* x_dev, int32_t dtype, int32_t n_heads, int32_t n_tokens,
@@ -355,9 +356,11 @@ kvq_status kvq_calibrate_fit(const void* x_dev, int32_t dtype, int32_t n_heads, 
   if (ws_bytes < need) return fail(KVQ_ERR_ARG, "workspace too small");
   const int nb = b_hi - b_lo + 1;
   const int64_t groups = (int64_t)n_tokens * head_dim / kGroup;
+  const int64_t blocks = (groups + kCalibThreads - 1) / kCalibThreads;
+  if (blocks > INT32_MAX || n_heads > 65535) return fail(KVQ_ERR_ARG, "calibration slice too large");
   CalibPlan p{};
   p.x = x_dev;
-  p.sse = static_cast<double*>(ws);
+  p.part = static_cast<double*>(ws);
   p.range_flag = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + need - kAlign);
   p.n_heads = n_heads;
   p.n_tokens = n_tokens;
@@ -368,26 +371,27 @@ kvq_status kvq_calibrate_fit(const void* x_dev, int32_t dtype, int32_t n_heads, 
   p.b_lo = b_lo;
   p.nb = nb;
   p.n_groups = groups;
+  p.n_blocks = (int)blocks;
   hipStream_t s = as_stream(stream);
   hipError_t e = hipMemsetAsync(p.range_flag, 0, 4, s);
   if (e != hipSuccess) return hip_fail(e, "calibrate flag clear");
   kvq_status st = check_launch(launch_calib(p, stream), "calibrate launch");
   if (st != KVQ_OK) return st;
-  std::vector<double> sse((size_t)n_heads * nb * groups);
+  std::vector<double> part((size_t)n_heads * nb * blocks);
   uint32_t flag = 0;
-  e = hipMemcpyAsync(sse.data(), p.sse, sse.size() * 8, hipMemcpyDeviceToHost, s);
+  e = hipMemcpyAsync(part.data(), p.part, part.size() * 8, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipMemcpyAsync(&flag, p.range_flag, 4, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "calibrate copy-back");
   if (flag) return fail(KVQ_ERR_RANGE, "calibration input non-finite or |x| > 2^14");
-  // D(b) = (sum of per-group SSE in group order) / element count
+  // D(b) = (sum of the per-group SSE: workgroup sums added in workgroup order) / element count
   std::vector<double> D((size_t)n_heads * nb);
   const double n_el = (double)n_tokens * head_dim;
   for (int h = 0; h < n_heads; ++h)
     for (int i = 0; i < nb; ++i) {
-      const double* g = sse.data() + ((size_t)h * nb + i) * groups;
+      const double* g = part.data() + ((size_t)h * nb + i) * blocks;
       double tot = 0.0;
-      for (int64_t k = 0; k < groups; ++k) tot = tot + g[k];
+      for (int64_t k = 0; k < blocks; ++k) tot = tot + g[k];
       D[(size_t)h * nb + i] = tot / n_el;
     }
   return fit_distortion(n_heads, nb, D.data(), b_lo, alpha, beta, r2);

@@ -94,11 +94,12 @@ int launch_append_flush(const AppendPlan& p, void* stream);
 int launch_append_window(const AppendPlan& p, void* stream);
 int launch_key_norms(const AppendPlan& p, void* stream);  // first append: per-channel key norms
 
+constexpr int kCalibThreads = 256;  // groups per calibration workgroup
 struct CalibPlan {
   const void* x;          // [n_heads][n_tokens][D]
-  double* sse;            // [n_heads][nb][n_groups]
+  double* part;           // [n_heads][nb][n_blocks]: per-workgroup sums of group errors
   uint32_t* range_flag;   // device
-  int n_heads, n_tokens, D, axis, hybrid, dtype, b_lo, nb;
+  int n_heads, n_tokens, D, axis, hybrid, dtype, b_lo, nb, n_blocks;
   int64_t n_groups;
 };
 int launch_calib(const CalibPlan& p, void* stream);

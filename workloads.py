@@ -19,7 +19,8 @@ import dataclasses
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make", "to_raw16", "from_raw16"]
+__all__ = ["Workload", "WORKLOADS", "make", "to_raw16", "from_raw16", "ModelCalib", "MODEL_CALIB",
+           "make_model_calib"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -155,6 +156,66 @@ def make(name: str, seed: int = 0, tokens: int | None = None, batch: int | None 
     del v
     out["q"] = to_raw16(q, s.dtype)
     return out
+
+
+@dataclasses.dataclass(frozen=True)
+class ModelCalib:
+    """Whole-model calibration set: every (layer, KV head) pair of a model, each with the
+    keys and values of `seqs` sequences of `seq_len` tokens, concatenated along tokens."""
+    name: str
+    layers: int
+    kv_heads: int
+    seqs: int
+    seq_len: int
+    head_dim: int
+    dtype: str
+    quant: str
+    k_avg_bits: float          # per-pair budgets: total = avg * layers * kv_heads
+    v_avg_bits: float
+    b_lo: int = 2
+    b_hi: int = 4
+
+    @property
+    def pairs(self) -> int:
+        return self.layers * self.kv_heads
+
+    @property
+    def tokens(self) -> int:
+        return self.seqs * self.seq_len
+
+
+# Qwen3-8B-shaped: 36 layers x 8 KV heads = 288 pairs, 16 sequences x 512 tokens, head_dim
+# 128, bf16, asymmetric quantizer, K budget 3.0 and V budget 2.5 average bits in {2, 3, 4}.
+MODEL_CALIB = ModelCalib("qwen8b_model_calib", 36, 8, 16, 512, 128, "bf16", "asym", 3.0, 2.5)
+
+
+def make_model_calib(spec: ModelCalib = MODEL_CALIB, seed: int = 0, pairs=None, seq_len: int | None = None) -> dict:
+    """Draw a whole-model calibration set. Per pair p (layer-major), from a generator seeded
+    with (seed, p): keys N(0, 1) times channel scales log-normal(0, spread_p) times a pair
+    scale a_p, values N(0, 1) times a pair scale c_p. The pair parameters spread_p ~ U(0.2, 1),
+    a_p, c_p ~ log-normal(0, 0.3) and the weights w_k, w_v ~ log-normal(0, 1) come from a
+    generator seeded with seed, so any subset of pairs can be drawn alone (`pairs`), with
+    identical bits. `seq_len` shrinks every sequence for quick tests.
+    Returns dict: spec, k, v uint16 [n][seqs*seq_len][D] (bits), w_k, w_v float64 [pairs],
+    k_total, v_total (integer budgets), pairs (the drawn pair indices)."""
+    P, D = spec.pairs, spec.head_dim
+    T = spec.seqs * (spec.seq_len if seq_len is None else seq_len)
+    top = np.random.default_rng(seed)
+    spread = top.uniform(0.2, 1.0, size=P)
+    a = top.lognormal(0.0, 0.3, size=P)
+    c = top.lognormal(0.0, 0.3, size=P)
+    w_k = top.lognormal(0.0, 1.0, size=P)
+    w_v = top.lognormal(0.0, 1.0, size=P)
+    idx = list(range(P)) if pairs is None else list(pairs)
+    k = np.empty((len(idx), T, D), dtype=np.uint16)
+    v = np.empty((len(idx), T, D), dtype=np.uint16)
+    for i, p in enumerate(idx):
+        r = np.random.default_rng((seed, p))
+        sig = np.exp(spread[p] * _normal(r, (D,))).astype(np.float32) * np.float32(a[p])
+        k[i] = to_raw16(_normal(r, (T, D)) * sig[None, :], spec.dtype)
+        v[i] = to_raw16(_normal(r, (T, D)) * np.float32(c[p]), spec.dtype)
+    return {"spec": spec, "k": k, "v": v, "w_k": w_k, "w_v": w_v, "pairs": idx,
+            "k_total": int(round(spec.k_avg_bits * P)), "v_total": int(round(spec.v_avg_bits * P))}
 
 
 def random_raw16(rng: np.random.Generator, shape, dtype: str, scale: float = 1.0) -> np.ndarray:
