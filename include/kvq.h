@@ -139,10 +139,10 @@ kvq_status kvq_append(kvq_cache* cache, const void* k_dev, const void* v_dev, in
 
 /* Split-K decode attention for one query token per row (InnerQ Algorithm 1 structure).
  * q_dev: [batch][n_q_heads][head_dim] 16-bit; out_dev: [batch][n_q_heads][head_dim] fp32.
- * The 64-token tiles of each (row, KV head) -- the tiles of the 16-bit sink + recent
- * windows first, then the packed body tiles -- are cut into n_splits (1..256) contiguous
- * ranges; each range yields one partial (m, l, o) and the partials are merged by
- * log-sum-exp. scale <= 0 means 1/sqrt(D).
+ * The packed body tiles of each (row, KV head) are cut into n_splits (1..256) contiguous
+ * ranges, and the 16-bit sink + recent window is dealt out over the same workgroups in
+ * 16-token units; each workgroup yields one partial (m, l, o), and a second launch merges
+ * the partials by log-sum-exp. scale <= 0 means 1/sqrt(D).
  * workspace_dev: at least kvq_decode_workspace_bytes(cache, n_splits) bytes, 256-byte
  * aligned, holding the split partials between the decode and merge launches (no
  * initialization needed). Calls that share a workspace must not run concurrently.
@@ -178,9 +178,9 @@ kvq_status kvq_decode_step(kvq_cache* cache, const void* k_dev, const void* v_de
 /* Synchronize `stream`, read the sticky range flag; KVQ_ERR_RANGE if it is set. */
 kvq_status kvq_cache_check(const kvq_cache* cache, void* stream);
 
-/* Byte offset, from the blob start, of region `region` (0..8: key codes, key meta, value
- * codes, value meta, hybrid flags, sink keys, sink values, ring keys, ring values) of
- * (row, kv_head), and its size; returns 0 and sets *size = 0 on bad arguments. */
+/* Byte offset, from the blob start, of region `region` (0..9: key codes, key meta, value
+ * codes, value meta, hybrid flags, sink keys, sink values, ring keys, ring values, key
+ * norms) of (row, kv_head), and its size; returns 0 and sets *size = 0 on bad arguments. */
 uint64_t kvq_region_offset(const kvq_config* cfg, int32_t row, int32_t kv_head, int32_t region,
                            uint64_t* size);
 

@@ -53,9 +53,9 @@ inline int64_t body_len(int64_t T, int64_t n_sink, int64_t n_recent) {
 }
 inline int ring_slots(int n_recent) { return n_recent + kGroup; }
 
-// Sizes of the 9 regions of one (row, KV head).
+// Sizes of the kRegions regions of one (row, KV head).
 void region_sizes(const kvq_config& cfg, int kv_head, uint64_t sz[kRegions]);
-// Full layout: off[(row*H + head)*9 + region], returns the total blob size.
+// Full layout: off[(row*H + head)*kRegions + region], returns the total blob size.
 uint64_t plan_layout(const kvq_config& cfg, uint64_t* off /* nullable */);
 
 // Validation (sets the error string and returns a status).
