@@ -29,18 +29,48 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 //          26, 35, 58, 70): every code at bit 2 or above; 6 shifts per group
 //   b = 4: per word, codes (i, i + 4) from the word << 2 (i < 2) or the word >> 6 (i >= 2),
 //          at bits 4 (i % 2) + 2: 8 shifts per group
+//   b = 5, 6, 7: the 16 pairs of wide_pair<B>() (one table serves keys and values), every code
+//          at most 4 bits below the top of the mantissa: 13, 13 and 15 shifts per group
 //   b = 8: codes k, k+2 of a word at bits 2-9 (exp 2)
-//   b = 5, 6, 7: codes 4s .. 4s+3 in order, each field extracted and placed at exp 10 - b
 // ---------------------------------------------------------------------------------------
-struct Pair3 {
+struct CodePair {
   int lo, hi, sh, el, eh;  // low code, high code, window shift, their bit positions in the halves
 };
-__host__ __device__ constexpr Pair3 pair3(int j) {
-  constexpr Pair3 t[16] = {{0, 5, -4, 4, 3},   {1, 6, -4, 7, 6},   {2, 7, 0, 6, 5},    {3, 8, 5, 4, 3},
+__host__ __device__ constexpr CodePair pair3(int j) {
+  constexpr CodePair t[16] = {{0, 5, -4, 4, 3},   {1, 6, -4, 7, 6},   {2, 7, 0, 6, 5},    {3, 8, 5, 4, 3},
                            {4, 9, 5, 7, 6},    {10, 15, 26, 4, 3}, {11, 16, 26, 7, 6}, {12, 17, 32, 4, 3},
                            {13, 18, 32, 7, 6}, {14, 19, 35, 7, 6}, {20, 26, 58, 2, 4}, {21, 27, 58, 5, 7},
                            {22, 28, 64, 2, 4}, {23, 29, 64, 5, 7}, {24, 30, 70, 2, 4}, {25, 31, 70, 5, 7}};
   return t[j];
+}
+
+// b = 5, 6, 7: registers j and j + 8 hold pairs of the same bit positions (the value-plan rule
+// below), from 16 windows each:
+//   b = 5: shifted at -5, 5, 25, 39, 52, 70, 75, 95, 100, 105, 125, 130, 135 (raw 0, 32, 64)
+//   b = 6: shifted at 4, 10, 40, 52, 76, 88, 98, 118, 124, 130, 154, 160, 168 (raw 0, 32, 64)
+//   b = 7: shifted at -3, 4, 25, 53, 60, 81, 88, 109, 116, 137, 144, 165, 172, 193, 200 (raw 32)
+template <int B>
+__host__ __device__ constexpr CodePair wide_pair(int j) {
+  static_assert(B >= 5 && B <= 7, "table-driven wide widths");
+  if constexpr (B == 5) {
+    constexpr CodePair t[16] = {{0, 3, -5, 5, 4},   {2, 5, 5, 5, 4},     {7, 10, 32, 3, 2},   {8, 12, 39, 1, 5},
+                                {15, 18, 70, 5, 4}, {20, 23, 95, 5, 4},  {22, 25, 105, 5, 4}, {27, 30, 130, 5, 4},
+                                {1, 4, 0, 5, 4},    {6, 9, 25, 5, 4},    {11, 14, 52, 3, 2},  {13, 17, 64, 1, 5},
+                                {16, 19, 75, 5, 4}, {21, 24, 100, 5, 4}, {26, 29, 125, 5, 4}, {28, 31, 135, 5, 4}};
+    return t[j];
+  } else if constexpr (B == 6) {
+    constexpr CodePair t[16] = {{0, 3, 0, 0, 2},     {1, 4, 4, 2, 4},     {6, 8, 32, 4, 0},    {7, 10, 40, 2, 4},
+                                {11, 14, 64, 2, 4},  {15, 18, 88, 2, 4},  {21, 24, 124, 2, 4}, {26, 29, 154, 2, 4},
+                                {28, 31, 168, 0, 2}, {2, 5, 10, 2, 4},    {17, 19, 98, 4, 0},  {9, 12, 52, 2, 4},
+                                {13, 16, 76, 2, 4},  {20, 23, 118, 2, 4}, {22, 25, 130, 2, 4}, {27, 30, 160, 2, 4}};
+    return t[j];
+  } else {
+    constexpr CodePair t[16] = {{0, 2, -3, 3, 1},    {4, 6, 25, 3, 1},    {8, 10, 53, 3, 1},   {12, 14, 81, 3, 1},
+                                {16, 18, 109, 3, 1}, {20, 22, 137, 3, 1}, {24, 26, 165, 3, 1}, {28, 30, 193, 3, 1},
+                                {1, 3, 4, 3, 1},     {5, 7, 32, 3, 1},    {9, 11, 60, 3, 1},   {13, 15, 88, 3, 1},
+                                {17, 19, 116, 3, 1}, {21, 23, 144, 3, 1}, {25, 27, 172, 3, 1}, {29, 31, 200, 3, 1}};
+    return t[j];
+  }
 }
 
 template <int B>
@@ -56,7 +86,7 @@ struct Slots {
     } else if constexpr (B == 8) {
       return 4 * s + (k >> 1) + 2 * (k & 1);
     } else {
-      return 4 * s + k;
+      return (k & 1) ? wide_pair<B>(j).hi : wide_pair<B>(j).lo;
     }
   }
   __host__ __device__ static constexpr int exp(int s, int k) {
@@ -71,7 +101,7 @@ struct Slots {
     } else if constexpr (B == 8) {
       return 2;
     } else {
-      return 10 - B;
+      return (k & 1) ? wide_pair<B>(j).eh : wide_pair<B>(j).el;
     }
   }
 };
@@ -84,14 +114,6 @@ __host__ __device__ __forceinline__ uint32_t funnel(uint32_t hi, uint32_t lo, in
 #else
   return (uint32_t)((((uint64_t)hi << 32) | lo) >> n);
 #endif
-}
-
-// Bits [pos, pos + B) of a group's little-endian code stream starting at word `base`.
-template <int B, int N>
-__host__ __device__ __forceinline__ uint32_t field(const uint32_t (&w)[N], int base, int pos) {
-  const int wi = base + (pos >> 5), off = pos & 31;
-  if (off + B <= 32) return (w[wi] >> off) & ((1u << B) - 1u);
-  return funnel(w[wi + 1], w[wi], off) & ((1u << B) - 1u);
 }
 
 // 32 bits of the group's stream starting at stream bit `sh` (sh may be negative: shifted
@@ -122,7 +144,7 @@ __host__ __device__ __forceinline__ u32x2 unpack_step(const uint32_t (&w)[N], in
     uint32_t r[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const Pair3 q = pair3(2 * s + h);
+      const CodePair q = pair3(2 * s + h);
       r[h] = window<3>(w, base, q.sh) & ((7u << q.el) | (7u << (16 + q.eh)));
     }
     return u32x2{r[0], r[1]};
@@ -141,10 +163,14 @@ __host__ __device__ __forceinline__ u32x2 unpack_step(const uint32_t (&w)[N], in
     const uint32_t x = w[base + s];
     return u32x2{(x << 2) & 0x03FC03FCu, (x >> 6) & 0x03FC03FCu};
   } else {
-    constexpr int e = 10 - B;
-    const uint32_t c0 = field<B>(w, base, (4 * s + 0) * B), c1 = field<B>(w, base, (4 * s + 1) * B);
-    const uint32_t c2 = field<B>(w, base, (4 * s + 2) * B), c3 = field<B>(w, base, (4 * s + 3) * B);
-    return u32x2{(c0 << e) | (c1 << (16 + e)), (c2 << e) | (c3 << (16 + e))};
+    constexpr uint32_t m = (1u << B) - 1u;
+    uint32_t r[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const CodePair q = wide_pair<B>(2 * s + h);
+      r[h] = window<B>(w, base, q.sh) & ((m << q.el) | (m << (16 + q.eh)));
+    }
+    return u32x2{r[0], r[1]};
   }
 }
 
@@ -161,9 +187,9 @@ __host__ __device__ __forceinline__ u32x2 unpack_step(const uint32_t (&w)[N], in
 // j + 8, cut from 10 windows (raw words at 0, 32, 64; shifted at -4, 5, 26, 36, 58, 67, 70),
 // every code at bit 2 or above: 7 shifts per stream.
 // ---------------------------------------------------------------------------------------
-__host__ __device__ constexpr Pair3 vpair3(int j) {
+__host__ __device__ constexpr CodePair vpair3(int j) {
   // register j = 2 s + h; steps s and s + 4 hold pairs of the same type
-  constexpr Pair3 t[16] = {{0, 5, -4, 4, 3},   {1, 6, -4, 7, 6},   {2, 7, 0, 6, 5},    {10, 15, 26, 4, 3},
+  constexpr CodePair t[16] = {{0, 5, -4, 4, 3},   {1, 6, -4, 7, 6},   {2, 7, 0, 6, 5},    {10, 15, 26, 4, 3},
                            {11, 16, 26, 7, 6}, {20, 26, 58, 2, 4}, {21, 27, 58, 5, 7}, {24, 30, 67, 5, 7},
                            {3, 8, 5, 4, 3},    {4, 9, 5, 7, 6},    {14, 19, 36, 6, 5}, {12, 17, 32, 4, 3},
                            {13, 18, 32, 7, 6}, {22, 28, 64, 2, 4}, {23, 29, 64, 5, 7}, {25, 31, 70, 5, 7}};
@@ -174,7 +200,7 @@ template <int B>
 struct VSlots {
   __host__ __device__ static constexpr int chan(int s, int k) {
     if constexpr (B == 3) {
-      const Pair3 q = vpair3(2 * s + (k >> 1));
+      const CodePair q = vpair3(2 * s + (k >> 1));
       return (k & 1) ? q.hi : q.lo;
     } else {
       return Slots<B>::chan(s, k);
@@ -182,7 +208,7 @@ struct VSlots {
   }
   __host__ __device__ static constexpr int exp(int s, int k) {
     if constexpr (B == 3) {
-      const Pair3 q = vpair3(2 * s + (k >> 1));
+      const CodePair q = vpair3(2 * s + (k >> 1));
       return (k & 1) ? q.eh : q.el;
     } else {
       return Slots<B>::exp(s, k);
@@ -196,7 +222,7 @@ __host__ __device__ __forceinline__ u32x2 unpack_step_v(const uint32_t (&w)[N], 
     uint32_t r[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const Pair3 q = vpair3(2 * s + h);
+      const CodePair q = vpair3(2 * s + h);
       r[h] = window<3>(w, base, q.sh) & ((7u << q.el) | (7u << (16 + q.eh)));
     }
     return u32x2{r[0], r[1]};

@@ -750,7 +750,10 @@ __device__ __forceinline__ void rows16_loop(Smem<D>& sm, const DecodePlan& p, in
 // ---------------------------------------------------------------------------------------
 // Kernel
 // ---------------------------------------------------------------------------------------
-template <int D>
+// WIDE: the instantiation that also holds the path for 5- to 8-bit codes and heads with one
+// 16-bit side. Its register pressure would make the compiler spill in the fast loops, so
+// caches whose heads all take the fast path (or are 16-bit on both sides) use the other one.
+template <int D, bool WIDE>
 // two wavefronts per SIMD (two workgroups per CU): the register budget is 256
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(const DecodePlan p) {
   __shared__ Smem<D> sm;
@@ -897,13 +900,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       default: (void)prologue(); break;
     }
 #undef KVQ_BODY
-  } else {
+  } else if constexpr (WIDE) {
     // wider codes or a 16-bit side: one phase at a time
     WinUnit<D> wt;
     window_issue(wt);
     const float kscale = prologue();
     window(wt);
     mixed_body_loop<D>(sm, p, off, t0, t1, lane, wave, kscale, st);
+  } else {
+    (void)prologue();  // not reached: the host launches the WIDE instantiation for such heads
   }
 
   // ---- combine the wavefronts of this workgroup into one partial (m, l, o). The packed-body
@@ -1048,10 +1053,22 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const DecodePlan p) {
 int launch_decode_splitk(const DecodePlan& p, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   dim3 grid(p.n_splits, p.H, p.B);
-  if (p.D == 128)
-    hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(kThreads), 0, s, p);
+  bool wide = false;
+  for (int h = 0; h < p.H; ++h) {
+    const int kb = p.k_bits[h], vb = p.v_bits[h];
+    wide |= !(kb <= 4 && vb <= 4) && !(kb == 16 && vb == 16);
+  }
+  if (p.D == 128) {
+    if (wide)
+      hipLaunchKernelGGL((decode_kernel<128, true>), grid, dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((decode_kernel<128, false>), grid, dim3(kThreads), 0, s, p);
+  } else {
+    if (wide)
+      hipLaunchKernelGGL((decode_kernel<64, true>), grid, dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((decode_kernel<64, false>), grid, dim3(kThreads), 0, s, p);
+  }
   return (int)hipGetLastError();
 }
 

@@ -617,9 +617,15 @@ def value_stream_position(b: int, s: int, k: int) -> int:
         return lo_hi[j][k % 2]
     if b == 4:
         return 8 * (j // 4) + j % 4 + 4 * (k % 2)
-    if b == 8:
-        return 4 * s + k // 2 + 2 * (k % 2)
-    return 4 * s + k
+    if b in (5, 6, 7):
+        lo_hi = {5: [(0, 3), (2, 5), (7, 10), (8, 12), (15, 18), (20, 23), (22, 25), (27, 30),
+                     (1, 4), (6, 9), (11, 14), (13, 17), (16, 19), (21, 24), (26, 29), (28, 31)],
+                 6: [(0, 3), (1, 4), (6, 8), (7, 10), (11, 14), (15, 18), (21, 24), (26, 29),
+                     (28, 31), (2, 5), (17, 19), (9, 12), (13, 16), (20, 23), (22, 25), (27, 30)],
+                 7: [(0, 2), (4, 6), (8, 10), (12, 14), (16, 18), (20, 22), (24, 26), (28, 30),
+                     (1, 3), (5, 7), (9, 11), (13, 15), (17, 19), (21, 23), (25, 27), (29, 31)]}[b]
+        return lo_hi[j][k % 2]
+    return 4 * s + k // 2 + 2 * (k % 2)   # b == 8
 
 
 def _align(x, a=256):

@@ -2,14 +2,14 @@
 // slot k of step s equal code[chan(s,k)] << exp(s,k), stay inside the 10-bit subnormal
 // mantissa, and chan(., .) is a permutation of the group. The value plans (unpack_step_v,
 // VSlots) must also give the chunks of one K-step the same exponents: exp(s, k) depends on
-// (s % 4, k) only. Codes of 2 to 4 bits sit at mantissa bit 2 or above (bit 4 or above for
-// 2 bits), where the MFMA sums them precisely.
+// (s % 4, k) only. No code sits more than 4 bits below the top of the 10-bit mantissa (2 bits:
+// from bit 4; 3, 4 bits: from bit 2; 5, 7 bits: from bit 1), where the MFMA sums them precisely.
 #include "code_plans.h"
 #include <cstdio>
 #include <random>
 using namespace kvq;
 template <int B>
-constexpr int min_exp() { return B == 2 ? 4 : B <= 4 ? 2 : 0; }
+constexpr int min_exp() { return B == 2 ? 4 : B <= 4 ? 2 : B == 6 ? 0 : B == 8 ? 2 : 1; }
 template <int B>
 int check(std::mt19937& g) {
   int bad = 0;
