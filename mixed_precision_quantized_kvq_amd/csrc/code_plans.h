@@ -174,9 +174,6 @@ __host__ __device__ __forceinline__ u32x2 unpack_step(const uint32_t (&w)[N], in
   }
 }
 
-// fp16 2^(exp(s, k) - 14) in every slot of step s: the weight sum sum_t p_t comes out of the
-// value MFMA with this operand (normal numbers, so its sums are exact to fp32).
-
 // ---------------------------------------------------------------------------------------
 // Value slot plans. The value product runs on the 16x16x32 MFMA: a lane's B operand is 8
 // consecutive tokens u = 0..7 of one channel ("chunk"), two steps s of a 32-code stream:
@@ -230,7 +227,5 @@ __host__ __device__ __forceinline__ u32x2 unpack_step_v(const uint32_t (&w)[N], 
     return unpack_step<B>(w, base, s);
   }
 }
-
-// fp16 2^(exp - 14) for token u = 0..7 of a chunk, as 4 registers (u = 2r low, 2r + 1 high)
 
 }  // namespace kvq

@@ -132,12 +132,6 @@ __device__ __forceinline__ void wave_lds_sync() { __asm__ __volatile__("" ::: "m
 // Keeps global loads issued above this point from being sunk below it (software prefetch).
 __device__ __forceinline__ void issue_barrier() { __asm__ __volatile__("" ::: "memory"); }
 
-template <int B>
-__device__ __forceinline__ u32x2 ones_step(int s) {
-  auto one = [&](int k) { return (uint32_t)(Slots<B>::exp(s, k) + 1) << 10; };
-  return u32x2{one(0) | (one(1) << 16), one(2) | (one(3) << 16)};
-}
-
 // fp16 2^(exp - 14) in the slot of token u = 0..7 of a chunk of K-step kk
 template <int B>
 __device__ __forceinline__ u32x4 ones_chunk(int kk) {
