@@ -162,6 +162,21 @@ kvq_status kvq_decode_splitk(const kvq_cache* cache, const void* q_dev, int32_t 
 kvq_status kvq_decode_merge(const kvq_cache* cache, float* out_dev, int32_t n_splits,
                             void* workspace_dev, size_t ws_bytes, void* stream);
 
+/* Decode attention for the last n_qtok cached tokens of every row at once (multi-token or
+ * speculative decode; the InnerQ Algorithm 1 structure per query token). q_dev:
+ * [batch][n_qtok][n_q_heads][head_dim] 16-bit, out_dev: same shape fp32. Query token i of a
+ * row is the (len - n_qtok + i)-th token and attends causally: to tokens 0 .. len - n_qtok + i.
+ * The n_qtok x G query rows of a KV head share one pass over its cache, so they fill the
+ * MFMA rows a single query leaves empty: n_qtok * (n_q_heads / n_kv_heads) <= 4, else
+ * KVQ_ERR_UNSUPPORTED. The newest n_qtok - 1 tokens must still be in the 16-bit window
+ * (true when n_recent >= n_qtok - 1), else KVQ_ERR_UNSUPPORTED. n_qtok == 1 is exactly
+ * kvq_decode_attention. Workspace: kvq_decode_multi_workspace_bytes(cache, n_splits, n_qtok)
+ * bytes; other arguments and rules as for kvq_decode_attention. */
+size_t kvq_decode_multi_workspace_bytes(const kvq_cache* cache, int32_t n_splits, int32_t n_qtok);
+kvq_status kvq_decode_multi(const kvq_cache* cache, const void* q_dev, int32_t n_qtok, float* out_dev,
+                            int32_t n_splits, float scale, void* workspace_dev, size_t ws_bytes,
+                            void* stream);
+
 /* One decode step (InnerQ Algorithm 1 with techniques (i)-(ii)): append n_new tokens (exactly
  * as kvq_append) and run decode attention for the query over all len + n_new tokens (exactly
  * as kvq_decode_attention), in one call. With n_new == 1 and the token past the sink, the

@@ -19,6 +19,7 @@ __all__ = [
     "KvqError", "Config", "KVCache", "lib", "lib_path", "cache_bytes", "cache_init",
     "calibrate_fit", "calibrate_workspace_bytes", "allocate_bits", "append",
     "decode_workspace_bytes", "decode_attention", "decode_splitk", "decode_merge", "decode_step",
+    "decode_multi_workspace_bytes", "decode_multi",
     "cache_check",
     "region_offset", "last_error",
     "F16", "BF16", "QUANT_ASYM", "QUANT_HYBRID", "KEY_NORM", "AXIS_KEY", "AXIS_VALUE", "ALLOC_CAP_W",
@@ -40,6 +41,7 @@ STATUS = {0: "OK", -1: "ERR_ARG", -2: "ERR_BUDGET", -3: "ERR_CAPACITY", -4: "ERR
 EXPORTS = ("kvq_cache_bytes", "kvq_cache_init", "kvq_calibrate_workspace_bytes",
            "kvq_calibrate_fit", "kvq_allocate_bits", "kvq_append", "kvq_decode_workspace_bytes",
            "kvq_decode_attention", "kvq_decode_splitk", "kvq_decode_merge", "kvq_decode_step",
+           "kvq_decode_multi_workspace_bytes", "kvq_decode_multi",
            "kvq_cache_check",
            "kvq_region_offset", "kvq_last_error")
 
@@ -114,6 +116,8 @@ def lib():
             "kvq_decode_splitk": (I32, [KP, P, I32, ctypes.c_float, P, SZ, P]),
             "kvq_decode_merge": (I32, [KP, P, I32, P, SZ, P]),
             "kvq_decode_step": (I32, [KP, P, P, I32, P, P, I32, ctypes.c_float, P, SZ, P]),
+            "kvq_decode_multi_workspace_bytes": (SZ, [KP, I32, I32]),
+            "kvq_decode_multi": (I32, [KP, P, I32, P, I32, ctypes.c_float, P, SZ, P]),
             "kvq_cache_check": (I32, [KP, P]),
             "kvq_region_offset": (U64, [CP, I32, I32, I32, ctypes.POINTER(U64)]),
             "kvq_last_error": (ctypes.c_char_p, []),
@@ -233,6 +237,26 @@ def decode_attention(cache: KVCache, q, out, n_splits: int, workspace, scale: fl
     _check(lib().kvq_decode_attention(ctypes.byref(cache.handle), _dptr(q), _dptr(out), int(n_splits),
                                       float(scale), _dptr(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream)))
+
+
+def decode_multi_workspace_bytes(cache: KVCache, n_splits: int, n_qtok: int) -> int:
+    n = lib().kvq_decode_multi_workspace_bytes(ctypes.byref(cache.handle), int(n_splits), int(n_qtok))
+    if n == 0:
+        raise KvqError(-1, last_error())
+    return int(n)
+
+
+def decode_multi(cache: KVCache, q, out, n_splits: int, workspace, scale: float = 0.0, stream=None):
+    """q: [batch][n_qtok][n_q_heads][head_dim] 16-bit, the queries of the last n_qtok cached
+    tokens (causal); out: same shape float32 (written)."""
+    import torch
+    c = cache.cfg
+    assert q.is_contiguous() and out.is_contiguous() and out.dtype == torch.float32 and q.dim() == 4
+    assert q.shape[0] == c.batch and tuple(q.shape[2:]) == (c.n_q_heads, c.head_dim)
+    assert tuple(out.shape) == tuple(q.shape)
+    _check(lib().kvq_decode_multi(ctypes.byref(cache.handle), _dptr(q), int(q.shape[1]), _dptr(out), int(n_splits),
+                                  float(scale), _dptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream)))
 
 
 def decode_step(cache: KVCache, k, v, q, out, n_splits: int, workspace, scale: float = 0.0, stream=None):

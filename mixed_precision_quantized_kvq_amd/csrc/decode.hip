@@ -40,6 +40,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxG = 4;
+constexpr float kMaskedScore = -1e30f;  // causally masked window score (log2 units)
 constexpr int kEp = 11;  // softmax weights enter the value MFMA as p * 2^(kEp - e)
 // Lazy rescaling: the running max m moves only when a score exceeds it by more than kTau
 // (log2 units), so weights stay below 2^kTau and p * 2^kEp * 2^kTau fits fp16.
@@ -554,8 +555,8 @@ __device__ __forceinline__ void win_issue(WinUnit<D>& w, int base, int n_valid, 
   }
 }
 template <int D, bool BF16>
-__device__ __forceinline__ void win_compute_t(Smem<D>& sm, const DecodePlan& p, const WinUnit<D>& w, int n_valid,
-                                              int lane, int wave, WaveState<D>& st) {
+__device__ __forceinline__ void win_compute_t(Smem<D>& sm, const DecodePlan& p, const WinUnit<D>& w, int u0,
+                                              int n_valid, int lane, int wave, WaveState<D>& st) {
   // scores: lane t < 16 ends with q_i . k_t for the queries i = 0..3 of rows 0..3
   const int i = lane & 15, j = lane >> 4;
   float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -567,6 +568,18 @@ __device__ __forceinline__ void win_compute_t(Smem<D>& sm, const DecodePlan& p, 
   float sc[kMaxG];
 #pragma unroll
   for (int r = 0; r < kMaxG; ++r) sc[r] = acc[r] * p.scale_log2;
+  if (p.Q > 1) {
+    // several query tokens: row r (query token r / G, the (T - Q + r / G)-th token) sees no
+    // later token. Window token u sits at position u (sink) or u + body (recent ring). A
+    // masked score is a huge finite negative rather than -inf: a wavefront whose first unit
+    // is all masked for a row then keeps a finite running max, and the masked terms vanish
+    // (weight 2^(-1e30 - m) = 0) once a visible token, which every row has, sets the max.
+    const int u = u0 + (lane & 15);
+    const int pos = u < p.n_sink_live ? u : u + p.body;
+#pragma unroll
+    for (int r = 0; r < kMaxG; ++r)
+      if (pos > p.T - p.Q + r / p.G) sc[r] = kMaskedScore;
+  }
   softmax_rows16<D>(sm, wave, lane, lane < n_valid, sc, st, lane & 31, 1.0f, BF16);
   // P.V over the unit's 16 rows: 4 steps of 4 tokens on the 4x4x4 MFMA (lane = channel)
   const int qi = lane & 3;
@@ -600,12 +613,12 @@ __device__ __forceinline__ void win_compute_t(Smem<D>& sm, const DecodePlan& p, 
   wave_lds_sync();
 }
 template <int D>
-__device__ __forceinline__ void win_compute(Smem<D>& sm, const DecodePlan& p, const WinUnit<D>& w, int n_valid,
+__device__ __forceinline__ void win_compute(Smem<D>& sm, const DecodePlan& p, const WinUnit<D>& w, int u0, int n_valid,
                                             int lane, int wave, WaveState<D>& st) {
   if (p.dtype == KVQ_BF16)
-    win_compute_t<D, true>(sm, p, w, n_valid, lane, wave, st);
+    win_compute_t<D, true>(sm, p, w, u0, n_valid, lane, wave, st);
   else
-    win_compute_t<D, false>(sm, p, w, n_valid, lane, wave, st);
+    win_compute_t<D, false>(sm, p, w, u0, n_valid, lane, wave, st);
 }
 
 // Quantized keys and values, both widths fixed: the loads of the next tile are issued before
@@ -755,8 +768,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.G;
+  const int R = G * p.Q;  // query rows of this KV head: row r is query token r / G of query head h G + r % G
   const int kb = head_bits(p.k_bits, h), vb = head_bits(p.v_bits, h);
-  const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)b * p.Hq + (size_t)h * G) * D;
+  // global query row of row r: [B][Q][Hq] order
+  auto grow = [&](int r) { return ((size_t)b * p.Q + r / G) * p.Hq + (size_t)h * G + r % G; };
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q);
 
   // ---- q operands in LDS: raw 16-bit copy, the per-group sums of q, and the fp16 key
   // operand in slot order with q scaled by 2^Eq so that max|q| * 2^Eq lies in [2^14, 2^15)
@@ -774,7 +790,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int i0 = (tid * E) / D;
   uint32_t qraw[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) qraw[e] = i0 < G ? q[(size_t)i0 * D + (tid * E + e) % D] : 0u;
+  for (int e = 0; e < E; ++e) qraw[e] = i0 < R ? q[grow(i0) * D + (tid * E + e) % D] : 0u;
   // per-channel key norms (caches with key normalization, packed key heads): the packed keys
   // hold k / n, so the packed-key operand is built from q * n
   const bool use_norm = p.key_norm && kb != 16;
@@ -867,11 +883,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   };
   auto window = [&](const WinUnit<D>& wt) {
     if (!has_w) return;
-    win_compute<D>(sm, p, wt, wlim(w_first) - w_first * kWinTile, lane, wave, st);
+    win_compute<D>(sm, p, wt, w_first * kWinTile, wlim(w_first) - w_first * kWinTile, lane, wave, st);
     for (int w = w_first + kWaves * p.n_splits; w < p.n_wtiles; w += kWaves * p.n_splits) {
       WinUnit<D> r;
       win_issue<D>(r, w * kWinTile, wlim(w) - w * kWinTile, lane, krow, vrow);
-      win_compute<D>(sm, p, r, wlim(w) - w * kWinTile, lane, wave, st);
+      win_compute<D>(sm, p, r, w * kWinTile, wlim(w) - w * kWinTile, lane, wave, st);
     }
   };
 
@@ -949,9 +965,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (lane == 0) sm.new_s[wave] = acc * p.scale_log2;
   }
   __syncthreads();
-  const size_t rows = (size_t)p.B * p.Hq;
-  const size_t row0 = (size_t)b * p.Hq + (size_t)h * G;
-  for (int idx = tid; idx < G * D; idx += kThreads) {
+  const size_t rows = (size_t)p.B * p.Q * p.Hq;
+  for (int idx = tid; idx < R * D; idx += kThreads) {
     const int i = idx / D, c = idx % D;
     float mw[kWaves], ms = -INFINITY;
 #pragma unroll
@@ -975,10 +990,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         ll += f;
       }
     }
-    p.ws_o[((size_t)split * rows + row0 + i) * D + c] = oo;
+    p.ws_o[((size_t)split * rows + grow(i)) * D + c] = oo;
     if (c == 0) {
-      p.ws_ml[((size_t)split * rows + row0 + i) * 2] = ms;
-      p.ws_ml[((size_t)split * rows + row0 + i) * 2 + 1] = ll;
+      p.ws_ml[((size_t)split * rows + grow(i)) * 2] = ms;
+      p.ws_ml[((size_t)split * rows + grow(i)) * 2 + 1] = ll;
     }
   }
 }
@@ -995,7 +1010,7 @@ constexpr int kMergeChunk = 16;
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const DecodePlan p) {
-  const size_t rows = (size_t)p.B * p.Hq;
+  const size_t rows = (size_t)p.B * p.Q * p.Hq;
   const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
   if (p.new_k != nullptr && idx < (size_t)p.B * p.H * (D / 4)) {
     // fused decode step: the appended token enters its ring slot once every read of the ring
@@ -1068,7 +1083,7 @@ int launch_decode_splitk(const DecodePlan& p, void* stream) {
 
 int launch_decode_merge(const DecodePlan& p, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  const unsigned blocks = (unsigned)(((size_t)p.B * p.Hq * p.D + kThreads - 1) / kThreads);
+  const unsigned blocks = (unsigned)(((size_t)p.B * p.Q * p.Hq * p.D + kThreads - 1) / kThreads);
   if (p.D == 128)
     hipLaunchKernelGGL(merge_kernel<128>, dim3(blocks), dim3(kThreads), 0, s, p);
   else

@@ -165,16 +165,24 @@ kvq_status kvq_append(kvq_cache* cache, const void* k_dev, const void* v_dev, in
   return KVQ_OK;
 }
 
-size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t n_splits) {
+size_t kvq_decode_multi_workspace_bytes(const kvq_cache* cache, int32_t n_splits, int32_t n_qtok) {
   if (check_cache(cache) != KVQ_OK) return 0;
   if (n_splits < 1 || n_splits > 256) {
     set_error("n_splits must be in 1..256");
     return 0;
   }
+  if (n_qtok < 1 || n_qtok > kMaxQueryRows) {
+    set_error("n_qtok must be in 1..4");
+    return 0;
+  }
   const kvq_config& c = cache->cfg;
   const size_t parts = (size_t)n_splits;
-  const size_t rows = (size_t)c.batch * c.n_q_heads;
+  const size_t rows = (size_t)c.batch * n_qtok * c.n_q_heads;
   return align_up(parts * rows * c.head_dim * 4) + align_up(parts * rows * 2 * 4);
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t n_splits) {
+  return kvq_decode_multi_workspace_bytes(cache, n_splits, 1);
 }
 
 }  // extern "C"
@@ -183,7 +191,7 @@ namespace {
 
 // Checks shared by the decode entry points; fills the launch plan.
 kvq_status decode_plan(const kvq_cache* cache, const void* q_dev, float* out_dev, int32_t n_splits, float scale,
-                       void* ws, size_t ws_bytes, DecodePlan& p) {
+                       void* ws, size_t ws_bytes, DecodePlan& p, int32_t n_qtok = 1) {
   kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
   if (cache->len < 1) return fail(KVQ_ERR_ARG, "decode on an empty cache");
@@ -192,7 +200,8 @@ kvq_status decode_plan(const kvq_cache* cache, const void* q_dev, float* out_dev
   if ((q_dev && !aligned(q_dev, 16)) || (out_dev && !aligned(out_dev, 16)) || !aligned(ws, 256))
     return fail(KVQ_ERR_ARG, "q/out must be 16-byte and workspace 256-byte aligned");
   if (!(std::isfinite(scale))) return fail(KVQ_ERR_ARG, "scale must be finite");
-  const size_t need = kvq_decode_workspace_bytes(cache, n_splits);
+  const size_t need = kvq_decode_multi_workspace_bytes(cache, n_splits, n_qtok);
+  if (need == 0) return fail(KVQ_ERR_ARG, last_error());
   if (ws_bytes < need) return fail(KVQ_ERR_ARG, "workspace too small");
   const kvq_config& c = cache->cfg;
   p = DecodePlan{};
@@ -201,13 +210,14 @@ kvq_status decode_plan(const kvq_cache* cache, const void* q_dev, float* out_dev
   p.q = q_dev;
   p.out = out_dev;
   const size_t parts = (size_t)n_splits;
-  const size_t rows = (size_t)c.batch * c.n_q_heads;
+  const size_t rows = (size_t)c.batch * n_qtok * c.n_q_heads;
   p.ws_o = static_cast<float*>(ws);
   p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(parts * rows * c.head_dim * 4));
   p.B = c.batch;
   p.H = c.n_kv_heads;
   p.Hq = c.n_q_heads;
   p.G = c.n_q_heads / c.n_kv_heads;
+  p.Q = n_qtok;
   p.D = c.head_dim;
   p.T = cache->len;
   p.body = (int)body_len(cache->len, c.n_sink, c.n_recent);
@@ -315,6 +325,28 @@ kvq_status kvq_decode_step(kvq_cache* cache, const void* k_dev, const void* v_de
   st = check_launch(launch_decode_splitk(d, stream), "decode launch");
   if (st != KVQ_OK) return st;
   return check_launch(launch_decode_merge(d, stream), "merge launch");
+}
+
+kvq_status kvq_decode_multi(const kvq_cache* cache, const void* q_dev, int32_t n_qtok, float* out_dev,
+                            int32_t n_splits, float scale, void* ws, size_t ws_bytes, void* stream) {
+  if (!q_dev || !out_dev) return fail(KVQ_ERR_ARG, "NULL pointer");
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  const kvq_config& c = cache->cfg;
+  if (n_qtok < 1) return fail(KVQ_ERR_ARG, "n_qtok must be >= 1");
+  if (n_qtok * (c.n_q_heads / c.n_kv_heads) > kMaxQueryRows)
+    return fail(KVQ_ERR_UNSUPPORTED, "n_qtok * (query heads per KV head) must be <= 4");
+  if (cache->len < n_qtok) return fail(KVQ_ERR_ARG, "the cache holds fewer tokens than n_qtok");
+  DecodePlan p;
+  st = decode_plan(cache, q_dev, out_dev, n_splits, scale, ws, ws_bytes, p, n_qtok);
+  if (st != KVQ_OK) return st;
+  // the causal mask is applied to the 16-bit window only: the newest n_qtok - 1 tokens must
+  // not have been quantized into the body yet
+  if (p.body > 0 && p.n_win < n_qtok - 1)
+    return fail(KVQ_ERR_UNSUPPORTED, "n_qtok - 1 exceeds the tokens of the recent window");
+  st = check_launch(launch_decode_splitk(p, stream), "decode launch");
+  if (st != KVQ_OK) return st;
+  return check_launch(launch_decode_merge(p, stream), "merge launch");
 }
 
 kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q_dev, float* out_dev,

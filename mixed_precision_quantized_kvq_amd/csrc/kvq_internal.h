@@ -19,6 +19,7 @@ constexpr int kTile = 64;         // body tokens per key tile (one wavefront, on
 #define KVQ_WIN_TILE 16
 #endif
 constexpr int kWinTile = KVQ_WIN_TILE;
+constexpr int kMaxQueryRows = 4;  // query rows per KV head in one decode launch (heads x tokens)
 constexpr int kRegions = 10;
 constexpr uint64_t kAlign = 256;  // every region starts on a 256-byte boundary
 constexpr uint64_t kHeaderBytes = 256;
@@ -112,6 +113,7 @@ struct DecodePlan {
   float* ws_o;           // [P][B][Hq][D]
   float* ws_ml;          // [P][B][Hq][2]
   int B, H, Hq, G, D, T, body, n_sink_live, n_win, n_sink_cfg, ring;
+  int Q;                 // query tokens per row: the last Q cached tokens, attended causally
   int ring0;             // ring slot of the oldest live window token (body mod ring)
   int n_splits, n_tiles, n_wtiles;  // partials, 64-token body tiles, kWinTile-token window units
   int tiles_per_split;   // body tiles per split (the window tiles are dealt out separately)

@@ -29,6 +29,8 @@ What it computes, and where the pages define it
   3.4, W.10).
 * Bit allocation: continuous reverse waterfilling and its integer greedy form (RateQuant
   page, sections 3.1, 3.3, B.1, B.3, U, W.7), optional sensitivity cap (section W.14).
+* Multi-token decode: the queries of the last Q tokens, each attending causally to its own
+  prefix (decode_multi; the same attention per query token).
 * Attention for the decode query, in float64, over the dequantized cache (InnerQ page,
   "Algorithm 1: multi-head attention with quantized cache in the decode phase", structure
   only: the page's listing is cut off and its projections are outside this path).
@@ -354,6 +356,27 @@ def decode(oc: OracleCache, q_raw: np.ndarray, scale: float | None = None, rows=
         for h in (range(cfg.n_kv) if heads is None else heads):
             Kt, Vt = logical_kv(oc, b, h)
             out[b, h * G:(h + 1) * G] = attention_head(q[b, h * G:(h + 1) * G], Kt, Vt, scale)
+    return out
+
+
+def decode_multi(oc: OracleCache, q_raw: np.ndarray, scale: float | None = None):
+    """Decode output float64 [B][Q][Hq][D] for the queries q_raw [B][Q][Hq][D] of the last Q
+    cached tokens: query token i is the (T - Q + i)-th token and attends to tokens
+    0 .. T - Q + i only (causal decoding of several tokens at once, as in speculative
+    decoding; the InnerQ Algorithm 1 structure per query token)."""
+    cfg = oc.cfg
+    B, Q, Hq, D = q_raw.shape
+    G = Hq // cfg.n_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    q = widen16(q_raw, cfg.dtype).astype(np.float64)
+    out = np.full((B, Q, Hq, D), np.nan)
+    for b in range(B):
+        for h in range(cfg.n_kv):
+            Kt, Vt = logical_kv(oc, b, h)
+            for i in range(Q):
+                n = oc.T - Q + i + 1
+                out[b, i, h * G:(h + 1) * G] = attention_head(q[b, i, h * G:(h + 1) * G], Kt[:n], Vt[:n], scale)
     return out
 
 

@@ -453,3 +453,56 @@ def test_key_norm_decode_steps(first):
     say(f"    worst error / bound over the steps: {worst:.3e}")
     kvq.cache_check(cache)
     assert_regions_equal(cache, O.build_cache(k, v, ocfg, norm_tokens=first))
+
+
+# ------------------------------------------------------------------------------------------
+# Multi-token (causal) decode: the query rows of a KV head are its G query heads x Q tokens
+
+@pytest.mark.parametrize("G,Q,D,T,dtype", [(1, 4, 128, 1333, "bf16"), (2, 2, 128, 700, "fp16"),
+                                           (1, 3, 64, 300, "fp16"), (1, 4, 128, 21, "bf16"),
+                                           (4, 1, 128, 500, "bf16")])
+def test_multi_token_decode(G, Q, D, T, dtype):
+    say(f"case: multi-token decode G={G} Q={Q} D={D} T={T} {dtype}")
+    rng = np.random.default_rng(400 + 10 * G + Q + T)
+    ocfg = O.CacheConfig(2, 3, 3 * G, D, T + 8, 4, 40, dtype, "hybrid", (3, 2, 16), (2, 4, 3))
+    k = workloads.random_raw16(rng, (2, 3, T, D), dtype, 2.0)
+    v = workloads.random_raw16(rng, (2, 3, T, D), dtype)
+    q = workloads.random_raw16(rng, (2, Q, 3 * G, D), dtype)
+    oc = O.build_cache(k, v, ocfg)
+    cache = gpu_cache(ocfg, k, v)
+    want = O.decode_multi(oc, q)
+    qd = to_dev(q)
+    for ns in (1, 3, 16):
+        out = torch.empty((2, Q, 3 * G, D), dtype=torch.float32, device=DEV)
+        ws = torch.zeros(kvq.decode_multi_workspace_bytes(cache, ns, Q), dtype=torch.uint8, device=DEV)
+        kvq.decode_multi(cache, qd, out, ns, ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        for i in range(Q):  # each query token against its own output scale
+            ok, err, bound = within_tol(got[:, i], want[:, i])
+            assert ok, (ns, i, err, bound)
+        say(f"    n_splits={ns}: every query token within tolerance")
+        if Q == 1:
+            ref = gpu_decode(cache, q[:, 0], ns)
+            assert np.array_equal(got[:, 0], ref)
+
+
+def test_multi_token_decode_rejects():
+    ocfg = O.CacheConfig(1, 2, 4, 64, 400, 2, 0, "bf16", "asym", (2, 2), (2, 2))
+    rng = np.random.default_rng(450)
+    k = workloads.random_raw16(rng, (1, 2, 300, 64), "bf16")
+    cache = gpu_cache(ocfg, k, k)
+    ws = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)
+    q3 = torch.zeros((1, 3, 4, 64), dtype=torch.int16, device=DEV)
+    out = torch.zeros((1, 3, 4, 64), dtype=torch.float32, device=DEV)
+    with pytest.raises(kvq.KvqError) as e:  # 2 query heads per KV head x 3 tokens > 4 rows
+        kvq.decode_multi(cache, q3, out, 2, ws)
+    assert e.value.status == -5
+    # n_recent = 0: after a flush the window holds fewer than Q - 1 tokens
+    ocfg1 = O.CacheConfig(1, 2, 2, 64, 400, 2, 0, "bf16", "asym", (2, 2), (2, 2))
+    cache1 = gpu_cache(ocfg1, k[:, :, :290], k[:, :, :290])  # body 288, window 0
+    q4 = torch.zeros((1, 4, 2, 64), dtype=torch.int16, device=DEV)
+    out4 = torch.zeros((1, 4, 2, 64), dtype=torch.float32, device=DEV)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.decode_multi(cache1, q4, out4, 2, ws)
+    assert e.value.status == -5

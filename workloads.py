@@ -64,6 +64,12 @@ WORKLOADS = {
     # first 512 tokens of row 0; K and V budgets 20 each in {2,3,4}.
     "prefill_t4k": Workload("prefill_t4k", 16, 8, 32, 128, 4096, "bf16", 4, 128, "asym", 16,
                             "calibrated", k_total=20, v_total=20, calib_tokens=512),
+    # Multi-head (no GQA) 7B-shaped layer for multi-token decode: 4 rows, 32 query = 32 KV
+    # heads, d 128, 8192 tokens, bf16, per-channel log-normal(0, 0.5) key scales, heads
+    # alternating 3 and 2 bits (K and V alike), 4 split-K chunks; up to 4 query tokens per
+    # row fill the rows a single query leaves empty.
+    "mha7b_t8k": Workload("mha7b_t8k", 4, 32, 32, 128, 8192, "bf16", 4, 128, "hybrid", 4,
+                          "fixed", fixed_bits=(3, 2) * 16),
     # Extreme context: 1 row, 131072 tokens, all heads at 2 bits, fp16, 1% of (head, key
     # channel) pairs scaled x10, 64 split-K chunks.
     "long_t128k": Workload("long_t128k", 1, 8, 32, 128, 131072, "fp16", 4, 128, "asym", 64,
@@ -105,6 +111,7 @@ def make(name: str, seed: int = 0, tokens: int | None = None, batch: int | None 
     Returns a dict with the Workload ``spec`` and:
       k, v      uint16 [B][Hkv][T][D]   16-bit keys / values (bits)
       q         uint16 [B][Hq][D]       decode queries (bits)
+      q_multi   uint16 [B][4][Hq][D]    (mha7b_t8k) queries of the last 4 tokens
       alpha, beta, w (joint) or alpha_k/beta_k/w_k/alpha_v/beta_v/w_v (separate),
       w_k / w_v (calibrated)            float64 [Hkv]
     """
@@ -150,6 +157,8 @@ def make(name: str, seed: int = 0, tokens: int | None = None, batch: int | None 
         elif s.alloc == "calibrated":
             out["w_k"] = rng.lognormal(0.0, 1.0, size=H)
             out["w_v"] = rng.lognormal(0.0, 1.0, size=H)
+    if name == "mha7b_t8k":  # queries of the last 4 tokens of every row (multi-token decode)
+        out["q_multi"] = to_raw16(_normal(rng, (B, 4, Hq, D)), s.dtype)
     out["k"] = to_raw16(k, s.dtype)
     del k
     out["v"] = to_raw16(v, s.dtype)
