@@ -162,6 +162,23 @@ kvq_status kvq_decode_splitk(const kvq_cache* cache, const void* q_dev, int32_t 
 kvq_status kvq_decode_merge(const kvq_cache* cache, float* out_dev, int32_t n_splits,
                             void* workspace_dev, size_t ws_bytes, void* stream);
 
+/* Ragged batches: rows of different lengths in one cache (serving several sequences that
+ * started at different times). The caller keeps each row's length in a host array
+ * row_len[batch] (all 0 after kvq_cache_init) and passes it to these calls, which do not use
+ * or change cache->len; a cache is used either through these calls or through the uniform
+ * ones. At most 64 rows (else KVQ_ERR_UNSUPPORTED).
+ * kvq_append_ragged: row b appends n_new[b] >= 0 tokens, the first n_new[b] of its n_max input
+ * slots: k_dev, v_dev [batch][n_kv_heads][n_max][head_dim] 16-bit. Each row follows the rules
+ * of kvq_append on its own (sink, ring, 32-token flushes; with KVQ_KEY_NORM the norms come
+ * from the row's first non-empty append). The caller then adds n_new[b] to row_len[b].
+ * Host arrays are read before the call returns; KVQ_ERR_CAPACITY if a row would exceed it.
+ * kvq_decode_ragged: one query token per row, row b attending to its row_len[b] >= 1 tokens;
+ * q, out, workspace and rules as for kvq_decode_attention. */
+kvq_status kvq_append_ragged(const kvq_cache* cache, const int32_t* row_len, const int32_t* n_new,
+                             const void* k_dev, const void* v_dev, int32_t n_max, void* stream);
+kvq_status kvq_decode_ragged(const kvq_cache* cache, const int32_t* row_len, const void* q_dev, float* out_dev,
+                             int32_t n_splits, float scale, void* workspace_dev, size_t ws_bytes, void* stream);
+
 /* Decode attention for the last n_qtok cached tokens of every row at once (multi-token or
  * speculative decode; the InnerQ Algorithm 1 structure per query token). q_dev:
  * [batch][n_qtok][n_q_heads][head_dim] 16-bit, out_dev: same shape fp32. Query token i of a

@@ -19,7 +19,7 @@ __all__ = [
     "KvqError", "Config", "KVCache", "lib", "lib_path", "cache_bytes", "cache_init",
     "calibrate_fit", "calibrate_workspace_bytes", "allocate_bits", "append",
     "decode_workspace_bytes", "decode_attention", "decode_splitk", "decode_merge", "decode_step",
-    "decode_multi_workspace_bytes", "decode_multi",
+    "decode_multi_workspace_bytes", "decode_multi", "append_ragged", "decode_ragged",
     "cache_check",
     "region_offset", "last_error",
     "F16", "BF16", "QUANT_ASYM", "QUANT_HYBRID", "KEY_NORM", "AXIS_KEY", "AXIS_VALUE", "ALLOC_CAP_W",
@@ -41,7 +41,7 @@ STATUS = {0: "OK", -1: "ERR_ARG", -2: "ERR_BUDGET", -3: "ERR_CAPACITY", -4: "ERR
 EXPORTS = ("kvq_cache_bytes", "kvq_cache_init", "kvq_calibrate_workspace_bytes",
            "kvq_calibrate_fit", "kvq_allocate_bits", "kvq_append", "kvq_decode_workspace_bytes",
            "kvq_decode_attention", "kvq_decode_splitk", "kvq_decode_merge", "kvq_decode_step",
-           "kvq_decode_multi_workspace_bytes", "kvq_decode_multi",
+           "kvq_decode_multi_workspace_bytes", "kvq_decode_multi", "kvq_append_ragged", "kvq_decode_ragged",
            "kvq_cache_check",
            "kvq_region_offset", "kvq_last_error")
 
@@ -118,6 +118,8 @@ def lib():
             "kvq_decode_step": (I32, [KP, P, P, I32, P, P, I32, ctypes.c_float, P, SZ, P]),
             "kvq_decode_multi_workspace_bytes": (SZ, [KP, I32, I32]),
             "kvq_decode_multi": (I32, [KP, P, I32, P, I32, ctypes.c_float, P, SZ, P]),
+            "kvq_append_ragged": (I32, [KP, ctypes.POINTER(I32), ctypes.POINTER(I32), P, P, I32, P]),
+            "kvq_decode_ragged": (I32, [KP, ctypes.POINTER(I32), P, P, I32, ctypes.c_float, P, SZ, P]),
             "kvq_cache_check": (I32, [KP, P]),
             "kvq_region_offset": (U64, [CP, I32, I32, I32, ctypes.POINTER(U64)]),
             "kvq_last_error": (ctypes.c_char_p, []),
@@ -257,6 +259,34 @@ def decode_multi(cache: KVCache, q, out, n_splits: int, workspace, scale: float 
     _check(lib().kvq_decode_multi(ctypes.byref(cache.handle), _dptr(q), int(q.shape[1]), _dptr(out), int(n_splits),
                                   float(scale), _dptr(workspace), workspace.numel() * workspace.element_size(),
                                   _stream(stream)))
+
+
+def _i32_array(vals):
+    return (ctypes.c_int32 * len(vals))(*[int(x) for x in vals])
+
+
+def append_ragged(cache: KVCache, row_len, n_new, k, v, stream=None):
+    """Row b (current length row_len[b]) appends the first n_new[b] of its k, v slots
+    ([batch][n_kv_heads][n_max][head_dim] 16-bit). The caller updates its row_len."""
+    c = cache.cfg
+    assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape and k.dim() == 4
+    assert tuple(k.shape[:2]) == (c.batch, c.n_kv_heads) and k.shape[3] == c.head_dim
+    assert k.element_size() == 2 and v.element_size() == 2
+    assert len(row_len) == c.batch and len(n_new) == c.batch
+    _check(lib().kvq_append_ragged(ctypes.byref(cache.handle), _i32_array(row_len), _i32_array(n_new), _dptr(k),
+                                   _dptr(v), int(k.shape[2]), _stream(stream)))
+
+
+def decode_ragged(cache: KVCache, row_len, q, out, n_splits: int, workspace, scale: float = 0.0, stream=None):
+    """One query per row ([batch][n_q_heads][head_dim] 16-bit), row b over its row_len[b] tokens."""
+    import torch
+    c = cache.cfg
+    assert q.is_contiguous() and out.is_contiguous() and out.dtype == torch.float32
+    assert tuple(q.shape) == (c.batch, c.n_q_heads, c.head_dim) and tuple(out.shape) == tuple(q.shape)
+    assert len(row_len) == c.batch
+    _check(lib().kvq_decode_ragged(ctypes.byref(cache.handle), _i32_array(row_len), _dptr(q), _dptr(out),
+                                   int(n_splits), float(scale), _dptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def decode_step(cache: KVCache, k, v, q, out, n_splits: int, workspace, scale: float = 0.0, stream=None):

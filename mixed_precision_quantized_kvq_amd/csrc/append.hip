@@ -12,15 +12,31 @@
 namespace kvq {
 namespace {
 
+// Token counts of row b for this append (uniform, or the row's own when ragged).
+__device__ __forceinline__ RowAppend row_append(const AppendPlan& p, int b) {
+  if (!p.ragged) return RowAppend{p.len0, p.len1, p.body0, p.body1, p.n_new};
+  RowAppend a;
+  a.len0 = p.row_len0[b];
+  a.n = p.row_new[b];
+  a.len1 = a.len0 + a.n;
+  auto body = [&](int T) {
+    const int r = T - p.n_sink - p.n_recent;
+    return r <= 0 ? 0 : (r / kGroup) * kGroup;
+  };
+  a.body0 = body(a.len0);
+  a.body1 = body(a.len1);
+  return a;
+}
+
 // Address of absolute token t of (row, head): the ring if it was appended before this call
 // (only live ring tokens are ever flushed), else the new input.
-__device__ __forceinline__ const uint16_t* token_row(const AppendPlan& p, const char* base_ring,
+__device__ __forceinline__ const uint16_t* token_row(const AppendPlan& p, int len0, const char* base_ring,
                                                      const uint16_t* in, int t) {
-  if (t < p.len0) {
+  if (t < len0) {
     const int slot = (t - p.n_sink) % (p.n_recent + kGroup);
     return reinterpret_cast<const uint16_t*>(base_ring) + (size_t)slot * p.D;
   }
-  return in + (size_t)(t - p.len0) * p.D;
+  return in + (size_t)(t - len0) * p.D;
 }
 
 __device__ __forceinline__ void load_row32(const uint16_t* src, int dtype, float (&x)[32]) {
@@ -74,8 +90,10 @@ __device__ __forceinline__ void pack_value_stream(const uint8_t (*codes)[36], in
 // decode kernel's value order.
 __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
   __shared__ alignas(4) uint8_t vcodes[128][36];  // [channel][token of the block], rows padded to 36 bytes
-  const int j = p.body0 / kGroup + blockIdx.x;  // body block index
   const int h = blockIdx.y, b = blockIdx.z;
+  const RowAppend ra = row_append(p, b);
+  if ((int)blockIdx.x >= (ra.body1 - ra.body0) / kGroup) return;  // ragged: this row flushes fewer blocks
+  const int j = ra.body0 / kGroup + blockIdx.x;                    // body block index
   const int D = p.D, Gd = D / kGroup;
   const uint64_t* off = p.off + ((size_t)b * p.H + h) * kRegions;
   const size_t in_off = ((size_t)b * p.H + h) * p.n_new * D;
@@ -91,7 +109,7 @@ __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
     // unquantized head: the block's rows are copied
     if (is_key) {
       const int tt = tid / Gd, g = tid % Gd;
-      const uint16_t* src = token_row(p, p.blob + off[RK], kin, p.n_sink + j * kGroup + tt) + g * kGroup;
+      const uint16_t* src = token_row(p, ra.len0, p.blob + off[RK], kin, p.n_sink + j * kGroup + tt) + g * kGroup;
       uint4* dst = reinterpret_cast<uint4*>(p.blob + off[KC]) + ((size_t)(j * kGroup + tt) * D + g * kGroup) / 8;
 #pragma unroll
       for (int v = 0; v < 4; ++v) dst[v] = reinterpret_cast<const uint4*>(src)[v];
@@ -100,13 +118,13 @@ __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
       uint16_t* dst = reinterpret_cast<uint16_t*>(p.blob + off[VC]);
 #pragma unroll
       for (int k = 0; k < 32; ++k)
-        dst[(size_t)(j * kGroup + k) * D + c] = token_row(p, p.blob + off[RV], vin, p.n_sink + j * kGroup + k)[c];
+        dst[(size_t)(j * kGroup + k) * D + c] = token_row(p, ra.len0, p.blob + off[RV], vin, p.n_sink + j * kGroup + k)[c];
     }
   } else {
     float x[32];
     if (is_key) {
       const int tt = tid / Gd, g = tid % Gd;
-      load_row32(token_row(p, p.blob + off[RK], kin, p.n_sink + j * kGroup + tt) + g * kGroup, p.dtype, x);
+      load_row32(token_row(p, ra.len0, p.blob + off[RK], kin, p.n_sink + j * kGroup + tt) + g * kGroup, p.dtype, x);
       if (p.key_norm) {  // the group holds k_c / n_c (IEEE fp32 division)
         const float* kn = reinterpret_cast<const float*>(p.blob + off[KN]) + g * kGroup;
 #pragma unroll
@@ -116,7 +134,7 @@ __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
       const int c = tid - D;
 #pragma unroll
       for (int k = 0; k < 32; ++k)
-        x[k] = widen16(token_row(p, p.blob + off[RV], vin, p.n_sink + j * kGroup + k)[c], p.dtype);
+        x[k] = widen16(token_row(p, ra.len0, p.blob + off[RV], vin, p.n_sink + j * kGroup + k)[c], p.dtype);
     }
     if (out_of_range(x)) atomicOr(p.range_flag, 1u);
     // the width is uniform over each wavefront (keys: wavefronts 0, 1; values: 2, 3)
@@ -217,7 +235,9 @@ __global__ __launch_bounds__(kNormThreads) void key_norm_kernel(const AppendPlan
   const uint4* k = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.k_in) +
                                                   ((size_t)b * p.H + h) * p.n_new * p.D) + l;
   float m[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-  for (int t = r; t < p.n_new; t += parts) {
+  const RowAppend ra = row_append(p, b);
+  if (p.ragged && !(ra.len0 == 0 && ra.n > 0)) return;  // norms come from a row's first append
+  for (int t = r; t < ra.n; t += parts) {
     const uint4 u = k[(size_t)t * pieces];
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -242,8 +262,10 @@ __global__ __launch_bounds__(kNormThreads) void key_norm_kernel(const AppendPlan
 }
 
 // Copy new tokens that land in the sink or in the recent ring: one thread per 16 bytes of a
-// key or value row. Token index k < n_a is sink token len0 + k, else ring token t_b + k - n_a.
-__global__ __launch_bounds__(256) void append_window_kernel(const AppendPlan p, int n_a, int t_b, int n_tok) {
+// key or value row. Token index k < n_a is sink token len0 + k, else ring token t_b + k - n_a
+// (per row: sink tokens [len0, min(len1, n_sink)), ring tokens [max(len0, n_sink + body1),
+// len1)). The grid covers n_tok tokens per row, the most any row copies.
+__global__ __launch_bounds__(256) void append_window_kernel(const AppendPlan p, int n_tok) {
   const int chunks = p.D / 8;                   // 16-byte chunks per row
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)p.B * p.H * n_tok * 2 * chunks;
@@ -255,10 +277,14 @@ __global__ __launch_bounds__(256) void append_window_kernel(const AppendPlan p, 
   const int k = (int)(r % n_tok);
   r /= n_tok;
   const int h = (int)(r % p.H), b = (int)(r / p.H);
-  const int t = k < n_a ? p.len0 + k : t_b + (k - n_a);
+  const RowAppend ra = row_append(p, b);
+  const int n_a = max(0, min(ra.len1, p.n_sink) - ra.len0);
+  const int t_b = max(ra.len0, p.n_sink + ra.body1);
+  if (k >= n_a + max(0, ra.len1 - t_b)) return;
+  const int t = k < n_a ? ra.len0 + k : t_b + (k - n_a);
   const uint64_t* off = p.off + ((size_t)b * p.H + h) * kRegions;
   const uint16_t* in = reinterpret_cast<const uint16_t*>(kv ? p.v_in : p.k_in) +
-                       (((size_t)b * p.H + h) * p.n_new + (t - p.len0)) * p.D;
+                       (((size_t)b * p.H + h) * p.n_new + (t - ra.len0)) * p.D;
   char* dst_row;
   if (t < p.n_sink) {
     dst_row = p.blob + off[kv ? SV : SK] + (size_t)t * p.D * 2;
@@ -272,7 +298,11 @@ __global__ __launch_bounds__(256) void append_window_kernel(const AppendPlan p, 
 }  // namespace
 
 int launch_append_flush(const AppendPlan& p, void* stream) {
-  const int nblk = (p.body1 - p.body0) / kGroup;
+  int nblk = 0;
+  for (int b = 0; b < (p.ragged ? p.B : 1); ++b) {
+    const RowAppend a = host_row_append(p, b);
+    nblk = max(nblk, (a.body1 - a.body0) / kGroup);
+  }
   if (nblk <= 0) return (int)hipSuccess;
   dim3 grid(nblk, p.H, p.B);
   hipLaunchKernelGGL(append_flush_kernel, grid, dim3(2 * p.D), 0, (hipStream_t)stream, p);
@@ -286,16 +316,19 @@ int launch_key_norms(const AppendPlan& p, void* stream) {
 
 int launch_append_window(const AppendPlan& p, void* stream) {
   // sink tokens [len0, min(len1, n_sink)); ring tokens [max(len0, n_sink + body1), len1)
-  const int n_a = max(0, min(p.len1, p.n_sink) - p.len0);
-  const int t_b = max(p.len0, p.n_sink + p.body1);
-  const int n_b = max(0, p.len1 - t_b);
-  const int n_tok = n_a + n_b;
+  int n_tok = 0;
+  for (int b = 0; b < (p.ragged ? p.B : 1); ++b) {
+    const RowAppend a = host_row_append(p, b);
+    const int n_a = max(0, min(a.len1, p.n_sink) - a.len0);
+    const int t_b = max(a.len0, p.n_sink + a.body1);
+    n_tok = max(n_tok, n_a + max(0, a.len1 - t_b));
+  }
   if (n_tok == 0) return (int)hipSuccess;
   const long long total = (long long)p.B * p.H * n_tok * 2 * (p.D / 8);
   const int threads = 256;
   const long long blocks = (total + threads - 1) / threads;
   hipLaunchKernelGGL(append_window_kernel, dim3((unsigned)blocks), dim3(threads), 0,
-                     (hipStream_t)stream, p, n_a, t_b, n_tok);
+                     (hipStream_t)stream, p, n_tok);
   return (int)hipGetLastError();
 }
 

@@ -534,6 +534,30 @@ __device__ __forceinline__ void rows16_compute(Smem<D>& sm, const DecodePlan& p,
 // Keys are read cooperatively (lane (t, j): token t = lane % 16, channels 32 s + 8 j .. +7 of
 // step s), which is the B operand of a 16x16x32 MFMA whose rows 0..3 are the queries; values
 // are whole rows, lane = channel pair (D = 128) or channel (D = 64), as for 16-bit tiles.
+// Token geometry of one row: its length, quantized body, live sink and window tokens, the
+// ring's oldest slot, and how its body tiles and window units are dealt out. Uniform rows
+// take it from the plan; ragged rows derive it from their length by the host's rules (the
+// body is every whole 32-token block that has left the window of n_recent..n_recent + 31).
+struct RowGeom {
+  int T, body, nsl, n_win, ring0, n_tiles, n_wtiles, tps;
+};
+__device__ __forceinline__ RowGeom row_geom(const DecodePlan& p, int b) {
+  if (!p.ragged)
+    return RowGeom{p.T, p.body, p.n_sink_live, p.n_win, p.ring0, p.n_tiles, p.n_wtiles, p.tiles_per_split};
+  RowGeom g;
+  g.T = p.row_len[b];
+  const int n_recent = p.ring - kGroup;
+  const int r = g.T - p.n_sink_cfg - n_recent;
+  g.body = r <= 0 ? 0 : (r / kGroup) * kGroup;
+  g.nsl = min(g.T, p.n_sink_cfg);
+  g.n_win = g.T - g.nsl - g.body;
+  g.ring0 = g.body % p.ring;
+  g.n_tiles = (g.body + kTile - 1) / kTile;
+  g.n_wtiles = (g.nsl + g.n_win + kWinTile - 1) / kWinTile;
+  g.tps = (g.n_tiles + p.n_splits - 1) / p.n_splits;
+  return g;
+}
+
 template <int D>
 struct WinUnit {
   u32x4 k[D / 32];
@@ -555,8 +579,8 @@ __device__ __forceinline__ void win_issue(WinUnit<D>& w, int base, int n_valid, 
   }
 }
 template <int D, bool BF16>
-__device__ __forceinline__ void win_compute_t(Smem<D>& sm, const DecodePlan& p, const WinUnit<D>& w, int u0,
-                                              int n_valid, int lane, int wave, WaveState<D>& st) {
+__device__ __forceinline__ void win_compute_t(Smem<D>& sm, const DecodePlan& p, const RowGeom& g, const WinUnit<D>& w,
+                                              int u0, int n_valid, int lane, int wave, WaveState<D>& st) {
   // scores: lane t < 16 ends with q_i . k_t for the queries i = 0..3 of rows 0..3
   const int i = lane & 15, j = lane >> 4;
   float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -575,10 +599,10 @@ __device__ __forceinline__ void win_compute_t(Smem<D>& sm, const DecodePlan& p, 
     // is all masked for a row then keeps a finite running max, and the masked terms vanish
     // (weight 2^(-1e30 - m) = 0) once a visible token, which every row has, sets the max.
     const int u = u0 + (lane & 15);
-    const int pos = u < p.n_sink_live ? u : u + p.body;
+    const int pos = u < g.nsl ? u : u + g.body;
 #pragma unroll
     for (int r = 0; r < kMaxG; ++r)
-      if (pos > p.T - p.Q + r / p.G) sc[r] = kMaskedScore;
+      if (pos > g.T - p.Q + r / p.G) sc[r] = kMaskedScore;
   }
   softmax_rows16<D>(sm, wave, lane, lane < n_valid, sc, st, lane & 31, 1.0f, BF16);
   // P.V over the unit's 16 rows: 4 steps of 4 tokens on the 4x4x4 MFMA (lane = channel)
@@ -613,20 +637,20 @@ __device__ __forceinline__ void win_compute_t(Smem<D>& sm, const DecodePlan& p, 
   wave_lds_sync();
 }
 template <int D>
-__device__ __forceinline__ void win_compute(Smem<D>& sm, const DecodePlan& p, const WinUnit<D>& w, int u0, int n_valid,
-                                            int lane, int wave, WaveState<D>& st) {
+__device__ __forceinline__ void win_compute(Smem<D>& sm, const DecodePlan& p, const RowGeom& g, const WinUnit<D>& w,
+                                            int u0, int n_valid, int lane, int wave, WaveState<D>& st) {
   if (p.dtype == KVQ_BF16)
-    win_compute_t<D, true>(sm, p, w, u0, n_valid, lane, wave, st);
+    win_compute_t<D, true>(sm, p, g, w, u0, n_valid, lane, wave, st);
   else
-    win_compute_t<D, false>(sm, p, w, u0, n_valid, lane, wave, st);
+    win_compute_t<D, false>(sm, p, g, w, u0, n_valid, lane, wave, st);
 }
 
 // Quantized keys and values, both widths fixed: the loads of the next tile are issued before
 // the current tile is computed.
 template <int D, int KB, int VB, class Prologue, class WindowIssue, class Window>
-__device__ __forceinline__ void body_loop(Smem<D>& sm, const DecodePlan& p, const uint64_t* off, int t0, int t1,
-                                          int lane, int wave, Prologue prologue, WindowIssue window_issue, Window window,
-                                          WaveState<D>& st) {
+__device__ __forceinline__ void body_loop(Smem<D>& sm, const DecodePlan& p, const uint64_t* off, int body, int t0,
+                                          int t1, int lane, int wave, Prologue prologue, WindowIssue window_issue,
+                                          Window window, WaveState<D>& st) {
   const BodySrc src = body_src(p, off);
   int tile = t0 + wave;
   const bool any = tile < t1;
@@ -654,8 +678,8 @@ __device__ __forceinline__ void body_loop(Smem<D>& sm, const DecodePlan& p, cons
     issue_barrier();
     float sc[kMaxG];
     key_phase<D, KB>(sm, kcur, lane, kscale, sc);
-    softmax_body<D>(sm, wave, lane, tile * kTile + lane < p.body, sc, st, pscl);
-    value_phase<D, VB>(sm, wave, vcur, lane, min(2, (p.body - tile * kTile) / 32), st);
+    softmax_body<D>(sm, wave, lane, tile * kTile + lane < body, sc, st, pscl);
+    value_phase<D, VB>(sm, wave, vcur, lane, min(2, (body - tile * kTile) / 32), st);
     wave_lds_sync();
     tile = next;
   };
@@ -687,8 +711,8 @@ __device__ __forceinline__ void value_tile_q(Smem<D>& sm, int wave, const BodySr
 // Body tiles of heads with a 16-bit key or value side (one phase 16-bit, the other packed
 // or 16-bit); no prefetch.
 template <int D>
-__device__ __forceinline__ void mixed_body_loop(Smem<D>& sm, const DecodePlan& p, const uint64_t* off, int t0, int t1, int lane,
-                                int wave, float kscale, WaveState<D>& st) {
+__device__ __forceinline__ void mixed_body_loop(Smem<D>& sm, const DecodePlan& p, const uint64_t* off, int body, int t0,
+                                                int t1, int lane, int wave, float kscale, WaveState<D>& st) {
   const int kb = head_bits(p.k_bits, blockIdx.y), vb = head_bits(p.v_bits, blockIdx.y);
   const bool bf16 = p.dtype == KVQ_BF16;
   const uint16_t* kr = reinterpret_cast<const uint16_t*>(p.blob + off[KC]);
@@ -696,8 +720,8 @@ __device__ __forceinline__ void mixed_body_loop(Smem<D>& sm, const DecodePlan& p
   const BodySrc src = body_src(p, off);
   for (int tile = t0 + wave; tile < t1; tile += kWaves) {
     const int tok = tile * kTile + lane;
-    const bool valid = tok < p.body;
-    const int n_valid = min(kTile, p.body - tile * kTile);
+    const bool valid = tok < body;
+    const int n_valid = min(kTile, body - tile * kTile);
     float sc[kMaxG];
     switch (kb) {
       case 2: key_tile_q<D, 2>(sm, src, tile, lane, kscale, sc); break;
@@ -859,8 +883,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // units spread the 16-bit window over many wavefronts instead of loading a few of them
   // with several body tiles' worth of bytes. A wavefront's first window unit is loaded
   // before the query prologue, so its latency is hidden.
-  const int t0 = split * p.tiles_per_split, t1 = min(p.n_tiles, t0 + p.tiles_per_split);
-  const int n_wtok = p.n_sink_live + p.n_win;
+  const RowGeom g = row_geom(p, b);
+  const int body = g.body;
+  const int t0 = split * g.tps, t1 = min(g.n_tiles, t0 + g.tps);
+  const int n_wtok = g.nsl + g.n_win;
   const int w_first = split + p.n_splits * (kWaves - 1 - wave);  // k = kWaves - 1 - wave
   const uint16_t* sk = reinterpret_cast<const uint16_t*>(p.blob + off[SK]);
   const uint16_t* sv = reinterpret_cast<const uint16_t*>(p.blob + off[SV]);
@@ -868,14 +894,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const uint16_t* rv = reinterpret_cast<const uint16_t*>(p.blob + off[RV]);
   // window token u < n_sink_live is sink row u, else ring slot (ring0 + u - n_sink_live) mod
   // ring, ring0 = body mod ring (the ring's oldest live slot)
-  const int nsl = p.n_sink_live, ring0 = p.ring0, ring = p.ring;
+  const int nsl = g.nsl, ring0 = g.ring0, ring = p.ring;
   auto slot = [=](int u) {
     const int r = ring0 + (u - nsl);
     return r >= ring ? r - ring : r;
   };
   auto krow = [=](int u) { return u < nsl ? sk + (size_t)u * D : rk + (size_t)slot(u) * D; };
   auto vrow = [=](int u) { return u < nsl ? sv + (size_t)u * D : rv + (size_t)slot(u) * D; };
-  const bool has_w = w_first < p.n_wtiles;
+  const bool has_w = w_first < g.n_wtiles;
   auto wlim = [=](int w) { return min(n_wtok, (w + 1) * kWinTile); };  // end of window unit w
   // issue the value loads of the first window tile (before the prologue); compute the window
   auto window_issue = [&](WinUnit<D>& wt) {
@@ -883,11 +909,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   };
   auto window = [&](const WinUnit<D>& wt) {
     if (!has_w) return;
-    win_compute<D>(sm, p, wt, w_first * kWinTile, wlim(w_first) - w_first * kWinTile, lane, wave, st);
-    for (int w = w_first + kWaves * p.n_splits; w < p.n_wtiles; w += kWaves * p.n_splits) {
+    win_compute<D>(sm, p, g, wt, w_first * kWinTile, wlim(w_first) - w_first * kWinTile, lane, wave, st);
+    for (int w = w_first + kWaves * p.n_splits; w < g.n_wtiles; w += kWaves * p.n_splits) {
       WinUnit<D> r;
       win_issue<D>(r, w * kWinTile, wlim(w) - w * kWinTile, lane, krow, vrow);
-      win_compute<D>(sm, p, r, w * kWinTile, wlim(w) - w * kWinTile, lane, wave, st);
+      win_compute<D>(sm, p, g, r, w * kWinTile, wlim(w) - w * kWinTile, lane, wave, st);
     }
   };
 
@@ -898,12 +924,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     window(wt);
     const uint16_t* kr = reinterpret_cast<const uint16_t*>(p.blob + off[KC]);
     const uint16_t* vr = reinterpret_cast<const uint16_t*>(p.blob + off[VC]);
-    rows16_loop<D>(sm, p, t0 * kTile, min(p.body, t1 * kTile), lane, wave, st,
+    rows16_loop<D>(sm, p, t0 * kTile, min(body, t1 * kTile), lane, wave, st,
                    [&](int u) { return kr + (size_t)u * D; }, [&](int u) { return vr + (size_t)u * D; });
   } else if (kb <= 4 && vb <= 4) {
     // the widths the allocator hands out in {2,3,4}: prefetching loop per combination
 #define KVQ_BODY(KB_, VB_) \
-  case KB_ * 16 + VB_: body_loop<D, KB_, VB_>(sm, p, off, t0, t1, lane, wave, prologue, window_issue, window, st); break;
+  case KB_ * 16 + VB_: body_loop<D, KB_, VB_>(sm, p, off, body, t0, t1, lane, wave, prologue, window_issue, window, st); break;
     switch (kb * 16 + vb) {
       KVQ_BODY(2, 2) KVQ_BODY(2, 3) KVQ_BODY(2, 4) KVQ_BODY(3, 2) KVQ_BODY(3, 3) KVQ_BODY(3, 4)
       KVQ_BODY(4, 2) KVQ_BODY(4, 3) KVQ_BODY(4, 4)
@@ -916,7 +942,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     window_issue(wt);
     const float kscale = prologue();
     window(wt);
-    mixed_body_loop<D>(sm, p, off, t0, t1, lane, wave, kscale, st);
+    mixed_body_loop<D>(sm, p, off, body, t0, t1, lane, wave, kscale, st);
   } else {
     (void)prologue();  // not reached: the host launches the WIDE instantiation for such heads
   }

@@ -165,6 +165,61 @@ kvq_status kvq_append(kvq_cache* cache, const void* k_dev, const void* v_dev, in
   return KVQ_OK;
 }
 
+kvq_status kvq_append_ragged(const kvq_cache* cache, const int32_t* row_len, const int32_t* n_new,
+                             const void* k_dev, const void* v_dev, int32_t n_max, void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  const kvq_config& c = cache->cfg;
+  if (!row_len || !n_new) return fail(KVQ_ERR_ARG, "NULL row_len or n_new");
+  if (c.batch > kMaxRaggedRows) return fail(KVQ_ERR_UNSUPPORTED, "ragged calls take at most 64 rows");
+  if (n_max < 0) return fail(KVQ_ERR_ARG, "n_max must be >= 0");
+  bool any = false, first = false;
+  for (int b = 0; b < c.batch; ++b) {
+    if (row_len[b] < 0 || n_new[b] < 0 || n_new[b] > n_max) return fail(KVQ_ERR_ARG, "row length or n_new out of range");
+    if ((int64_t)row_len[b] + n_new[b] > c.capacity) return fail(KVQ_ERR_CAPACITY, "append exceeds capacity");
+    any |= n_new[b] > 0;
+    first |= row_len[b] == 0 && n_new[b] > 0;
+  }
+  if (!any) return KVQ_OK;
+  if (!k_dev || !v_dev) return fail(KVQ_ERR_ARG, "NULL input");
+  if (!aligned(k_dev, 16) || !aligned(v_dev, 16)) return fail(KVQ_ERR_ARG, "inputs must be 16-byte aligned");
+  AppendPlan p{};
+  p.k_in = k_dev;
+  p.v_in = v_dev;
+  p.blob = static_cast<char*>(cache->dev);
+  p.off = table_ptr(cache);
+  p.range_flag = flag_ptr(cache);
+  p.B = c.batch;
+  p.H = c.n_kv_heads;
+  p.D = c.head_dim;
+  p.n_new = n_max;  // the input's token stride
+  p.n_sink = c.n_sink;
+  p.n_recent = c.n_recent;
+  p.dtype = c.dtype;
+  p.hybrid = quant_mode(c) == KVQ_QUANT_HYBRID;
+  p.key_norm = key_norm(c);
+  std::memcpy(p.k_bits, c.k_bits, sizeof(p.k_bits));
+  std::memcpy(p.v_bits, c.v_bits, sizeof(p.v_bits));
+  p.ragged = 1;
+  bool flush = false;
+  for (int b = 0; b < c.batch; ++b) {
+    p.row_len0[b] = row_len[b];
+    p.row_new[b] = n_new[b];
+    const RowAppend a = host_row_append(p, b);
+    flush |= a.body1 > a.body0;
+  }
+  // same order as kvq_append: norms of rows appended for the first time, flushes, window copies
+  if (p.key_norm && first) {
+    st = check_launch(launch_key_norms(p, stream), "key norm launch");
+    if (st != KVQ_OK) return st;
+  }
+  if (flush) {
+    st = check_launch(launch_append_flush(p, stream), "append flush launch");
+    if (st != KVQ_OK) return st;
+  }
+  return check_launch(launch_append_window(p, stream), "append window launch");
+}
+
 size_t kvq_decode_multi_workspace_bytes(const kvq_cache* cache, int32_t n_splits, int32_t n_qtok) {
   if (check_cache(cache) != KVQ_OK) return 0;
   if (n_splits < 1 || n_splits > 256) {
@@ -325,6 +380,28 @@ kvq_status kvq_decode_step(kvq_cache* cache, const void* k_dev, const void* v_de
   st = check_launch(launch_decode_splitk(d, stream), "decode launch");
   if (st != KVQ_OK) return st;
   return check_launch(launch_decode_merge(d, stream), "merge launch");
+}
+
+kvq_status kvq_decode_ragged(const kvq_cache* cache, const int32_t* row_len, const void* q_dev, float* out_dev,
+                             int32_t n_splits, float scale, void* ws, size_t ws_bytes, void* stream) {
+  if (!q_dev || !out_dev || !row_len) return fail(KVQ_ERR_ARG, "NULL pointer");
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  const kvq_config& c = cache->cfg;
+  if (c.batch > kMaxRaggedRows) return fail(KVQ_ERR_UNSUPPORTED, "ragged calls take at most 64 rows");
+  for (int b = 0; b < c.batch; ++b)
+    if (row_len[b] < 1 || row_len[b] > c.capacity) return fail(KVQ_ERR_ARG, "every row needs 1..capacity tokens");
+  // plan on a copy whose len is a valid stand-in; the kernels take each row's own length
+  kvq_cache any = *cache;
+  any.len = row_len[0];
+  DecodePlan p;
+  st = decode_plan(&any, q_dev, out_dev, n_splits, scale, ws, ws_bytes, p);
+  if (st != KVQ_OK) return st;
+  p.ragged = 1;
+  for (int b = 0; b < c.batch; ++b) p.row_len[b] = row_len[b];
+  st = check_launch(launch_decode_splitk(p, stream), "decode launch");
+  if (st != KVQ_OK) return st;
+  return check_launch(launch_decode_merge(p, stream), "merge launch");
 }
 
 kvq_status kvq_decode_multi(const kvq_cache* cache, const void* q_dev, int32_t n_qtok, float* out_dev,

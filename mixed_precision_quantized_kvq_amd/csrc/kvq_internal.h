@@ -20,6 +20,7 @@ constexpr int kTile = 64;         // body tokens per key tile (one wavefront, on
 #endif
 constexpr int kWinTile = KVQ_WIN_TILE;
 constexpr int kMaxQueryRows = 4;  // query rows per KV head in one decode launch (heads x tokens)
+constexpr int kMaxRaggedRows = 64;  // rows of a ragged call (per-row lengths travel as kernel arguments)
 constexpr int kRegions = 10;
 constexpr uint64_t kAlign = 256;  // every region starts on a 256-byte boundary
 constexpr uint64_t kHeaderBytes = 256;
@@ -90,7 +91,21 @@ struct AppendPlan {
   int key_norm;          // keys of quantized heads are divided by the stored per-channel norms
   alignas(4) uint8_t k_bits[KVQ_MAX_KV_HEADS];  // word-aligned: kernels read them a word at a time
   alignas(4) uint8_t v_bits[KVQ_MAX_KV_HEADS];
+  // ragged rows: row b holds row_len0[b] tokens and appends row_new[b] (its first ones of the
+  // n_new input slots); len0, len1, body0 and body1 above are then ignored
+  int ragged;
+  int32_t row_len0[kMaxRaggedRows];
+  int32_t row_new[kMaxRaggedRows];
 };
+// Token counts of one row for an append: before / after, body before / after, new tokens.
+struct RowAppend {
+  int len0, len1, body0, body1, n;
+};
+inline RowAppend host_row_append(const AppendPlan& p, int b) {
+  if (!p.ragged) return RowAppend{p.len0, p.len1, p.body0, p.body1, p.n_new};
+  const int l0 = p.row_len0[b], n = p.row_new[b];
+  return RowAppend{l0, l0 + n, (int)body_len(l0, p.n_sink, p.n_recent), (int)body_len(l0 + n, p.n_sink, p.n_recent), n};
+}
 int launch_append_flush(const AppendPlan& p, void* stream);
 int launch_append_window(const AppendPlan& p, void* stream);
 int launch_key_norms(const AppendPlan& p, void* stream);  // first append: per-channel key norms
@@ -129,6 +144,10 @@ struct DecodePlan {
   int new_slot;
   alignas(4) uint8_t k_bits[KVQ_MAX_KV_HEADS];  // word-aligned: kernels read them a word at a time
   alignas(4) uint8_t v_bits[KVQ_MAX_KV_HEADS];
+  // ragged rows: row b holds row_len[b] tokens, and T, body, n_sink_live, n_win, ring0,
+  // n_tiles, n_wtiles and tiles_per_split above are ignored (each workgroup derives its row's)
+  int ragged;
+  int32_t row_len[kMaxRaggedRows];
 };
 int launch_decode_splitk(const DecodePlan& p, void* stream);
 

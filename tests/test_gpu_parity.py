@@ -506,3 +506,127 @@ def test_multi_token_decode_rejects():
     with pytest.raises(kvq.KvqError) as e:
         kvq.decode_multi(cache1, q4, out4, 2, ws)
     assert e.value.status == -5
+
+
+# ------------------------------------------------------------------------------------------
+# Ragged batches: rows of different lengths, each appended and decoded on its own schedule
+
+def _ragged_input(chunks_k, chunks_v, n_max, H, D):
+    """[B][H][n_max][D] inputs holding row b's chunk in its first slots; the unused slots hold
+    garbage that must never be read."""
+    B = len(chunks_k)
+    rng = np.random.default_rng(n_max + 7 * B)
+    k = rng.integers(0, 1 << 16, size=(B, H, n_max, D), dtype=np.uint16)
+    v = rng.integers(0, 1 << 16, size=(B, H, n_max, D), dtype=np.uint16)
+    for b in range(B):
+        n = chunks_k[b].shape[1]
+        k[b, :, :n] = chunks_k[b]
+        v[b, :, :n] = chunks_v[b]
+    return k, v
+
+
+def _row_cfg(ocfg):
+    return O.CacheConfig(1, ocfg.n_kv, ocfg.n_q, ocfg.head_dim, ocfg.capacity, ocfg.n_sink, ocfg.n_recent,
+                         ocfg.dtype, ocfg.quant, ocfg.k_bits, ocfg.v_bits, key_norm=ocfg.key_norm)
+
+
+def _check_ragged(cache, ocfg, k_rows, v_rows, lens, first, q, splits):
+    outs = {}
+    for ns in splits:
+        out = torch.empty((ocfg.batch, ocfg.n_q, ocfg.head_dim), dtype=torch.float32, device=DEV)
+        ws = torch.zeros(kvq.decode_workspace_bytes(cache, ns), dtype=torch.uint8, device=DEV)
+        kvq.decode_ragged(cache, lens, to_dev(q), out, ns, ws)
+        torch.cuda.synchronize()
+        outs[ns] = out.cpu().numpy()
+    for b in range(ocfg.batch):
+        T = lens[b]
+        oc = O.build_cache(k_rows[b][None, :, :T], v_rows[b][None, :, :T], _row_cfg(ocfg), norm_tokens=first[b])
+        assert_regions_equal(cache, oc, rows=[0], map_bh=lambda _b, h, b=b: (b, h))
+        want = O.decode(oc, q[b:b + 1])[0]
+        for ns, got in outs.items():
+            ok, err, bound = within_tol(got[b], want)
+            assert ok, (b, T, ns, err, bound)
+
+
+@pytest.mark.parametrize("key_norm", [False, True])
+def test_ragged_appends_and_decode(key_norm):
+    say(f"case: ragged appends and decode, key norm {key_norm}")
+    B, H, D, G = 3, 2, 128, 2
+    schedule = [[100, 0, 37], [1, 250, 64], [37, 5, 1], [0, 1, 200], [300, 33, 0]]
+    totals = [sum(c[b] for c in schedule) for b in range(B)]
+    ocfg = O.CacheConfig(B, H, H * G, D, 1200, 4, 40, "bf16", "hybrid", (3, 2), (2, 4), key_norm=key_norm)
+    rng = np.random.default_rng(500 + key_norm)
+    k_rows = [outlier_keys(rng, (1, H, totals[b], D), "bf16")[0] for b in range(B)]
+    v_rows = [workloads.random_raw16(rng, (H, totals[b], D), "bf16") for b in range(B)]
+    q = workloads.random_raw16(rng, (B, H * G, D), "bf16")
+    cache = kvq.KVCache(lib_cfg(kvq, ocfg), device=DEV)
+    lens, first = [0] * B, [None] * B
+    for step, n_new in enumerate(schedule):
+        n_max = max(n_new)
+        ck = [k_rows[b][:, lens[b]:lens[b] + n_new[b]] for b in range(B)]
+        cv = [v_rows[b][:, lens[b]:lens[b] + n_new[b]] for b in range(B)]
+        kin, vin = _ragged_input(ck, cv, n_max, H, D)
+        kvq.append_ragged(cache, lens, n_new, to_dev(kin), to_dev(vin))
+        for b in range(B):
+            if first[b] is None and n_new[b] > 0:
+                first[b] = n_new[b]
+            lens[b] += n_new[b]
+        if step in (2, 4):
+            _check_ragged(cache, ocfg, k_rows, v_rows, lens, first, q, splits=(1, 5))
+            say(f"    after call {step}: lengths {lens}, regions and decode match")
+    kvq.cache_check(cache)
+
+
+def test_ragged_serving_steps():
+    # rows prefilled to different lengths, then one token per row per step: the rows flush
+    # their 32-token blocks at different steps
+    say("case: ragged serving steps")
+    B, H, D, G = 4, 2, 64, 2
+    pre = [90, 300, 150, 33]
+    steps = 40
+    ocfg = O.CacheConfig(B, H, H * G, D, 400, 3, 32, "fp16", "asym", (2, 4), (3, 2))
+    rng = np.random.default_rng(510)
+    k_rows = [workloads.random_raw16(rng, (H, pre[b] + steps, D), "fp16", 2.0) for b in range(B)]
+    v_rows = [workloads.random_raw16(rng, (H, pre[b] + steps, D), "fp16") for b in range(B)]
+    cache = kvq.KVCache(lib_cfg(kvq, ocfg), device=DEV)
+    lens = [0] * B
+    kin, vin = _ragged_input([k[:, :p] for k, p in zip(k_rows, pre)], [v[:, :p] for v, p in zip(v_rows, pre)],
+                             max(pre), H, D)
+    kvq.append_ragged(cache, lens, pre, to_dev(kin), to_dev(vin))
+    lens = list(pre)
+    first = list(pre)
+    for s_ in range(steps):
+        ck = [k_rows[b][:, lens[b]:lens[b] + 1] for b in range(B)]
+        cv = [v_rows[b][:, lens[b]:lens[b] + 1] for b in range(B)]
+        kin, vin = _ragged_input(ck, cv, 1, H, D)
+        kvq.append_ragged(cache, lens, [1] * B, to_dev(kin), to_dev(vin))
+        lens = [n + 1 for n in lens]
+        if s_ % 8 == 7:
+            q = workloads.random_raw16(rng, (B, H * G, D), "fp16")
+            _check_ragged(cache, ocfg, k_rows, v_rows, lens, first, q, splits=(3,))
+            say(f"    step {s_}: lengths {lens} match")
+
+
+def test_ragged_rejects():
+    ocfg = O.CacheConfig(2, 1, 1, 64, 100, 2, 8, "bf16", "asym", (2,), (2,))
+    cache = kvq.KVCache(lib_cfg(kvq, ocfg), device=DEV)
+    k = torch.zeros((2, 1, 4, 64), dtype=torch.int16, device=DEV)
+    with pytest.raises(kvq.KvqError) as e:  # n_new above the input's slots
+        kvq.append_ragged(cache, [0, 0], [5, 1], k, k)
+    assert e.value.status == -1
+    with pytest.raises(kvq.KvqError) as e:  # past the capacity
+        kvq.append_ragged(cache, [98, 0], [4, 1], k, k)
+    assert e.value.status == -3
+    kvq.append_ragged(cache, [0, 0], [4, 0], k, k)
+    q = torch.zeros((2, 1, 64), dtype=torch.int16, device=DEV)
+    out = torch.zeros((2, 1, 64), dtype=torch.float32, device=DEV)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(kvq.KvqError) as e:  # row 1 is empty
+        kvq.decode_ragged(cache, [4, 0], q, out, 1, ws)
+    assert e.value.status == -1
+    big = O.CacheConfig(65, 1, 1, 64, 100, 2, 8, "bf16", "asym", (2,), (2,))
+    cache65 = kvq.KVCache(lib_cfg(kvq, big), device=DEV)
+    k65 = torch.zeros((65, 1, 1, 64), dtype=torch.int16, device=DEV)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.append_ragged(cache65, [0] * 65, [1] * 65, k65, k65)
+    assert e.value.status == -5
