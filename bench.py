@@ -182,7 +182,8 @@ def other_configs():
     layer, of the 128k-token context and of the 32k-token workload with per-channel key
     normalization (caches rotated so their reads come from HBM, launches back to back behind
     a spin kernel, HIP events on the launch stream), decode + merge of one and of four query
-    tokens per row on the multi-head 7B-shaped layer, and the ingest rate of the 16 x
+    tokens per row on the multi-head 7B-shaped layer, a ragged serving step (rows of 32767,
+    28000, 20000 and 12000 tokens; host loop, append + decode + merge), and the ingest rate of the 16 x
     4096-token prefill (calibration, allocation, then one append of every token), with and
     without key normalization."""
     import torch
@@ -268,6 +269,47 @@ def other_configs():
         multi[f"q{Q}_frac_of_8tbs"] = nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS
     res["mha7b_t8k_multi_token"] = multi
     del caches, qm
+    torch.cuda.empty_cache()
+    # ragged serving step on the 32k-token workload: the four rows hold 32767, 28000, 20000 and
+    # 12000 tokens; one step appends one token to every row and decodes one query per row
+    w = workloads.make("qwen8b_t32k")
+    s = w["spec"]
+    kb, vb = workload_bits(kvq, w)
+    cfg = kvq.Config.make(s.batch, s.n_kv, s.n_q, s.head_dim, s.tokens + 256, s.n_sink, s.n_recent, s.dtype,
+                          s.quant, kb, vb)
+    lens0 = [32767, 28000, 20000, 12000]
+    kd = torch.from_numpy(w["k"][:, :, :max(lens0)].view(np.int16)).to(dev)
+    vd = torch.from_numpy(w["v"][:, :, :max(lens0)].view(np.int16)).to(dev)
+    rcaches = []
+    for _ in range(3):
+        c = kvq.KVCache(cfg, device=dev)
+        kvq.append_ragged(c, [0] * s.batch, lens0, kd, vd)
+        rcaches.append(c)
+    k1 = torch.from_numpy(np.ascontiguousarray(w["k"][:, :, -1:]).view(np.int16)).to(dev)
+    v1 = torch.from_numpy(np.ascontiguousarray(w["v"][:, :, -1:]).view(np.int16)).to(dev)
+    q = torch.from_numpy(w["q"].view(np.int16)).to(dev)
+    out = torch.empty((s.batch, s.n_q, s.head_dim), dtype=torch.float32, device=dev)
+    ws = torch.zeros(kvq.decode_workspace_bytes(rcaches[0], s.n_splits), dtype=torch.uint8, device=dev)
+    lens = [list(lens0) for _ in rcaches]
+    n_steps = 60
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(20_000_000)
+    e0.record(stream)
+    for i in range(n_steps):
+        c, L = rcaches[i % 3], lens[i % 3]
+        kvq.append_ragged(c, L, [1] * s.batch, k1, v1, stream=stream)
+        for b in range(s.batch):
+            L[b] += 1
+        kvq.decode_ragged(c, L, q, out, s.n_splits, ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) * 1e3 / n_steps
+    tok = sum(lens0) + s.batch * n_steps // 2
+    res["qwen8b_t32k_ragged_step"] = {"row_lengths": lens0, "step_us": step_us,
+                                      "kv_tokens_heads_per_s": tok * s.n_kv / (step_us * 1e-6),
+                                      "step": "append_ragged 1 token per row + decode_ragged + merge"}
+    del rcaches, kd, vd
     torch.cuda.empty_cache()
     # prefill ingest
     w = workloads.make("prefill_t4k")
