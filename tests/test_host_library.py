@@ -150,3 +150,46 @@ def test_config_errors():
     cfg.group = 16
     with pytest.raises(kvq.KvqError):
         kvq.cache_bytes(cfg)
+
+
+def _fake_cache(cfg, length):
+    """A cache handle whose device pointer is never dereferenced: the calls below must fail
+    their host-side checks before anything reaches the device."""
+    h = kvq._Cache()
+    h.cfg = cfg
+    h.dev = 256  # non-null, aligned, never used
+    h.bytes = kvq.cache_bytes(cfg)
+    h.len = length
+    return h
+
+
+def test_multi_and_ragged_host_checks():
+    L = kvq.lib()
+    i32 = lambda v: (ctypes.c_int32 * len(v))(*v)  # noqa: E731
+    cfg = kvq.Config.make(2, 2, 4, 64, 100, 2, 8, "bf16", "asym", (2, 2), (2, 2))  # G = 2
+    h = _fake_cache(cfg, 50)
+    p = ctypes.c_void_p(4096)
+    # multi-token decode: G * Q = 2 * 3 > 4 rows
+    assert L.kvq_decode_multi(ctypes.byref(h), p, 3, p, 2, 0.0, p, 1 << 20, None) == -5
+    assert "<= 4" in kvq.last_error()
+    # more query tokens than cached tokens
+    h.len = 1
+    assert L.kvq_decode_multi(ctypes.byref(h), p, 2, p, 2, 0.0, p, 1 << 20, None) == -1
+    h.len = 50
+    # workspace sizes grow with the query tokens
+    assert L.kvq_decode_multi_workspace_bytes(ctypes.byref(h), 4, 2) > L.kvq_decode_workspace_bytes(ctypes.byref(h), 4)
+    assert L.kvq_decode_multi_workspace_bytes(ctypes.byref(h), 4, 5) == 0
+    # ragged append: n_new above the input slots, a row past the capacity, negative lengths
+    assert L.kvq_append_ragged(ctypes.byref(h), i32([0, 0]), i32([5, 1]), p, p, 4, None) == -1
+    assert L.kvq_append_ragged(ctypes.byref(h), i32([98, 0]), i32([4, 1]), p, p, 4, None) == -3
+    assert L.kvq_append_ragged(ctypes.byref(h), i32([-1, 0]), i32([1, 1]), p, p, 4, None) == -1
+    # nothing to append: a no-op that touches nothing
+    assert L.kvq_append_ragged(ctypes.byref(h), i32([3, 7]), i32([0, 0]), None, None, 0, None) == 0
+    # ragged decode: an empty row, a row past the capacity
+    assert L.kvq_decode_ragged(ctypes.byref(h), i32([4, 0]), p, p, 2, 0.0, p, 1 << 20, None) == -1
+    assert L.kvq_decode_ragged(ctypes.byref(h), i32([4, 101]), p, p, 2, 0.0, p, 1 << 20, None) == -1
+    # more than 64 rows
+    big = kvq.Config.make(65, 1, 1, 64, 100, 2, 8, "bf16", "asym", (2,), (2,))
+    hb = _fake_cache(big, 0)
+    assert L.kvq_append_ragged(ctypes.byref(hb), i32([0] * 65), i32([1] * 65), p, p, 1, None) == -5
+    assert L.kvq_decode_ragged(ctypes.byref(hb), i32([1] * 65), p, p, 2, 0.0, p, 1 << 20, None) == -5
