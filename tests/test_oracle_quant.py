@@ -294,3 +294,18 @@ def test_range_check_rejects_large_inputs():
     kr = k.astype(np.float16).view(np.uint16)
     with pytest.raises(ValueError):
         O.build_cache(kr, np.zeros_like(kr), cfg)
+
+
+def test_value_stream_order_is_a_permutation_one_window_per_register():
+    # the value-stream order of every width: the 32 (step, slot) reads cover positions 0..31
+    # once, and the two codes of a register (slots 2h, 2h + 1 of a step) are b bits apart in
+    # a way one shift and one mask can serve: their fields, read from one 32-bit window, sit
+    # in the low and high 16-bit halves at most 10 - b bits up
+    for b in range(2, 9):
+        pos = [O.value_stream_position(b, s, k) for s in range(8) for k in range(4)]
+        assert sorted(pos) == list(range(32)), b
+        for s in range(8):
+            for h in range(2):
+                lo, hi = O.value_stream_position(b, s, 2 * h), O.value_stream_position(b, s, 2 * h + 1)
+                gap = b * (hi - lo) - 16  # high field offset minus low field offset within the window
+                assert abs(gap) <= 10 - b, (b, s, h, lo, hi)
