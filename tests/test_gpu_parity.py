@@ -487,6 +487,28 @@ def test_multi_token_decode(G, Q, D, T, dtype):
             assert np.array_equal(got[:, 0], ref)
 
 
+def test_multi_token_decode_key_norm():
+    # the folded key norms apply to every (query token, head) row
+    say("case: multi-token decode with key normalization, G=1 Q=4")
+    rng = np.random.default_rng(460)
+    T, D = 900, 128
+    ocfg = O.CacheConfig(2, 2, 2, D, T, 4, 40, "bf16", "hybrid", (3, 2), (2, 4), key_norm=True)
+    k = outlier_keys(rng, (2, 2, T, D), "bf16")
+    v = workloads.random_raw16(rng, (2, 2, T, D), "bf16")
+    q = workloads.random_raw16(rng, (2, 4, 2, D), "bf16")
+    oc = O.build_cache(k, v, ocfg, norm_tokens=300)
+    cache = gpu_cache(ocfg, k, v, chunks=[300, T - 300])
+    want = O.decode_multi(oc, q)
+    out = torch.empty((2, 4, 2, D), dtype=torch.float32, device=DEV)
+    ws = torch.zeros(kvq.decode_multi_workspace_bytes(cache, 6, 4), dtype=torch.uint8, device=DEV)
+    kvq.decode_multi(cache, to_dev(q), out, 6, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for i in range(4):
+        ok, err, bound = within_tol(got[:, i], want[:, i])
+        assert ok, (i, err, bound)
+
+
 def test_multi_token_decode_rejects():
     ocfg = O.CacheConfig(1, 2, 4, 64, 400, 2, 0, "bf16", "asym", (2, 2), (2, 2))
     rng = np.random.default_rng(450)
