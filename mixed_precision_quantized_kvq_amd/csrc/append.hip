@@ -88,7 +88,12 @@ __device__ __forceinline__ void pack_value_stream(const uint8_t (*codes)[36], in
 // i = (token tt of the block) * (D/32) + channel group g, thread D + c handles value channel c.
 // Value codes are staged in LDS and then written, one (decode lane, stream) per thread, in the
 // decode kernel's value order.
+// ASYM: the instantiation for asymmetric caches. The hybrid choice's float64 errors of both
+// variants need about twice the registers (166 against 78), so an asymmetric cache runs at
+// twice the occupancy without that code.
+template <bool ASYM>
 __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
+  const bool hybrid = !ASYM && p.hybrid != 0;
   __shared__ alignas(4) uint8_t vcodes[128][36];  // [channel][token of the block], rows padded to 36 bytes
   const int h = blockIdx.y, b = blockIdx.z;
   const RowAppend ra = row_append(p, b);
@@ -141,7 +146,7 @@ __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
     auto group = [&](auto bc) {
       constexpr int B = decltype(bc)::value;
       uint32_t w[B];
-      const GroupQ q = quantize_pack<B>(x, p.hybrid != 0, w);
+      const GroupQ q = quantize_pack<B>(x, hybrid, w);
       sym = q.sym;
       const uint32_t meta = (uint32_t)q.s_bits | ((uint32_t)q.z_bits << 16);
       if (is_key) {
@@ -186,7 +191,7 @@ __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
       default: group(std::integral_constant<int, 8>{}); break;
     }
   }
-  if (p.hybrid && bits != 16) {
+  if (hybrid && bits != 16) {
     // flag bit i of this block's key (value) words = group i of thread i (D + i)
     const unsigned long long m = __ballot(sym);
     if ((tid & 63) == 0) {
@@ -305,7 +310,10 @@ int launch_append_flush(const AppendPlan& p, void* stream) {
   }
   if (nblk <= 0) return (int)hipSuccess;
   dim3 grid(nblk, p.H, p.B);
-  hipLaunchKernelGGL(append_flush_kernel, grid, dim3(2 * p.D), 0, (hipStream_t)stream, p);
+  if (p.hybrid)
+    hipLaunchKernelGGL(append_flush_kernel<false>, grid, dim3(2 * p.D), 0, (hipStream_t)stream, p);
+  else
+    hipLaunchKernelGGL(append_flush_kernel<true>, grid, dim3(2 * p.D), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 
