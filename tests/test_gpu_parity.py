@@ -570,13 +570,14 @@ def _check_ragged(cache, ocfg, k_rows, v_rows, lens, first, q, splits):
             assert ok, (b, T, ns, err, bound)
 
 
-@pytest.mark.parametrize("key_norm", [False, True])
-def test_ragged_appends_and_decode(key_norm):
-    say(f"case: ragged appends and decode, key norm {key_norm}")
+@pytest.mark.parametrize("key_norm,kb,vb", [(False, (3, 2), (2, 4)), (True, (3, 2), (2, 4)),
+                                             (False, (5, 16), (8, 3))], ids=["plain", "key-norm", "wide"])
+def test_ragged_appends_and_decode(key_norm, kb, vb):
+    say(f"case: ragged appends and decode, key norm {key_norm}, K bits {kb}, V bits {vb}")
     B, H, D, G = 3, 2, 128, 2
     schedule = [[100, 0, 37], [1, 250, 64], [37, 5, 1], [0, 1, 200], [300, 33, 0]]
     totals = [sum(c[b] for c in schedule) for b in range(B)]
-    ocfg = O.CacheConfig(B, H, H * G, D, 1200, 4, 40, "bf16", "hybrid", (3, 2), (2, 4), key_norm=key_norm)
+    ocfg = O.CacheConfig(B, H, H * G, D, 1200, 4, 40, "bf16", "hybrid", kb, vb, key_norm=key_norm)
     rng = np.random.default_rng(500 + key_norm)
     k_rows = [outlier_keys(rng, (1, H, totals[b], D), "bf16")[0] for b in range(B)]
     v_rows = [workloads.random_raw16(rng, (H, totals[b], D), "bf16") for b in range(B)]
