@@ -18,7 +18,10 @@
  *     calibration slice and allocated by reverse waterfilling / greedy integer allocation
  *     (RateQuant, sections 3.1, 3.3, 3.4);
  *   - decode reads the packed codes with dequantization fused into q.K^T and P.V, split-K
- *     over tokens, merged by log-sum-exp (InnerQ, "Algorithm 1 ... decode phase").
+ *     over tokens, merged by log-sum-exp (InnerQ, "Algorithm 1 ... decode phase");
+ *   - optionally, per-channel key normalization folded into the query (InnerQ, technique
+ *     (iii)); several query tokens per row decoded causally at once; rows of different
+ *     lengths in one cache (ragged batches).
  *
  * Ownership: the caller allocates and frees every device buffer (cache blob, inputs,
  * outputs, workspace). The library never allocates or frees device memory and keeps no
