@@ -16,7 +16,8 @@ namespace {
 // Each workgroup adds its groups' float64 errors per width in a fixed order (a butterfly
 // within each wavefront, then the wavefronts in order) and writes one sum per width:
 // part[head][width][workgroup].
-__global__ __launch_bounds__(kCalibThreads) void calib_kernel(const CalibPlan p) {
+template <bool ASYM>
+__device__ __forceinline__ void calib_body(const CalibPlan& p) {
   __shared__ double wsum[kCalibThreads / 64][8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t gi = (int64_t)blockIdx.x * kCalibThreads + tid;
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(kCalibThreads) void calib_kernel(const CalibPlan p)
     if (out_of_range(v)) atomicOr(p.range_flag, 1u);
   }
   for (int bi = 0; bi < p.nb; ++bi) {
-    double e = live ? group_sse(v, choose_quant(v, p.b_lo + bi, p.hybrid != 0)) : 0.0;
+    double e = live ? group_sse(v, choose_quant(v, p.b_lo + bi, !ASYM && p.hybrid != 0)) : 0.0;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) e = e + __shfl_xor(e, o, 64);
     if (lane == 0) wsum[wave][bi] = e;
@@ -58,11 +59,22 @@ __global__ __launch_bounds__(kCalibThreads) void calib_kernel(const CalibPlan p)
   }
 }
 
+// Two kernels: the hybrid choice's registers (248 VGPRs) would keep the asymmetric one, which
+// fits 3 wavefronts per SIMD, at 2.
+__global__ __launch_bounds__(kCalibThreads) void calib_kernel(const CalibPlan p) { calib_body<false>(p); }
+__global__ __launch_bounds__(kCalibThreads) __attribute__((amdgpu_waves_per_eu(3))) void calib_kernel_asym(
+    const CalibPlan p) {
+  calib_body<true>(p);
+}
+
 }  // namespace
 
 int launch_calib(const CalibPlan& p, void* stream) {
   dim3 grid((unsigned)p.n_blocks, (unsigned)p.n_heads);
-  hipLaunchKernelGGL(calib_kernel, grid, dim3(kCalibThreads), 0, (hipStream_t)stream, p);
+  if (p.hybrid)
+    hipLaunchKernelGGL(calib_kernel, grid, dim3(kCalibThreads), 0, (hipStream_t)stream, p);
+  else
+    hipLaunchKernelGGL(calib_kernel_asym, grid, dim3(kCalibThreads), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 
