@@ -21,7 +21,8 @@
  *     over tokens, merged by log-sum-exp (InnerQ, "Algorithm 1 ... decode phase");
  *   - optionally, per-channel key normalization folded into the query (InnerQ, technique
  *     (iii)); several query tokens per row decoded causally at once; rows of different
- *     lengths in one cache (ragged batches).
+ *     lengths in one cache (ragged batches); a paged body (pages of 64 tokens placed by a
+ *     per-row page table) for serving engines that hand out cache memory page by page.
  *
  * Ownership: the caller allocates and frees every device buffer (cache blob, inputs,
  * outputs, workspace). The library never allocates or frees device memory and keeps no
@@ -47,7 +48,8 @@ typedef enum {
   KVQ_ERR_CAPACITY = -3,    /* append would exceed the cache capacity */
   KVQ_ERR_RANGE = -4,       /* a quantized input was non-finite or |x| > 2^14 */
   KVQ_ERR_UNSUPPORTED = -5, /* a configuration this build does not implement */
-  KVQ_ERR_DEVICE = -6       /* a HIP call failed; kvq_last_error() has HIP's message */
+  KVQ_ERR_DEVICE = -6,      /* a HIP call failed; kvq_last_error() has HIP's message */
+  KVQ_ERR_PAGE = -7         /* paged cache: an append reached a tile with no page mapped */
 } kvq_status;
 
 typedef enum { KVQ_F16 = 0, KVQ_BF16 = 1 } kvq_dtype;
@@ -81,14 +83,15 @@ typedef struct {
 } kvq_config;
 
 /* A cache handle: the caller's POD. `dev` is a device blob of `bytes` bytes laid out by
- * kvq_cache_init; `len` is the token count of every row. kvq_append changes `len`, so
- * calls on one cache must be serialized by the caller (same stream, or host order). */
+ * kvq_cache_init (n_pages = 0) or kvq_cache_init_paged (n_pages > 0); `len` is the token
+ * count of every row. kvq_append changes `len`, so calls on one cache must be serialized by
+ * the caller (same stream, or host order). */
 typedef struct {
   kvq_config cfg;
   void* dev;
   uint64_t bytes;
   int32_t len;
-  int32_t reserved;
+  int32_t n_pages;
 } kvq_cache;
 
 /* Blob bytes needed for `cfg` (0 if cfg is invalid; kvq_last_error() says why). */
@@ -99,6 +102,40 @@ size_t kvq_cache_bytes(const kvq_config* cfg);
  * kvq_cache_bytes(cfg) bytes and 256-byte aligned. */
 kvq_status kvq_cache_init(kvq_cache* cache, const kvq_config* cfg, void* dev_mem, size_t bytes,
                           void* stream);
+
+/* Paged caches. The quantized body (regions 0..4) of every row is cut into tiles of 64
+ * tokens (two 32-token groups of values); tile t of row b lives in page page[b][t] of a pool
+ * of n_pages pages that every row shares. Each KV head has its own pools (its pages differ in
+ * size with its bit widths) and one page index serves all heads of a row. Sink, ring and norm
+ * regions stay per (row, head). Bytes inside a page are laid out as in a contiguous cache's
+ * tile, so paged and contiguous caches hold the same codes and decode to the same outputs.
+ * The page table (int32 [batch][page_stride], page_stride = the tiles of a row holding
+ * `capacity` tokens) lives in the blob; kvq_cache_init_paged sets every entry to -1
+ * (unmapped). Mapping a tile to a page already in use by another (row, tile) is the caller's
+ * error; the library does not detect it. A flush into an unmapped tile writes nothing and sets
+ * a sticky flag that kvq_cache_check reports as KVQ_ERR_PAGE; decode reads of an unmapped tile
+ * stay inside the pools but return meaningless values. All other calls (append, ragged,
+ * multi-token, decode, step) take paged caches as they are.
+ * Motivation: a fixed bit budget per token and head is what lets serving engines hand out
+ * cache memory in fixed-size blocks (NOVA-KV page, "If this is right"); the page mechanics
+ * are this library's. */
+
+/* Blob bytes for a paged cache of n_pages pages (1 <= n_pages; every pool under 2 GiB);
+ * 0 on bad arguments. */
+size_t kvq_cache_bytes_paged(const kvq_config* cfg, int32_t n_pages);
+
+/* As kvq_cache_init, for a paged cache of n_pages pages; also writes the page table with
+ * every entry -1. Synchronous on `stream`. */
+kvq_status kvq_cache_init_paged(kvq_cache* cache, const kvq_config* cfg, int32_t n_pages, void* dev_mem,
+                                size_t bytes, void* stream);
+
+/* Map tiles first_tile .. first_tile + n_tiles - 1 of `row` to pages[0 .. n_tiles - 1]
+ * (host array; each entry in [0, n_pages), or -1 to unmap). Tile t holds body tokens
+ * 64t .. 64t + 63 of the row, i.e. tokens n_sink + 64t .. of the sequence; a row holding T
+ * tokens needs its first ceil(body(T) / 64) tiles mapped, body(T) as in the decode
+ * description. Copies synchronously on `stream` (host order with earlier work on it). */
+kvq_status kvq_cache_map_pages(const kvq_cache* cache, int32_t row, int32_t first_tile, int32_t n_tiles,
+                               const int32_t* pages, void* stream);
 
 /* Calibration + distortion fit (RateQuant sections 3.1, 3.4, 4.1, W.10).
  * x_dev: [n_heads][n_tokens][head_dim] 16-bit (dtype), one calibration slice per head.
@@ -210,12 +247,15 @@ kvq_status kvq_decode_step(kvq_cache* cache, const void* k_dev, const void* v_de
                            const void* q_dev, float* out_dev, int32_t n_splits, float scale,
                            void* workspace_dev, size_t ws_bytes, void* stream);
 
-/* Synchronize `stream`, read the sticky range flag; KVQ_ERR_RANGE if it is set. */
+/* Synchronize `stream`, read the sticky flags; KVQ_ERR_RANGE if an input was out of range,
+ * else KVQ_ERR_PAGE if a paged cache's append reached an unmapped tile. */
 kvq_status kvq_cache_check(const kvq_cache* cache, void* stream);
 
 /* Byte offset, from the blob start, of region `region` (0..9: key codes, key meta, value
  * codes, value meta, hybrid flags, sink keys, sink values, ring keys, ring values, key
- * norms) of (row, kv_head), and its size; returns 0 and sets *size = 0 on bad arguments. */
+ * norms) of (row, kv_head), and its size; returns 0 and sets *size = 0 on bad arguments.
+ * Contiguous caches only; a paged blob's region table (uint64 [batch][n_kv_heads][10] at
+ * byte 256 of the blob) names the pools and regions of a paged cache. */
 uint64_t kvq_region_offset(const kvq_config* cfg, int32_t row, int32_t kv_head, int32_t region,
                            uint64_t* size);
 

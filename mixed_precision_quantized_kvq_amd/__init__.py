@@ -36,13 +36,13 @@ REGIONS = ("key_codes", "key_meta", "value_codes", "value_meta", "flags", "sink_
            "sink_values", "ring_keys", "ring_values")
 
 STATUS = {0: "OK", -1: "ERR_ARG", -2: "ERR_BUDGET", -3: "ERR_CAPACITY", -4: "ERR_RANGE",
-          -5: "ERR_UNSUPPORTED", -6: "ERR_DEVICE"}
+          -5: "ERR_UNSUPPORTED", -6: "ERR_DEVICE", -7: "ERR_PAGE"}
 
 EXPORTS = ("kvq_cache_bytes", "kvq_cache_init", "kvq_calibrate_workspace_bytes",
            "kvq_calibrate_fit", "kvq_allocate_bits", "kvq_append", "kvq_decode_workspace_bytes",
            "kvq_decode_attention", "kvq_decode_splitk", "kvq_decode_merge", "kvq_decode_step",
            "kvq_decode_multi_workspace_bytes", "kvq_decode_multi", "kvq_append_ragged", "kvq_decode_ragged",
-           "kvq_cache_check",
+           "kvq_cache_check", "kvq_cache_bytes_paged", "kvq_cache_init_paged", "kvq_cache_map_pages",
            "kvq_region_offset", "kvq_last_error")
 
 
@@ -79,7 +79,7 @@ class Config(ctypes.Structure):
 
 class _Cache(ctypes.Structure):
     _fields_ = [("cfg", Config), ("dev", ctypes.c_void_p), ("bytes", ctypes.c_uint64),
-                ("len", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("len", ctypes.c_int32), ("n_pages", ctypes.c_int32)]
 
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -106,6 +106,9 @@ def lib():
         sig = {
             "kvq_cache_bytes": (SZ, [CP]),
             "kvq_cache_init": (I32, [KP, CP, P, SZ, P]),
+            "kvq_cache_bytes_paged": (SZ, [CP, I32]),
+            "kvq_cache_init_paged": (I32, [KP, CP, I32, P, SZ, P]),
+            "kvq_cache_map_pages": (I32, [KP, I32, I32, I32, P, P]),
             "kvq_calibrate_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
             "kvq_calibrate_fit": (I32, [P, I32, I32, I32, I32, I32, I32, I32, I32, P, SZ, D, D, D, P]),
             "kvq_allocate_bits": (I32, [I32, D, D, D, I32, I32, I32, U32,
@@ -188,16 +191,33 @@ def allocate_bits(alpha, beta, w, total_bits: int, b_lo: int, b_hi: int, cap: bo
 class KVCache:
     """A cache blob in a torch uint8 device tensor plus the C handle."""
 
-    def __init__(self, cfg: Config, device="cuda", stream=None, blob=None):
+    def __init__(self, cfg: Config, device="cuda", stream=None, blob=None, n_pages: int = 0):
         import torch
         self.cfg = cfg
-        nbytes = cache_bytes(cfg)
+        self.n_pages = n_pages
+        nbytes = cache_bytes(cfg) if n_pages == 0 else cache_bytes_paged(cfg, n_pages)
         self.blob = blob if blob is not None else torch.empty(nbytes, dtype=torch.uint8, device=device)
         if self.blob.numel() < nbytes:
             raise ValueError("blob tensor too small")
         self.handle = _Cache()
-        _check(lib().kvq_cache_init(ctypes.byref(self.handle), ctypes.byref(cfg), _dptr(self.blob),
-                                    nbytes, _stream(stream)))
+        if n_pages == 0:
+            _check(lib().kvq_cache_init(ctypes.byref(self.handle), ctypes.byref(cfg), _dptr(self.blob),
+                                        nbytes, _stream(stream)))
+        else:
+            _check(lib().kvq_cache_init_paged(ctypes.byref(self.handle), ctypes.byref(cfg), int(n_pages),
+                                              _dptr(self.blob), nbytes, _stream(stream)))
+
+    def map_pages(self, row: int, first_tile: int, pages, stream=None):
+        """Map tiles first_tile.. of `row` to the host int list/array `pages`."""
+        arr = _i32_array(pages)
+        _check(lib().kvq_cache_map_pages(ctypes.byref(self.handle), int(row), int(first_tile), len(pages),
+                                         arr, _stream(stream)))
+
+    def region_table(self):
+        """The blob's region table as a host int64 array [batch][n_kv_heads][10]."""
+        c = self.cfg
+        n = c.batch * c.n_kv_heads * 10
+        return self.blob[256:256 + 8 * n].cpu().numpy().view("<u8").reshape(c.batch, c.n_kv_heads, 10)
 
     @property
     def len(self) -> int:
@@ -210,6 +230,18 @@ class KVCache:
 
 def cache_init(cfg: Config, device="cuda", stream=None) -> KVCache:
     return KVCache(cfg, device, stream)
+
+
+def cache_bytes_paged(cfg: Config, n_pages: int) -> int:
+    n = lib().kvq_cache_bytes_paged(ctypes.byref(cfg), int(n_pages))
+    if n == 0:
+        raise KvqError(-1, last_error())
+    return int(n)
+
+
+def cache_init_paged(cfg: Config, n_pages: int, device="cuda", stream=None) -> KVCache:
+    """A paged cache: body tiles of 64 tokens placed through a page table (all unmapped)."""
+    return KVCache(cfg, device, stream, n_pages=n_pages)
 
 
 def append(cache: KVCache, k, v, stream=None):

@@ -109,13 +109,24 @@ __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
   const int bits = is_key ? p.k_bits[h] : p.v_bits[h];
   const int vbits = p.v_bits[h];
   const int tile = j >> 1, jj = j & 1;
+  // paged caches: the tile's page in this head's pools; an unmapped tile writes nothing and
+  // sets flag bit 1 (uniform over the workgroup, so no barrier is skipped by part of it)
+  int ptile = tile;
+  if (p.pages) {
+    ptile = p.pages[(size_t)b * p.page_stride + tile];
+    if (ptile < 0 || ptile >= p.n_pages) {
+      if (tid == 0) atomicOr(p.range_flag, 2u);
+      return;
+    }
+  }
+  const int pj = 2 * ptile + jj;  // the block's slot in the body region or pools
   bool sym = false;
   if (bits == 16) {
     // unquantized head: the block's rows are copied
     if (is_key) {
       const int tt = tid / Gd, g = tid % Gd;
       const uint16_t* src = token_row(p, ra.len0, p.blob + off[RK], kin, p.n_sink + j * kGroup + tt) + g * kGroup;
-      uint4* dst = reinterpret_cast<uint4*>(p.blob + off[KC]) + ((size_t)(j * kGroup + tt) * D + g * kGroup) / 8;
+      uint4* dst = reinterpret_cast<uint4*>(p.blob + off[KC]) + ((size_t)(pj * kGroup + tt) * D + g * kGroup) / 8;
 #pragma unroll
       for (int v = 0; v < 4; ++v) dst[v] = reinterpret_cast<const uint4*>(src)[v];
     } else {
@@ -123,7 +134,7 @@ __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
       uint16_t* dst = reinterpret_cast<uint16_t*>(p.blob + off[VC]);
 #pragma unroll
       for (int k = 0; k < 32; ++k)
-        dst[(size_t)(j * kGroup + k) * D + c] = token_row(p, ra.len0, p.blob + off[RV], vin, p.n_sink + j * kGroup + k)[c];
+        dst[(size_t)(pj * kGroup + k) * D + c] = token_row(p, ra.len0, p.blob + off[RV], vin, p.n_sink + j * kGroup + k)[c];
     }
   } else {
     float x[32];
@@ -153,14 +164,14 @@ __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
         const int tt = tid / Gd, g = tid % Gd;
         const int W = Gd * B;  // words per token
         const int t_in_tile = jj * kGroup + tt;
-        uint32_t* kc = reinterpret_cast<uint32_t*>(p.blob + off[KC]) + (size_t)tile * kTile * W;
+        uint32_t* kc = reinterpret_cast<uint32_t*>(p.blob + off[KC]) + (size_t)ptile * kTile * W;
 #pragma unroll
         for (int k = 0; k < B; ++k) {
           const int wi = g * B + k;
           const int qc = wi >> 2, nq = min(4, W - 4 * qc);
           kc[256 * qc + t_in_tile * nq + (wi - 4 * qc)] = w[k];
         }
-        reinterpret_cast<uint32_t*>(p.blob + off[KM])[(size_t)(j * kGroup + tt) * Gd + g] = meta;
+        reinterpret_cast<uint32_t*>(p.blob + off[KM])[(size_t)(pj * kGroup + tt) * Gd + g] = meta;
       } else {
         const int c = tid - D;
         // codes of the 32 tokens, four to a word (the rows of vcodes are 36 bytes apart)
@@ -177,7 +188,7 @@ __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
           reinterpret_cast<uint32_t*>(vcodes[c])[m] = v4;
         }
         // (s|z) of channel c = 16 nb + n for this block, at [tile][block][n][nb]
-        reinterpret_cast<uint32_t*>(p.blob + off[VM])[(size_t)tile * 2 * D + jj * D + (c & 15) * (D / 16) + (c >> 4)] =
+        reinterpret_cast<uint32_t*>(p.blob + off[VM])[(size_t)ptile * 2 * D + jj * D + (c & 15) * (D / 16) + (c >> 4)] =
             meta;
       }
     };
@@ -195,7 +206,7 @@ __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
     // flag bit i of this block's key (value) words = group i of thread i (D + i)
     const unsigned long long m = __ballot(sym);
     if ((tid & 63) == 0) {
-      uint32_t* fl = reinterpret_cast<uint32_t*>(p.blob + off[FL]) + (size_t)j * 2 * Gd;
+      uint32_t* fl = reinterpret_cast<uint32_t*>(p.blob + off[FL]) + (size_t)pj * 2 * Gd;
       const int wbase = (is_key ? 0 : Gd) + ((is_key ? tid : tid - D) >> 5);
       fl[wbase] = (uint32_t)m;
       fl[wbase + 1] = (uint32_t)(m >> 32);
@@ -209,7 +220,7 @@ __global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
     const int lane_local = x / nv, vg = x % nv;
     const int jp = lane_local >> 4, n = lane_local & 15;
     const int lane = (2 * jj + jp) * 16 + n;
-    uint32_t* dst = reinterpret_cast<uint32_t*>(p.blob + off[VC]) + (size_t)tile * 2 * D * vbits +
+    uint32_t* dst = reinterpret_cast<uint32_t*>(p.blob + off[VC]) + (size_t)ptile * 2 * D * vbits +
                     ((size_t)lane * nv + vg) * vbits;
     switch (vbits) {
       case 2: pack_value_stream<2>(vcodes, vg, jp, n, dst); break;

@@ -248,17 +248,34 @@ struct VTile {
 // fixed byte offset (a VGPR computed once) + the tile's byte offset (an SGPR). No address
 // register is rewritten per tile, so none can alias the destination of a load still in
 // flight, and an offset past the region returns zeros instead of faulting.
+// Paged caches also carry the row's page table: tile t is read from page pages[t] of the
+// head's pools.
 struct BodySrc {
   __amdgpu_buffer_rsrc_t kc, km, vc, vm;
+  const int32_t* pages;  // null for contiguous caches
+  int n_pages;
 };
+// The page (paged caches) or region slot (contiguous caches) of body tile `tile`. An unmapped
+// entry is clamped into the pools, so reading it stays in bounds (its values are meaningless).
+__device__ __forceinline__ int body_page(const int32_t* pages, int n_pages, int tile) {
+  if (!pages) return tile;
+  const int pg = pages[tile];
+  return pg < 0 ? 0 : (pg >= n_pages ? n_pages - 1 : pg);
+}
+// Slot of body token u (16-bit rows) in the region or pools.
+__device__ __forceinline__ int body_row(const int32_t* pages, int n_pages, int u) {
+  return body_page(pages, n_pages, u / kTile) * kTile + u % kTile;
+}
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t region_rsrc(const char* blob, const uint64_t* off, int r) {
   // 0x00020000: raw (untyped) buffer, 32-bit dwords
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(blob + off[r]), (short)0,
                                            (int)(uint32_t)(off[r + 1] - off[r]), 0x00020000);
 }
-__device__ __forceinline__ BodySrc body_src(const DecodePlan& p, const uint64_t* off) {
+// paged = false drops the page lookups at compile time (contiguous caches)
+__device__ __forceinline__ BodySrc body_src(const DecodePlan& p, const uint64_t* off, bool paged) {
   return BodySrc{region_rsrc(p.blob, off, KC), region_rsrc(p.blob, off, KM), region_rsrc(p.blob, off, VC),
-                 region_rsrc(p.blob, off, VM)};
+                 region_rsrc(p.blob, off, VM), paged && p.pages ? p.pages + (size_t)blockIdx.z * p.page_stride : nullptr,
+                 p.n_pages};
 }
 // Cache policy of the body loads: non-temporal (nt). Every packed byte is read once per
 // launch, and streaming it past the caches this way measured 7 % faster than the default
@@ -276,7 +293,8 @@ __device__ __forceinline__ void bload2(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 template <int D, int KB>
 __device__ __forceinline__ void load_k(KTile<D, KB>& t, const BodySrc& src, int tile, int lane) {
   constexpr int W = KTile<D, KB>::W;
-  const uint32_t soff = (uint32_t)tile * (kTile * W * 4);
+  const int pg = body_page(src.pages, src.n_pages, tile);
+  const uint32_t soff = (uint32_t)pg * (kTile * W * 4);
 #pragma unroll
   for (int q = 0; q < (W + 3) / 4; ++q) {
     const int nq = (W - 4 * q) < 4 ? (W - 4 * q) : 4;  // 4, or 2 for the last chunk
@@ -286,7 +304,7 @@ __device__ __forceinline__ void load_k(KTile<D, KB>& t, const BodySrc& src, int 
     else
       bload2(src.kc, voff, soff, &t.w[4 * q]);
   }
-  const uint32_t msoff = (uint32_t)tile * (kTile * (D / 32) * 4), mvoff = (uint32_t)lane * (D / 32) * 4;
+  const uint32_t msoff = (uint32_t)pg * (kTile * (D / 32) * 4), mvoff = (uint32_t)lane * (D / 32) * 4;
   if constexpr (D == 128)
     bload4(src.km, mvoff, msoff, t.m);
   else
@@ -300,7 +318,8 @@ __device__ __forceinline__ void load_k(KTile<D, KB>& t, const BodySrc& src, int 
 template <int D, int VB>
 __device__ __forceinline__ void load_v(VTile<D, VB>& t, const BodySrc& src, int tile, int lane) {
   constexpr int NB = D / 16, NW = (NB / 2) * VB;
-  const uint32_t soff = (uint32_t)tile * (2 * D * VB * 4), voff = (uint32_t)lane * NW * 4;
+  const int pg = body_page(src.pages, src.n_pages, tile);
+  const uint32_t soff = (uint32_t)pg * (2 * D * VB * 4), voff = (uint32_t)lane * NW * 4;
   if constexpr (NW % 4 == 0) {
 #pragma unroll
     for (int x = 0; x < NW; x += 4) bload4(src.vc, voff + 4 * x, soff, &t.w[x]);
@@ -308,7 +327,7 @@ __device__ __forceinline__ void load_v(VTile<D, VB>& t, const BodySrc& src, int 
 #pragma unroll
     for (int x = 0; x < NW; x += 2) bload2(src.vc, voff + 4 * x, soff, &t.w[x]);
   }
-  const uint32_t msoff = (uint32_t)tile * (2 * D * 4);
+  const uint32_t msoff = (uint32_t)pg * (2 * D * 4);
   const uint32_t mvoff = (uint32_t)((lane >> 5) * D + (lane & 15) * NB) * 4;
 #pragma unroll
   for (int x = 0; x < NB; x += 4) bload4(src.vm, mvoff + 4 * x, msoff, &t.m[x]);
@@ -647,11 +666,11 @@ __device__ __forceinline__ void win_compute(Smem<D>& sm, const DecodePlan& p, co
 
 // Quantized keys and values, both widths fixed: the loads of the next tile are issued before
 // the current tile is computed.
-template <int D, int KB, int VB, class Prologue, class WindowIssue, class Window>
+template <int D, int KB, int VB, bool PAGED, class Prologue, class WindowIssue, class Window>
 __device__ __forceinline__ void body_loop(Smem<D>& sm, const DecodePlan& p, const uint64_t* off, int body, int t0,
                                           int t1, int lane, int wave, Prologue prologue, WindowIssue window_issue,
                                           Window window, WaveState<D>& st) {
-  const BodySrc src = body_src(p, off);
+  const BodySrc src = body_src(p, off, PAGED);
   int tile = t0 + wave;
   const bool any = tile < t1;
   // two register buffers: the next tile is in flight while this one is computed
@@ -717,11 +736,12 @@ __device__ __forceinline__ void mixed_body_loop(Smem<D>& sm, const DecodePlan& p
   const bool bf16 = p.dtype == KVQ_BF16;
   const uint16_t* kr = reinterpret_cast<const uint16_t*>(p.blob + off[KC]);
   const uint16_t* vr = reinterpret_cast<const uint16_t*>(p.blob + off[VC]);
-  const BodySrc src = body_src(p, off);
+  const BodySrc src = body_src(p, off, true);
   for (int tile = t0 + wave; tile < t1; tile += kWaves) {
     const int tok = tile * kTile + lane;
     const bool valid = tok < body;
     const int n_valid = min(kTile, body - tile * kTile);
+    const int pg = body_page(src.pages, src.n_pages, tile);
     float sc[kMaxG];
     switch (kb) {
       case 2: key_tile_q<D, 2>(sm, src, tile, lane, kscale, sc); break;
@@ -733,7 +753,7 @@ __device__ __forceinline__ void mixed_body_loop(Smem<D>& sm, const DecodePlan& p
       case 8: key_tile_q<D, 8>(sm, src, tile, lane, kscale, sc); break;
       default:
         uint4 x[D / 8];
-        const uint4* r4 = reinterpret_cast<const uint4*>(kr + (size_t)(valid ? tok : tile * kTile) * D);
+        const uint4* r4 = reinterpret_cast<const uint4*>(kr + ((size_t)pg * kTile + (valid ? lane : 0)) * D);
 #pragma unroll
         for (int v = 0; v < D / 8; ++v) x[v] = r4[v];
         issue_barrier();
@@ -754,7 +774,7 @@ __device__ __forceinline__ void mixed_body_loop(Smem<D>& sm, const DecodePlan& p
       case 8: value_tile_q<D, 8>(sm, wave, src, tile, lane, valid, sc, nblk, st); break;
       default: {
         uint32_t rows[2][32];
-        load_v16<D>(rows, lane, n_valid, [&](int k) { return vr + (size_t)(tile * kTile + k) * D; });
+        load_v16<D>(rows, lane, n_valid, [&](int k) { return vr + ((size_t)pg * kTile + k) * D; });
         softmax_rows16<D>(sm, wave, lane, valid, sc, st, lane & 31, 1.0f, bf16);
         if (bf16)
           value_phase_16<D, true>(sm, wave, lane, n_valid, rows, st);
@@ -784,7 +804,9 @@ __device__ __forceinline__ void rows16_loop(Smem<D>& sm, const DecodePlan& p, in
 // WIDE: the instantiation that also holds the path for 5- to 8-bit codes and heads with one
 // 16-bit side. Its register pressure would make the compiler spill in the fast loops, so
 // caches whose heads all take the fast path (or are 16-bit on both sides) use the other one.
-template <int D, bool WIDE>
+// PAGED: the instantiation for paged caches (the page lookups cost the contiguous fast loop
+// registers and time, so contiguous caches use one without them; WIDE always looks them up).
+template <int D, bool WIDE, bool PAGED>
 // two wavefronts per SIMD (two workgroups per CU): the register budget is 256
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_kernel(const DecodePlan p) {
   __shared__ Smem<D> sm;
@@ -924,12 +946,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     window(wt);
     const uint16_t* kr = reinterpret_cast<const uint16_t*>(p.blob + off[KC]);
     const uint16_t* vr = reinterpret_cast<const uint16_t*>(p.blob + off[VC]);
+    const int32_t* pages = p.pages ? p.pages + (size_t)b * p.page_stride : nullptr;
     rows16_loop<D>(sm, p, t0 * kTile, min(body, t1 * kTile), lane, wave, st,
-                   [&](int u) { return kr + (size_t)u * D; }, [&](int u) { return vr + (size_t)u * D; });
+                   [&](int u) { return kr + (size_t)body_row(pages, p.n_pages, u) * D; },
+                   [&](int u) { return vr + (size_t)body_row(pages, p.n_pages, u) * D; });
   } else if (kb <= 4 && vb <= 4) {
     // the widths the allocator hands out in {2,3,4}: prefetching loop per combination
 #define KVQ_BODY(KB_, VB_) \
-  case KB_ * 16 + VB_: body_loop<D, KB_, VB_>(sm, p, off, body, t0, t1, lane, wave, prologue, window_issue, window, st); break;
+  case KB_ * 16 + VB_: body_loop<D, KB_, VB_, PAGED>(sm, p, off, body, t0, t1, lane, wave, prologue, window_issue, window, st); break;
     switch (kb * 16 + vb) {
       KVQ_BODY(2, 2) KVQ_BODY(2, 3) KVQ_BODY(2, 4) KVQ_BODY(3, 2) KVQ_BODY(3, 3) KVQ_BODY(3, 4)
       KVQ_BODY(4, 2) KVQ_BODY(4, 3) KVQ_BODY(4, 4)
@@ -1093,16 +1117,21 @@ int launch_decode_splitk(const DecodePlan& p, void* stream) {
     const int kb = p.k_bits[h], vb = p.v_bits[h];
     wide |= !(kb <= 4 && vb <= 4) && !(kb == 16 && vb == 16);
   }
+  const bool paged = p.pages != nullptr;
   if (p.D == 128) {
     if (wide)
-      hipLaunchKernelGGL((decode_kernel<128, true>), grid, dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((decode_kernel<128, true, true>), grid, dim3(kThreads), 0, s, p);
+    else if (paged)
+      hipLaunchKernelGGL((decode_kernel<128, false, true>), grid, dim3(kThreads), 0, s, p);
     else
-      hipLaunchKernelGGL((decode_kernel<128, false>), grid, dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((decode_kernel<128, false, false>), grid, dim3(kThreads), 0, s, p);
   } else {
     if (wide)
-      hipLaunchKernelGGL((decode_kernel<64, true>), grid, dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((decode_kernel<64, true, true>), grid, dim3(kThreads), 0, s, p);
+    else if (paged)
+      hipLaunchKernelGGL((decode_kernel<64, false, true>), grid, dim3(kThreads), 0, s, p);
     else
-      hipLaunchKernelGGL((decode_kernel<64, false>), grid, dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((decode_kernel<64, false, false>), grid, dim3(kThreads), 0, s, p);
   }
   return (int)hipGetLastError();
 }

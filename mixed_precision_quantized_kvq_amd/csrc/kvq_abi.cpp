@@ -33,13 +33,25 @@ kvq_status check_cache(const kvq_cache* c) {
   if (st != KVQ_OK) return st;
   if (!c->dev) return fail(KVQ_ERR_ARG, "cache has no device memory");
   if (c->len < 0 || c->len > c->cfg.capacity) return fail(KVQ_ERR_ARG, "cache len out of range");
-  if (c->bytes < plan_layout(c->cfg, nullptr)) return fail(KVQ_ERR_ARG, "cache blob too small");
+  if (c->n_pages < 0) return fail(KVQ_ERR_ARG, "negative n_pages");
+  if (c->bytes < plan_layout(c->cfg, nullptr, c->n_pages)) return fail(KVQ_ERR_ARG, "cache blob too small");
   return KVQ_OK;
 }
 
 const uint64_t* table_ptr(const kvq_cache* c) {
   return reinterpret_cast<const uint64_t*>(static_cast<const char*>(c->dev) + kHeaderBytes);
 }
+// The page table of a paged cache into a launch plan (null for contiguous caches).
+template <class Plan>
+void set_pages(const kvq_cache* c, Plan& p) {
+  if (c->n_pages <= 0) return;
+  uint64_t pt_off = 0;
+  plan_layout(c->cfg, nullptr, c->n_pages, &pt_off);
+  p.pages = reinterpret_cast<const int32_t*>(static_cast<const char*>(c->dev) + pt_off);
+  p.page_stride = page_stride(c->cfg);
+  p.n_pages = c->n_pages;
+}
+
 uint32_t* flag_ptr(const kvq_cache* c) {
   return reinterpret_cast<uint32_t*>(static_cast<char*>(c->dev) + offsetof(BlobHeader, range_flag));
 }
@@ -72,16 +84,34 @@ uint64_t kvq_region_offset(const kvq_config* cfg, int32_t row, int32_t kv_head, 
   return off[((size_t)row * cfg->n_kv_heads + kv_head) * kRegions + region];
 }
 
-kvq_status kvq_cache_init(kvq_cache* cache, const kvq_config* cfg, void* dev_mem, size_t bytes,
-                          void* stream) {
+}  // extern "C"
+
+namespace {
+
+kvq_status check_pages(const kvq_config* cfg, int32_t n_pages) {
+  if (n_pages < 1) return fail(KVQ_ERR_ARG, "n_pages must be >= 1");
+  for (int h = 0; h < cfg->n_kv_heads; ++h) {
+    uint64_t sz[kRegions];
+    region_sizes(*cfg, h, sz, n_pages);
+    for (int r = KC; r <= FL; ++r)
+      if (sz[r] > 0x7FFFFFFFull) return fail(KVQ_ERR_ARG, "a page pool would exceed 2 GiB");
+  }
+  return KVQ_OK;
+}
+
+// Header, region table and (paged caches) a page table of -1 entries, copied synchronously.
+kvq_status init_blob(kvq_cache* cache, const kvq_config* cfg, int32_t n_pages, void* dev_mem, size_t bytes,
+                     void* stream) {
   if (!cache) return fail(KVQ_ERR_ARG, "cache is NULL");
   kvq_status st = check_config(cfg);
   if (st != KVQ_OK) return st;
+  if (n_pages > 0 && (st = check_pages(cfg, n_pages)) != KVQ_OK) return st;
   if (!dev_mem || !aligned(dev_mem, 256)) return fail(KVQ_ERR_ARG, "dev_mem must be 256-byte aligned");
   const size_t n_off = (size_t)cfg->batch * cfg->n_kv_heads * kRegions;
   std::vector<uint64_t> host(kHeaderBytes / 8 + n_off, 0);
-  const uint64_t total = plan_layout(*cfg, host.data() + kHeaderBytes / 8);
-  if (bytes < total) return fail(KVQ_ERR_ARG, "dev_mem smaller than kvq_cache_bytes()");
+  uint64_t pt_off = 0;
+  const uint64_t total = plan_layout(*cfg, host.data() + kHeaderBytes / 8, n_pages, &pt_off);
+  if (bytes < total) return fail(KVQ_ERR_ARG, "dev_mem smaller than the cache's size");
   BlobHeader hdr{};
   hdr.magic = kMagic;
   hdr.version = kVersion;
@@ -93,16 +123,66 @@ kvq_status kvq_cache_init(kvq_cache* cache, const kvq_config* cfg, void* dev_mem
   hdr.capacity = cfg->capacity;
   hdr.table_offset = kHeaderBytes;
   hdr.total_bytes = total;
+  hdr.page_table_offset = pt_off;
+  hdr.n_pages = n_pages;
+  hdr.page_stride = n_pages > 0 ? page_stride(*cfg) : 0;
   std::memcpy(host.data(), &hdr, sizeof(hdr));
   hipError_t e = hipMemcpyAsync(dev_mem, host.data(), host.size() * 8, hipMemcpyHostToDevice,
                                 as_stream(stream));
+  std::vector<int32_t> table(n_pages > 0 ? (size_t)cfg->batch * hdr.page_stride : 0, -1);
+  if (e == hipSuccess && !table.empty())
+    e = hipMemcpyAsync(static_cast<char*>(dev_mem) + pt_off, table.data(), table.size() * 4,
+                       hipMemcpyHostToDevice, as_stream(stream));
   if (e == hipSuccess) e = hipStreamSynchronize(as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "cache init copy");
   cache->cfg = *cfg;
   cache->dev = dev_mem;
   cache->bytes = bytes;
   cache->len = 0;
-  cache->reserved = 0;
+  cache->n_pages = n_pages;
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_cache_init(kvq_cache* cache, const kvq_config* cfg, void* dev_mem, size_t bytes,
+                          void* stream) {
+  return init_blob(cache, cfg, 0, dev_mem, bytes, stream);
+}
+
+size_t kvq_cache_bytes_paged(const kvq_config* cfg, int32_t n_pages) {
+  if (check_config(cfg) != KVQ_OK || check_pages(cfg, n_pages) != KVQ_OK) return 0;
+  return (size_t)plan_layout(*cfg, nullptr, n_pages);
+}
+
+kvq_status kvq_cache_init_paged(kvq_cache* cache, const kvq_config* cfg, int32_t n_pages, void* dev_mem,
+                                size_t bytes, void* stream) {
+  if (n_pages < 1) return fail(KVQ_ERR_ARG, "n_pages must be >= 1");
+  return init_blob(cache, cfg, n_pages, dev_mem, bytes, stream);
+}
+
+kvq_status kvq_cache_map_pages(const kvq_cache* cache, int32_t row, int32_t first_tile, int32_t n_tiles,
+                               const int32_t* pages, void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (cache->n_pages <= 0) return fail(KVQ_ERR_ARG, "not a paged cache");
+  const int stride = page_stride(cache->cfg);
+  if (row < 0 || row >= cache->cfg.batch) return fail(KVQ_ERR_ARG, "row out of range");
+  if (n_tiles < 0 || first_tile < 0 || (int64_t)first_tile + n_tiles > stride)
+    return fail(KVQ_ERR_ARG, "tiles out of range (a row has " + std::to_string(stride) + ")");
+  if (n_tiles == 0) return KVQ_OK;
+  if (!pages) return fail(KVQ_ERR_ARG, "pages is NULL");
+  for (int i = 0; i < n_tiles; ++i)
+    if (pages[i] < -1 || pages[i] >= cache->n_pages)
+      return fail(KVQ_ERR_ARG, "page index out of range at " + std::to_string(i));
+  uint64_t pt_off = 0;
+  plan_layout(cache->cfg, nullptr, cache->n_pages, &pt_off);
+  char* dst = static_cast<char*>(cache->dev) + pt_off + ((size_t)row * stride + first_tile) * 4;
+  hipError_t e = hipMemcpyAsync(dst, pages, (size_t)n_tiles * 4, hipMemcpyHostToDevice, as_stream(stream));
+  if (e == hipSuccess) e = hipStreamSynchronize(as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "page table copy");
   return KVQ_OK;
 }
 
@@ -113,7 +193,8 @@ kvq_status kvq_cache_check(const kvq_cache* cache, void* stream) {
   hipError_t e = hipMemcpyAsync(&flag, flag_ptr(cache), 4, hipMemcpyDeviceToHost, as_stream(stream));
   if (e == hipSuccess) e = hipStreamSynchronize(as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "cache check");
-  if (flag) return fail(KVQ_ERR_RANGE, "a quantized input was non-finite or |x| > 2^14");
+  if (flag & 1u) return fail(KVQ_ERR_RANGE, "a quantized input was non-finite or |x| > 2^14");
+  if (flag & 2u) return fail(KVQ_ERR_PAGE, "an append reached a tile with no page mapped");
   return KVQ_OK;
 }
 
@@ -132,6 +213,7 @@ kvq_status kvq_append(kvq_cache* cache, const void* k_dev, const void* v_dev, in
   p.v_in = v_dev;
   p.blob = static_cast<char*>(cache->dev);
   p.off = table_ptr(cache);
+  set_pages(cache, p);
   p.range_flag = flag_ptr(cache);
   p.B = c.batch;
   p.H = c.n_kv_heads;
@@ -188,6 +270,7 @@ kvq_status kvq_append_ragged(const kvq_cache* cache, const int32_t* row_len, con
   p.v_in = v_dev;
   p.blob = static_cast<char*>(cache->dev);
   p.off = table_ptr(cache);
+  set_pages(cache, p);
   p.range_flag = flag_ptr(cache);
   p.B = c.batch;
   p.H = c.n_kv_heads;
@@ -262,6 +345,7 @@ kvq_status decode_plan(const kvq_cache* cache, const void* q_dev, float* out_dev
   p = DecodePlan{};
   p.blob = static_cast<const char*>(cache->dev);
   p.off = table_ptr(cache);
+  set_pages(cache, p);
   p.q = q_dev;
   p.out = out_dev;
   const size_t parts = (size_t)n_splits;
@@ -346,6 +430,7 @@ kvq_status kvq_decode_step(kvq_cache* cache, const void* k_dev, const void* v_de
   a.v_in = v_dev;
   a.blob = static_cast<char*>(cache->dev);
   a.off = table_ptr(cache);
+  set_pages(cache, a);
   a.range_flag = flag_ptr(cache);
   a.B = c.batch;
   a.H = c.n_kv_heads;

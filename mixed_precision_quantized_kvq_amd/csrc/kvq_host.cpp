@@ -35,9 +35,16 @@ const char* last_error() { return g_last_error.c_str(); }
 //   SK, SV sink    [n_sink][D] 16-bit
 //   RK, RV ring    [n_recent + 32][D] 16-bit; token t >= n_sink sits in slot (t-n_sink) mod R
 //   KN key norms   [D] fp32 (caches with KVQ_KEY_NORM, quantized key heads only)
-void region_sizes(const kvq_config& cfg, int h, uint64_t sz[kRegions]) {
+//   Paged caches hold KC..FL as pools of n_pages tiles in the same per-tile order (a 16-bit
+//   head's page holds 64 rows), one set of pools per head, shared by all rows.
+int page_stride(const kvq_config& cfg) {
+  return (int)((body_len(cfg.capacity, cfg.n_sink, cfg.n_recent) / kGroup + 1) / 2);
+}
+
+void region_sizes(const kvq_config& cfg, int h, uint64_t sz[kRegions], int n_pages) {
   const uint64_t D = (uint64_t)cfg.head_dim;
-  const uint64_t bmax = (uint64_t)body_len(cfg.capacity, cfg.n_sink, cfg.n_recent);
+  const uint64_t bmax = n_pages > 0 ? (uint64_t)n_pages * kTile
+                                    : (uint64_t)body_len(cfg.capacity, cfg.n_sink, cfg.n_recent);
   const uint64_t nblk = bmax / kGroup;
   const uint64_t ntile = (nblk + 1) / 2;
   const uint64_t kb = cfg.k_bits[h], vb = cfg.v_bits[h];
@@ -51,19 +58,42 @@ void region_sizes(const kvq_config& cfg, int h, uint64_t sz[kRegions]) {
   sz[KN] = key_norm(cfg) && kb != 16 ? D * 4 : 0;
 }
 
-uint64_t plan_layout(const kvq_config& cfg, uint64_t* off) {
+uint64_t plan_layout(const kvq_config& cfg, uint64_t* off, int n_pages, uint64_t* pt_off) {
   const uint64_t B = cfg.batch, H = cfg.n_kv_heads;
   uint64_t pos = align_up(kHeaderBytes + B * H * kRegions * 8);
+  if (n_pages <= 0) {
+    for (uint64_t b = 0; b < B; ++b)
+      for (uint64_t h = 0; h < H; ++h) {
+        uint64_t sz[kRegions];
+        region_sizes(cfg, (int)h, sz);
+        for (int r = 0; r < kRegions; ++r) {
+          if (off) off[(b * H + h) * kRegions + r] = pos;
+          pos = align_up(pos + sz[r]);
+        }
+      }
+    if (pt_off) *pt_off = 0;
+    return pos;
+  }
+  // pools KC..FL of each head, then the windows and norms of each (row, head), then the table
+  for (uint64_t h = 0; h < H; ++h) {
+    uint64_t sz[kRegions];
+    region_sizes(cfg, (int)h, sz, n_pages);
+    for (int r = KC; r <= FL; ++r) {
+      for (uint64_t b = 0; b < B && off; ++b) off[(b * H + h) * kRegions + r] = pos;
+      pos = align_up(pos + sz[r]);
+    }
+  }
   for (uint64_t b = 0; b < B; ++b)
     for (uint64_t h = 0; h < H; ++h) {
       uint64_t sz[kRegions];
-      region_sizes(cfg, (int)h, sz);
-      for (int r = 0; r < kRegions; ++r) {
+      region_sizes(cfg, (int)h, sz, n_pages);
+      for (int r = SK; r < kRegions; ++r) {
         if (off) off[(b * H + h) * kRegions + r] = pos;
         pos = align_up(pos + sz[r]);
       }
     }
-  return pos;
+  if (pt_off) *pt_off = pos;
+  return align_up(pos + B * (uint64_t)page_stride(cfg) * 4);
 }
 
 static bool bits_ok(int b) { return (b >= 2 && b <= 8) || b == 16; }

@@ -25,7 +25,7 @@ constexpr int kRegions = 10;
 constexpr uint64_t kAlign = 256;  // every region starts on a 256-byte boundary
 constexpr uint64_t kHeaderBytes = 256;
 constexpr uint32_t kMagic = 0x3151564Bu;  // "KVQ1"
-constexpr uint32_t kVersion = 2;        // 2: region KN (key norms) added
+constexpr uint32_t kVersion = 3;        // 2: region KN (key norms) added; 3: paged caches
 constexpr float kRangeLimit = 16384.0f;   // |x| <= 2^14 for quantized heads
 
 enum Region { KC = 0, KM, VC, VM, FL, SK, SV, RK, RV, KN };
@@ -43,6 +43,9 @@ struct BlobHeader {
   int32_t batch, n_kv_heads, head_dim, capacity;
   uint64_t table_offset; // byte offset of uint64 off[batch][n_kv_heads][kRegions]
   uint64_t total_bytes;
+  // paged caches (n_pages > 0): int32 page[batch][page_stride] at page_table_offset; -1 = unmapped
+  uint64_t page_table_offset;
+  int32_t n_pages, page_stride;
 };
 
 inline uint64_t align_up(uint64_t x, uint64_t a = kAlign) { return (x + a - 1) / a * a; }
@@ -56,9 +59,15 @@ inline int64_t body_len(int64_t T, int64_t n_sink, int64_t n_recent) {
 inline int ring_slots(int n_recent) { return n_recent + kGroup; }
 
 // Sizes of the kRegions regions of one (row, KV head).
-void region_sizes(const kvq_config& cfg, int kv_head, uint64_t sz[kRegions]);
+// Paged caches (n_pages > 0): the body regions KC..FL are pools of n_pages 64-token tiles.
+void region_sizes(const kvq_config& cfg, int kv_head, uint64_t sz[kRegions], int n_pages = 0);
+// Body tiles of a full row: the page table's row stride.
+int page_stride(const kvq_config& cfg);
 // Full layout: off[(row*H + head)*kRegions + region], returns the total blob size.
-uint64_t plan_layout(const kvq_config& cfg, uint64_t* off /* nullable */);
+// Paged caches: every row's entries for KC..FL name its head's pools, and *pt_off (nullable)
+// receives the page table's offset.
+uint64_t plan_layout(const kvq_config& cfg, uint64_t* off /* nullable */, int n_pages = 0,
+                     uint64_t* pt_off = nullptr);
 
 // Validation (sets the error string and returns a status).
 kvq_status check_config(const kvq_config* cfg);
@@ -83,6 +92,10 @@ struct AppendPlan {
   char* blob;            // device blob base
   const uint64_t* off;   // device region table
   uint32_t* range_flag;  // device sticky flag
+  // paged caches: the body tile t of row b lives in page pages[b * page_stride + t] of each
+  // head's pools (null for contiguous caches)
+  const int32_t* pages;
+  int page_stride, n_pages;
   int B, H, D, n_new;
   int len0, len1;        // token counts before / after
   int body0, body1;      // body lengths before / after
@@ -127,6 +140,8 @@ struct DecodePlan {
   float* out;            // [B][Hq][D]
   float* ws_o;           // [P][B][Hq][D]
   float* ws_ml;          // [P][B][Hq][2]
+  const int32_t* pages;  // paged caches: as in AppendPlan (null for contiguous caches)
+  int page_stride, n_pages;
   int B, H, Hq, G, D, T, body, n_sink_live, n_win, n_sink_cfg, ring;
   int Q;                 // query tokens per row: the last Q cached tokens, attended causally
   int ring0;             // ring slot of the oldest live window token (body mod ring)

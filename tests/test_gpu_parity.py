@@ -653,3 +653,96 @@ def test_ragged_rejects():
     with pytest.raises(kvq.KvqError) as e:
         kvq.append_ragged(cache65, [0] * 65, [1] * 65, k65, k65)
     assert e.value.status == -5
+
+
+# ------------------------------------------------------------------------- paged caches ---
+
+def _tile_bytes(ocfg, h):
+    """Bytes of one 64-token tile of regions KC..FL of head h (the page sizes of its pools)."""
+    D, kb, vb = ocfg.head_dim, ocfg.k_bits[h], ocfg.v_bits[h]
+    return [64 * D * 2 if kb == 16 else 64 * D * kb // 8,
+            0 if kb == 16 else 64 * (D // 32) * 4,
+            64 * D * 2 if vb == 16 else 64 * D * vb // 8,
+            0 if vb == 16 else 2 * D * 4,
+            2 * 2 * (D // 32) * 4 if ocfg.quant == "hybrid" else 0]
+
+
+def assert_paged_regions_equal(cache, oc, table, stride):
+    """Gather each (row, head)'s body regions out of the pools through `table` and compare
+    them, and the per-row regions, with the oracle's contiguous regions."""
+    cfg = oc.cfg
+    blob = cache.blob.cpu().numpy()
+    rt = cache.region_table().astype(np.int64)
+    ccfg = lib_cfg(kvq, cfg)
+    for b in range(cfg.batch):
+        for h in range(cfg.n_kv):
+            data, mask = O.expected_regions(oc, b, h)
+            tb = _tile_bytes(cfg, h)
+            for r in range(O.N_REGIONS):
+                size = kvq.region_offset(ccfg, b, h, r)[1]
+                if r <= 4:
+                    base = int(rt[b, h, r])
+                    got = np.concatenate([blob[base + int(table[b][t]) * tb[r]:][:tb[r]] for t in range(stride)])
+                    got = got[:size]
+                else:
+                    got = blob[int(rt[b, h, r]):int(rt[b, h, r]) + size]
+                assert got.size == data[r].size, (b, h, r)
+                m = mask[r]
+                bad = np.nonzero(got[m] != data[r][m])[0]
+                assert bad.size == 0, f"row {b} head {h} region {r}: {bad.size} bytes differ (first at {bad[:4]})"
+
+
+@pytest.mark.parametrize("kb,vb,quant,dtype,D", [((3, 2, 4), (2, 4, 3), "hybrid", "bf16", 128),
+                                                 ((16, 5, 2), (7, 16, 16), "asym", "fp16", 64)])
+def test_paged_cache(kb, vb, quant, dtype, D):
+    say(f"case: paged cache K bits {kb}, V bits {vb}, {quant}, {dtype}, D {D}")
+    B, H, G, T = 3, len(kb), 2, 1100
+    ocfg = O.CacheConfig(B, H, H * G, D, 1200, 4, 40, dtype, quant, kb, vb)
+    rng = np.random.default_rng(700 + D)
+    k = workloads.random_raw16(rng, (B, H, T, D), dtype, 3.0)
+    v = workloads.random_raw16(rng, (B, H, T, D), dtype)
+    q = workloads.random_raw16(rng, (B, H * G, D), dtype)
+    oc = O.build_cache(k, v, ocfg)
+    ref = gpu_cache(ocfg, k, v, chunks=[300, 1, 64, 735])
+    # a pool larger than the rows need, its pages dealt to (row, tile) in a shuffled order
+    stride = (O.body_len(1200, 4, 40) // 32 + 1) // 2
+    n_pages = B * stride + 7
+    perm = rng.permutation(n_pages)[:B * stride].astype(np.int32)
+    table = perm.reshape(B, stride)
+    cache = kvq.cache_init_paged(lib_cfg(kvq, ocfg), n_pages, device=DEV)
+    for b in range(B):
+        cache.map_pages(b, 0, table[b, :5].tolist())
+        cache.map_pages(b, 5, table[b, 5:].tolist())
+    pos = 0
+    for n in [300, 1, 64, 735]:
+        kvq.append(cache, to_dev(k[:, :, pos:pos + n]), to_dev(v[:, :, pos:pos + n]))
+        pos += n
+    torch.cuda.synchronize()
+    kvq.cache_check(cache)
+    assert_paged_regions_equal(cache, oc, table, stride)
+    say("    pooled regions gathered through the page table match the oracle")
+    check_decode(cache, oc, q, splits=(1, 5))
+    for ns in (1, 5):
+        assert np.array_equal(gpu_decode(cache, q, ns), gpu_decode(ref, q, ns)), ns
+    say("    paged decode equals the contiguous cache's decode bit for bit")
+
+
+def test_paged_unmapped_tile_is_flagged():
+    say("case: paged cache append into an unmapped tile")
+    ocfg = O.CacheConfig(1, 1, 1, 64, 400, 2, 8, "bf16", "asym", (2,), (3,))
+    rng = np.random.default_rng(710)
+    k = workloads.random_raw16(rng, (1, 1, 300, 64), "bf16")
+    v = workloads.random_raw16(rng, (1, 1, 300, 64), "bf16")
+    cache = kvq.cache_init_paged(lib_cfg(kvq, ocfg), 8, device=DEV)
+    cache.map_pages(0, 0, [3, 1])  # tiles 0 and 1: body tokens 0..127
+    kvq.append(cache, to_dev(k[:, :, :100]), to_dev(v[:, :, :100]))
+    torch.cuda.synchronize()
+    kvq.cache_check(cache)  # body 64 tokens: tile 0 only
+    kvq.append(cache, to_dev(k[:, :, 100:]), to_dev(v[:, :, 100:]))
+    torch.cuda.synchronize()
+    with pytest.raises(kvq.KvqError, match="ERR_PAGE"):
+        kvq.cache_check(cache)
+    with pytest.raises(kvq.KvqError, match="ERR_ARG"):
+        cache.map_pages(0, 0, [8])
+    with pytest.raises(kvq.KvqError, match="ERR_ARG"):
+        cache.map_pages(0, (O.body_len(400, 2, 8) // 32 + 1) // 2, [0])

@@ -25,7 +25,7 @@ def _header_functions():
 
 def test_library_exports_every_declared_function():
     names = _header_functions()
-    assert len(names) == 18
+    assert len(names) == 21
     assert sorted(kvq.EXPORTS) == names
     L = ctypes.CDLL(kvq.lib_path())
     for n in names:
@@ -193,3 +193,27 @@ def test_multi_and_ragged_host_checks():
     hb = _fake_cache(big, 0)
     assert L.kvq_append_ragged(ctypes.byref(hb), i32([0] * 65), i32([1] * 65), p, p, 1, None) == -5
     assert L.kvq_decode_ragged(ctypes.byref(hb), i32([1] * 65), p, p, 2, 0.0, p, 1 << 20, None) == -5
+
+
+def test_paged_cache_sizes_and_checks():
+    import mixed_precision_quantized_kvq_amd as kvq
+    from oracle import kvq_oracle as O
+    from tests.kvq_test_util import lib_cfg
+    ocfg = O.CacheConfig(2, 2, 4, 128, 1000, 4, 40, "bf16", "hybrid", (3, 16), (2, 4))
+    cfg = lib_cfg(kvq, ocfg)
+    stride = (O.body_len(1000, 4, 40) // 32 + 1) // 2
+    n1, n2 = kvq.cache_bytes_paged(cfg, 8), kvq.cache_bytes_paged(cfg, 12)
+    # every pool of every head grows by one tile per page; at multiples of 4 pages each pool
+    # is a whole number of 256-byte alignment units, so the difference is exact
+    per_page = sum(64 * 128 * 2 if b == 16 else 64 * 128 * b // 8 for b in (3, 16, 2, 4)) \
+        + 64 * 4 * 4 + 2 * 128 * 4 * 2 + 2 * (2 * 2 * 4 * 4)
+    assert n2 - n1 == 4 * per_page
+    # the per-row windows and the page table come on top of the pools
+    assert n1 >= 8 * per_page + 2 * stride * 4
+    with pytest.raises(kvq.KvqError, match="ERR_ARG"):
+        kvq.cache_bytes_paged(cfg, 0)
+    with pytest.raises(kvq.KvqError, match="ERR_ARG"):
+        kvq.cache_bytes_paged(cfg, 1 << 24)  # a pool over 2 GiB
+    h = kvq._Cache()
+    assert kvq.lib().kvq_cache_init_paged(ctypes.byref(h), ctypes.byref(cfg), 10, None, n1, None) == -1
+    assert kvq.lib().kvq_cache_map_pages(ctypes.byref(h), 0, 0, 1, None, None) == -1
