@@ -248,6 +248,8 @@ struct VTile {
 // fixed byte offset (a VGPR computed once) + the tile's byte offset (an SGPR). No address
 // register is rewritten per tile, so none can alias the destination of a load still in
 // flight, and an offset past the region returns zeros instead of faulting.
+constexpr int kWavePages = 64;  // page numbers one wavefront register holds (one per lane)
+
 // Paged caches also carry the row's page table: tile t is read from page pages[t] of the
 // head's pools.
 struct BodySrc {
@@ -670,7 +672,26 @@ template <int D, int KB, int VB, bool PAGED, class Prologue, class WindowIssue, 
 __device__ __forceinline__ void body_loop(Smem<D>& sm, const DecodePlan& p, const uint64_t* off, int body, int t0,
                                           int t1, int lane, int wave, Prologue prologue, WindowIssue window_issue,
                                           Window window, WaveState<D>& st) {
-  const BodySrc src = body_src(p, off, PAGED);
+  // paged caches: lane i holds the page of this wavefront's tile number pbase + i (loaded 64 at
+  // a time), and each tile's page is read out of that register, so the loads of the next tile
+  // never wait for a page-table lookup. src then carries no table: load_k / load_v take the
+  // page as the tile slot.
+  const BodySrc src = body_src(p, off, false);
+  const int32_t* row_pages = PAGED ? p.pages + (size_t)blockIdx.z * p.page_stride : nullptr;
+  int pv = 0, pbase = -kWavePages;
+  auto page_of = [&](int t) -> int {
+    if constexpr (!PAGED) {
+      return t;
+    } else {
+      const int k = (t - t0 - wave) / kWaves;  // the wavefront's k-th tile
+      if (k - pbase >= kWavePages) {
+        pbase = k;
+        const int tl = t0 + wave + (pbase + lane) * kWaves;
+        pv = tl < t1 ? body_page(row_pages, p.n_pages, tl) : 0;
+      }
+      return __builtin_amdgcn_readlane(pv, k - pbase);
+    }
+  };
   int tile = t0 + wave;
   const bool any = tile < t1;
   // two register buffers: the next tile is in flight while this one is computed
@@ -679,8 +700,9 @@ __device__ __forceinline__ void body_loop(Smem<D>& sm, const DecodePlan& p, cons
   WinUnit<D> wt;
   window_issue(wt);
   if (any) {  // the first tile is in flight while the query operands are prepared
-    load_k<D, KB>(kt[0], src, tile, lane);
-    load_v<D, VB>(vt[0], src, tile, lane);
+    const int pg = page_of(tile);
+    load_k<D, KB>(kt[0], src, pg, lane);
+    load_v<D, VB>(vt[0], src, pg, lane);
   }
   issue_barrier();
   const float kscale = prologue();
@@ -692,8 +714,9 @@ __device__ __forceinline__ void body_loop(Smem<D>& sm, const DecodePlan& p, cons
     // keep fixed registers and the loads stay in flight while this tile is computed
     const int next = tile + kWaves;
     const int fetch = next < t1 ? next : tile;
-    load_k<D, KB>(kfree, src, fetch, lane);
-    load_v<D, VB>(vfree, src, fetch, lane);
+    const int pg = page_of(fetch);
+    load_k<D, KB>(kfree, src, pg, lane);
+    load_v<D, VB>(vfree, src, pg, lane);
     issue_barrier();
     float sc[kMaxG];
     key_phase<D, KB>(sm, kcur, lane, kscale, sc);
