@@ -40,10 +40,15 @@ precision); every squared-error sum and the attention are float64. Where a float
 value decides an integer (a code, a hybrid flag, a bit allocation), the arithmetic and its
 order are written out so the device can reproduce it exactly.
 
-parity unpinned (against the pages): the byte layout of the packed cache and the exact
-definition of the symmetric variant are this library's own format; the pages print no
-worked example for them. They are pinned here only by internal invariants (round trips,
-brute-force nearest level, streaming == bulk).
+The oracle holds only the logical content of a cache: codes, float16 scales and zeros,
+hybrid flags, 16-bit rows and key norms. How the library lays those out in device memory is
+its own storage format, which no page defines; the tests read device blobs through a
+separate format module and compare the logical content with this module's.
+
+parity unpinned (against the pages): the exact definition of the symmetric variant is a
+reading of its own (the pages name the variant but give no formula or worked example). It
+is pinned here only by internal invariants (brute-force nearest level, exact zero level,
+hybrid error never above either variant's).
 """
 from __future__ import annotations
 
@@ -201,10 +206,6 @@ def body_len(T: int, n_sink: int, n_recent: int) -> int:
     """Quantized token count after T tokens: whole 32-token blocks that have left the
     recent window, so the window keeps between n_recent and n_recent + 31 tokens."""
     return GROUP * max(0, (T - n_sink - n_recent) // GROUP)
-
-
-def ring_slots(n_recent: int) -> int:
-    return n_recent + GROUP
 
 
 @dataclasses.dataclass
@@ -613,206 +614,3 @@ def allocate_continuous(alpha, beta, w, total, b_lo, b_hi, cap=False, tol=1e-13)
         if hi - lo < tol:
             break
     return bits_at(0.5 * (lo + hi))
-
-
-# ----------------------------------------------------------------------------------------
-# Device blob layout (this library's format; parity unpinned against the pages)
-# ----------------------------------------------------------------------------------------
-
-HEADER_BYTES = 256
-N_REGIONS = 10
-REG_KC, REG_KM, REG_VC, REG_VM, REG_FL, REG_SK, REG_SV, REG_RK, REG_RV, REG_KN = range(N_REGIONS)
-TILE = 64  # body tokens per key tile
-
-
-def value_stream_position(b: int, s: int, k: int) -> int:
-    """Position, inside a 32-code value stream of width b, of the code that step s (0..7), slot
-    k (0..3) of the device's value plan reads. Step s covers chunk s // 2 (8 tokens of one
-    channel), token u = 4 (s % 2) + k of it. This is the library's storage order (a format
-    choice, restated here from its definition): pairs of codes that one shift and one mask
-    separate for the device sit at fixed distances in the stream."""
-    j = 2 * s + k // 2  # the step's register (pair of codes) k // 2
-    if b == 2:
-        return 16 * (j // 8) + j % 8 + 8 * (k % 2)
-    if b == 3:
-        lo_hi = [(0, 5), (1, 6), (2, 7), (10, 15), (11, 16), (20, 26), (21, 27), (24, 30),
-                 (3, 8), (4, 9), (14, 19), (12, 17), (13, 18), (22, 28), (23, 29), (25, 31)]
-        return lo_hi[j][k % 2]
-    if b == 4:
-        return 8 * (j // 4) + j % 4 + 4 * (k % 2)
-    if b in (5, 6, 7):
-        lo_hi = {5: [(0, 3), (2, 5), (7, 10), (8, 12), (15, 18), (20, 23), (22, 25), (27, 30),
-                     (1, 4), (6, 9), (11, 14), (13, 17), (16, 19), (21, 24), (26, 29), (28, 31)],
-                 6: [(0, 3), (1, 4), (6, 8), (7, 10), (11, 14), (15, 18), (21, 24), (26, 29),
-                     (28, 31), (2, 5), (17, 19), (9, 12), (13, 16), (20, 23), (22, 25), (27, 30)],
-                 7: [(0, 2), (4, 6), (8, 10), (12, 14), (16, 18), (20, 22), (24, 26), (28, 30),
-                     (1, 3), (5, 7), (9, 11), (13, 15), (17, 19), (21, 23), (25, 27), (29, 31)]}[b]
-        return lo_hi[j][k % 2]
-    return 4 * s + k // 2 + 2 * (k % 2)   # b == 8
-
-
-def _align(x, a=256):
-    return (x + a - 1) // a * a
-
-
-def region_sizes(cfg: CacheConfig, h: int):
-    """Bytes of each region of one (row, KV head) with key bits kb and value bits vb."""
-    D = cfg.head_dim
-    bmax = body_len(cfg.capacity, cfg.n_sink, cfg.n_recent)
-    nblk = bmax // GROUP
-    ntile = (nblk + 1) // 2
-    kb, vb = cfg.k_bits[h], cfg.v_bits[h]
-    sz = [0] * N_REGIONS
-    sz[REG_KC] = bmax * D * 2 if kb == 16 else ntile * TILE * D * kb // 8
-    sz[REG_KM] = 0 if kb == 16 else ntile * TILE * (D // GROUP) * 4
-    sz[REG_VC] = bmax * D * 2 if vb == 16 else ntile * TILE * D * vb // 8
-    sz[REG_VM] = 0 if vb == 16 else ntile * 2 * D * 4
-    sz[REG_FL] = nblk * 2 * (D // GROUP) * 4 if cfg.quant == "hybrid" else 0
-    sz[REG_SK] = sz[REG_SV] = cfg.n_sink * D * 2
-    sz[REG_RK] = sz[REG_RV] = ring_slots(cfg.n_recent) * D * 2
-    sz[REG_KN] = D * 4 if cfg.key_norm and kb != 16 else 0
-    return sz
-
-
-def layout(cfg: CacheConfig):
-    """Offsets (bytes from the blob start) [B][H][10] and the total blob size.
-    Header (256 B), then the offset table (uint64 [B][H][10]), then every region in
-    (row, head, region) order, each starting on a 256-byte boundary."""
-    B, H = cfg.batch, cfg.n_kv
-    off = np.zeros((B, H, N_REGIONS), dtype=np.uint64)
-    pos = _align(HEADER_BYTES + B * H * N_REGIONS * 8)
-    for b in range(B):
-        for h in range(H):
-            sz = region_sizes(cfg, h)
-            for r in range(N_REGIONS):
-                off[b, h, r] = pos
-                pos = _align(pos + sz[r])
-    return off, pos
-
-
-def kc_word_index(t_in_tile: int, w: int, W: int) -> int:
-    """uint32 index, inside one 64-token key tile, of word w (of W) of a token: the token's
-    words are cut into 16-byte chunks; chunk q of all 64 tokens is stored contiguously."""
-    q = w // 4
-    nq = min(4, W - 4 * q)
-    return 256 * q + t_in_tile * nq + (w - 4 * q)
-
-
-def expected_regions(oc: OracleCache, b: int, h: int):
-    """Expected bytes of each region of (row b, head h) in the device format, with a mask
-    of the bytes that are defined (written body tokens, live ring slots, filled sink)."""
-    cfg = oc.cfg
-    D, Gd = cfg.head_dim, cfg.groups
-    sz = region_sizes(cfg, h)
-    data = [np.zeros(s, dtype=np.uint8) for s in sz]
-    mask = [np.zeros(s, dtype=bool) for s in sz]
-    e = oc.heads[h]
-    body = oc.body
-    nblk = body // GROUP
-    kb, vb = cfg.k_bits[h], cfg.v_bits[h]
-    if kb == 16:
-        raw = e["k_raw"][b].reshape(-1).view(np.uint8)
-        data[REG_KC][:raw.size] = raw
-        mask[REG_KC][:raw.size] = True
-    elif body:
-        W = Gd * kb
-        words = pack(e["k_codes"][b], kb).reshape(body, W)          # [t][g*kb + k]
-        kc = np.zeros(sz[REG_KC] // 4, dtype=np.uint32)
-        km = np.zeros(sz[REG_KC] // 4, dtype=bool)
-        t = np.arange(body)
-        for w in range(W):
-            idx = (t // TILE) * (TILE * W) + np.array([kc_word_index(tt, w, W) for tt in range(TILE)])[t % TILE]
-            kc[idx] = words[:, w]
-            km[idx] = True
-        data[REG_KC] = kc.view(np.uint8)
-        mask[REG_KC] = np.repeat(km, 4)
-        meta = (e["k_s"][b].view(np.uint16).astype(np.uint32)
-                | (e["k_z"][b].view(np.uint16).astype(np.uint32) << np.uint32(16)))   # [t][g]
-        m = np.zeros(sz[REG_KM] // 4, dtype=np.uint32)
-        m[:body * Gd] = meta.reshape(-1)
-        data[REG_KM] = m.view(np.uint8)
-        mask[REG_KM][:body * Gd * 4] = True
-    if vb == 16:
-        raw = e["v_raw"][b].reshape(-1).view(np.uint8)
-        data[REG_VC][:raw.size] = raw
-        mask[REG_VC][:raw.size] = True
-    elif body:
-        # value tile (2 blocks of 32 tokens): decode lane l = 16 g4 + n (g4 = 2 * block + jp)
-        # holds D/32 streams of 32 codes; stream vg, step s, slot k is token 16 kk + 8 jp + u of
-        # channel 16 nb + n, with chunk c = s // 2, nb = 2 vg + c // 2, kk = c % 2,
-        # u = 4 (s % 2) + k; the stream sits at words (tile * 64 + l) * (D/32) * vb + vg * vb
-        codes = e["v_codes"][b]                                           # [j][c][32 tokens]
-        nv = D // GROUP
-        streams = np.zeros((nblk, 2, 16, nv, GROUP), dtype=np.int64)      # [j][jp][n][vg][pos]
-        jp_i = np.arange(2)[:, None, None]
-        n_i = np.arange(16)[None, :, None]
-        vg_i = np.arange(nv)[None, None, :]
-        for s_ in range(8):
-            for k_ in range(4):
-                c_ = s_ // 2
-                nb, kk, u = 2 * vg_i + c_ // 2, c_ % 2, 4 * (s_ % 2) + k_
-                ch = 16 * nb + n_i                                          # [1][16][nv]
-                tok = 16 * kk + 8 * jp_i + u                                # [2][1][1]
-                streams[..., value_stream_position(vb, s_, k_)] = codes[:, ch, tok]
-        words = pack(streams, vb)                                           # [j][jp][n][vg][vb]
-        vc = np.zeros(sz[REG_VC] // 4, dtype=np.uint32)
-        vm = np.zeros(sz[REG_VC] // 4, dtype=bool)
-        jb = np.arange(nblk)[:, None, None, None]
-        tile, blk = jb // 2, jb % 2
-        lane = (2 * blk + jp_i[None]) * 16 + n_i[None]                      # [j][2][16][1]
-        base = tile * 2 * D * vb + (lane * nv + vg_i[None]) * vb            # [j][2][16][nv]
-        for w in range(vb):
-            vc[(base + w).reshape(-1)] = words[..., w].reshape(-1)
-            vm[(base + w).reshape(-1)] = True
-        data[REG_VC] = vc.view(np.uint8)
-        mask[REG_VC] = np.repeat(vm, 4)
-        meta = (e["v_s"][b].view(np.uint16).astype(np.uint32)
-                | (e["v_z"][b].view(np.uint16).astype(np.uint32) << np.uint32(16)))   # [j][c]
-        m = np.zeros(sz[REG_VM] // 4, dtype=np.uint32)
-        mm = np.zeros(sz[REG_VM] // 4, dtype=bool)
-        jb = np.arange(nblk)[:, None]
-        c = np.arange(D)[None, :]
-        idx = (jb // 2) * 2 * D + (jb % 2) * D + (c % 16) * (D // 16) + c // 16
-        m[idx.reshape(-1)] = meta.reshape(-1)
-        mm[idx.reshape(-1)] = True
-        data[REG_VM] = m.view(np.uint8)
-        mask[REG_VM] = np.repeat(mm, 4)
-    if cfg.quant == "hybrid" and nblk:
-        Wf = Gd
-        fl = np.zeros(sz[REG_FL] // 4, dtype=np.uint32)
-        fm = np.zeros(sz[REG_FL] // 4, dtype=bool)
-        if kb != 16:
-            kf = e["k_flag"][b].reshape(nblk, GROUP * Gd).astype(np.uint64)   # bit tt*Gd + g
-            for jb in range(nblk):
-                for wd in range(Wf):
-                    bits = kf[jb, wd * 32:(wd + 1) * 32]
-                    fl[jb * 2 * Wf + wd] = int(sum(int(x) << i for i, x in enumerate(bits)))
-                    fm[jb * 2 * Wf + wd] = True
-        if vb != 16:
-            vf = e["v_flag"][b].astype(np.uint64)                           # [j][c]
-            for jb in range(nblk):
-                for wd in range(Wf):
-                    bits = vf[jb, wd * 32:(wd + 1) * 32]
-                    fl[jb * 2 * Wf + Wf + wd] = int(sum(int(x) << i for i, x in enumerate(bits)))
-                    fm[jb * 2 * Wf + Wf + wd] = True
-        data[REG_FL] = fl.view(np.uint8)
-        mask[REG_FL] = np.repeat(fm, 4)
-    ns = oc.sink_k.shape[2]
-    for reg, src in ((REG_SK, oc.sink_k), (REG_SV, oc.sink_v)):
-        raw = src[b, h].reshape(-1).view(np.uint8)
-        data[reg][:raw.size] = raw
-        mask[reg][:raw.size] = True
-    R = ring_slots(cfg.n_recent)
-    nwin = oc.win_k.shape[2]
-    for reg, src in ((REG_RK, oc.win_k), (REG_RV, oc.win_v)):
-        buf = data[reg].view(np.uint16).reshape(R, D)
-        mk = mask[reg].reshape(R, D * 2)
-        for i in range(nwin):
-            tok = ns + body + i
-            slot = (tok - cfg.n_sink) % R
-            buf[slot] = src[b, h, i]
-            mk[slot] = True
-    if sz[REG_KN]:
-        data[REG_KN] = oc.k_norm[b, h].astype(np.float32).view(np.uint8).copy()
-        mask[REG_KN][:] = True
-    return data, mask

@@ -13,6 +13,7 @@ import torch
 import mixed_precision_quantized_kvq_amd as kvq
 import workloads
 from oracle import kvq_oracle as O
+from tests import cache_format as F
 from tests.kvq_test_util import (head_slice_cfg, lib_cfg, oracle_bits, oracle_calibration,
                                  oracle_cfg, within_tol)
 
@@ -46,17 +47,17 @@ def gpu_cache(ocfg, k, v, chunks=None):
 
 
 def assert_regions_equal(cache, oc, rows=None, heads=None, map_bh=lambda b, h: (b, h)):
+    """Read every (row, KV head) of the device blob through the cache format and compare its
+    logical content (codes, scales, zeros, flags, 16-bit rows, norms) with the oracle's, bit
+    for bit."""
     cfg = oc.cfg
     for b in (range(cfg.batch) if rows is None else rows):
         for h in (range(cfg.n_kv) if heads is None else heads):
-            data, mask = O.expected_regions(oc, b, h)
             gb, gh = map_bh(b, h)
-            for r in range(O.N_REGIONS):
-                got = cache.region(gb, gh, r).cpu().numpy()
-                assert got.size == data[r].size, (b, h, r)
-                m = mask[r]
-                bad = np.nonzero(got[m] != data[r][m])[0]
-                assert bad.size == 0, f"row {b} head {h} region {r}: {bad.size} bytes differ (first at {bad[:4]})"
+            regions = [cache.region(gb, gh, r).cpu().numpy() for r in range(F.N_REGIONS)]
+            assert [x.size for x in regions] == F.region_sizes(cfg, h), (b, h)
+            got = F.decode_head(regions, cfg, h, oc.T)
+            F.assert_content_equal(got, F.oracle_head_content(oc, b, h), f"row {b} head {h}")
 
 
 def gpu_decode(cache, q, n_splits, scale=0.0):
@@ -657,39 +658,28 @@ def test_ragged_rejects():
 
 # ------------------------------------------------------------------------- paged caches ---
 
-def _tile_bytes(ocfg, h):
-    """Bytes of one 64-token tile of regions KC..FL of head h (the page sizes of its pools)."""
-    D, kb, vb = ocfg.head_dim, ocfg.k_bits[h], ocfg.v_bits[h]
-    return [64 * D * 2 if kb == 16 else 64 * D * kb // 8,
-            0 if kb == 16 else 64 * (D // 32) * 4,
-            64 * D * 2 if vb == 16 else 64 * D * vb // 8,
-            0 if vb == 16 else 2 * D * 4,
-            2 * 2 * (D // 32) * 4 if ocfg.quant == "hybrid" else 0]
-
-
 def assert_paged_regions_equal(cache, oc, table, stride):
-    """Gather each (row, head)'s body regions out of the pools through `table` and compare
-    them, and the per-row regions, with the oracle's contiguous regions."""
+    """Gather each (row, head)'s body regions out of the pools through `table`, read them and
+    the per-row regions through the cache format, and compare the logical content with the
+    oracle's."""
     cfg = oc.cfg
     blob = cache.blob.cpu().numpy()
     rt = cache.region_table().astype(np.int64)
     ccfg = lib_cfg(kvq, cfg)
     for b in range(cfg.batch):
         for h in range(cfg.n_kv):
-            data, mask = O.expected_regions(oc, b, h)
-            tb = _tile_bytes(cfg, h)
-            for r in range(O.N_REGIONS):
+            tb = F.tile_bytes(cfg, h)
+            regions = []
+            for r in range(F.N_REGIONS):
                 size = kvq.region_offset(ccfg, b, h, r)[1]
                 if r <= 4:
                     base = int(rt[b, h, r])
                     got = np.concatenate([blob[base + int(table[b][t]) * tb[r]:][:tb[r]] for t in range(stride)])
-                    got = got[:size]
+                    regions.append(got[:size])
                 else:
-                    got = blob[int(rt[b, h, r]):int(rt[b, h, r]) + size]
-                assert got.size == data[r].size, (b, h, r)
-                m = mask[r]
-                bad = np.nonzero(got[m] != data[r][m])[0]
-                assert bad.size == 0, f"row {b} head {h} region {r}: {bad.size} bytes differ (first at {bad[:4]})"
+                    regions.append(blob[int(rt[b, h, r]):int(rt[b, h, r]) + size])
+            got = F.decode_head(regions, cfg, h, oc.T)
+            F.assert_content_equal(got, F.oracle_head_content(oc, b, h), f"row {b} head {h}")
 
 
 @pytest.mark.parametrize("kb,vb,quant,dtype,D", [((3, 2, 4), (2, 4, 3), "hybrid", "bf16", 128),

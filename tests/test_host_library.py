@@ -12,6 +12,7 @@ import pytest
 import mixed_precision_quantized_kvq_amd as kvq
 import workloads
 from oracle import kvq_oracle as O
+from tests import cache_format as F
 from tests.kvq_test_util import lib_cfg, oracle_bits, oracle_cfg
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -107,25 +108,25 @@ def _configs():
 
 
 @pytest.mark.parametrize("ocfg", _configs(), ids=lambda c: f"B{c.batch}H{c.n_kv}D{c.head_dim}cap{c.capacity}")
-def test_layout_matches_oracle(ocfg):
+def test_layout_matches_format(ocfg):
     cfg = lib_cfg(kvq, ocfg)
-    off, total = O.layout(ocfg)
+    off, total = F.layout(ocfg)
     assert kvq.cache_bytes(cfg) == total
     for b in range(ocfg.batch):
         for h in range(ocfg.n_kv):
-            sz = O.region_sizes(ocfg, h)
-            for r in range(O.N_REGIONS):
+            sz = F.region_sizes(ocfg, h)
+            for r in range(F.N_REGIONS):
                 got = kvq.region_offset(cfg, b, h, r)
                 assert got == (int(off[b, h, r]), sz[r])
 
 
 def test_layout_regions_disjoint_and_aligned():
     ocfg = O.CacheConfig(2, 8, 32, 128, 32768, 4, 128, "bf16", "hybrid", (2, 3, 4, 3, 3, 4, 2, 3), (2,) * 8)
-    off, total = O.layout(ocfg)
+    off, total = F.layout(ocfg)
     spans = []
     for b in range(2):
         for h in range(8):
-            for r, s in enumerate(O.region_sizes(ocfg, h)):
+            for r, s in enumerate(F.region_sizes(ocfg, h)):
                 spans.append((int(off[b, h, r]), s))
     spans.sort()
     assert spans[0][0] >= 256 + 2 * 8 * 9 * 8

@@ -241,3 +241,60 @@ def test_calibration_distortion_orders_and_law():
     assert np.allclose(Dk, Dv, rtol=0.05)
     a, bt, r2, _ = O.fit_one(range(2, 9), list(Dk))
     assert 4.2 <= bt <= 4.5 and r2 > 0.99
+
+
+def test_calibration_grouping_direction_closed_form():
+    # values are grouped along tokens (32 tokens of one channel), keys along channels (32
+    # channels of one token), InnerQ page, abstract and "Core claim". Data constant along the
+    # tokens of every channel makes every value group constant, so its error is exactly 0
+    # (z = the group's value, s = 0), while key groups, which mix channels, are not; data
+    # constant along channels does the opposite. A transposed grouping on either axis fails.
+    rng = np.random.default_rng(15)
+    a = rng.normal(size=64).astype(np.float16)              # one fp16 value per channel
+    b = rng.normal(size=96).astype(np.float16)              # one fp16 value per token
+    tok_const = np.broadcast_to(a[None, :], (96, 64)).copy().view(np.uint16)
+    ch_const = np.broadcast_to(b[:, None], (96, 64)).copy().view(np.uint16)
+    for bits in (2, 3, 8):
+        for hyb in (False, True):
+            assert np.all(O.calib_group_sse(tok_const, "fp16", 1, bits, hyb) == 0.0)
+            assert np.all(O.calib_group_sse(tok_const, "fp16", 0, bits, hyb) > 0.0)
+            assert np.all(O.calib_group_sse(ch_const, "fp16", 0, bits, hyb) == 0.0)
+            assert np.all(O.calib_group_sse(ch_const, "fp16", 1, bits, hyb) > 0.0)
+    D = O.calib_distortion(tok_const, "fp16", 1, 2, 8, False)
+    assert np.all(D == 0.0)
+
+
+def test_calibration_groups_brute_force_on_channel_scaled_data():
+    # per-channel scales and x8 outlier channels (the key statistics of the workloads): the
+    # per-group errors, in the documented order (keys: token, then group; values: token block,
+    # then channel), equal a group-by-group loop over explicit index ranges
+    rng = np.random.default_rng(16)
+    T, D = 64, 64
+    x = rng.normal(size=(T, D)) * rng.lognormal(0.0, 0.5, size=D)[None, :]
+    x[:, [3, 17, 40, 41]] *= 8.0
+    raw = x.astype(np.float16).view(np.uint16)
+    xf = raw.view(np.float16).astype(np.float32)
+    for bits in (2, 4):
+        for hyb in (False, True):
+            want_k, want_v = [], []
+            for t in range(T):
+                for g in range(D // 32):
+                    want_k.append(_group_err(xf[t, 32 * g:32 * g + 32], bits, hyb))
+            for j in range(T // 32):
+                for c in range(D):
+                    want_v.append(_group_err(xf[32 * j:32 * j + 32, c], bits, hyb))
+            got_k = O.calib_group_sse(raw, "fp16", 0, bits, hyb)
+            got_v = O.calib_group_sse(raw, "fp16", 1, bits, hyb)
+            assert np.array_equal(got_k, np.array(want_k)), (bits, hyb)
+            assert np.array_equal(got_v, np.array(want_v)), (bits, hyb)
+
+
+def _group_err(g, bits, hyb):
+    """Squared error of one group of 32 values, summed element by element in float64."""
+    c, s, z, _ = O.quant_group(np.asarray(g, dtype=np.float32)[None, :], bits, hyb)
+    xhat = [float(ci) * float(s[0]) + float(z[0]) for ci in c[0]]
+    tot = 0.0
+    for xi, yi in zip(g.tolist(), xhat):
+        d = float(xi) - yi
+        tot = tot + d * d
+    return tot

@@ -6,12 +6,16 @@ value plans (code_plans.h) for the host and checks, for every width 2..8, that s
 step s holds code[chan(s, k)] << exp(s, k), inside the 10-bit mantissa, that every element
 of a group is used exactly once, that the value plans' exponents repeat every two steps
 (one weight operand serves every chunk), and that 2- to 4-bit codes sit at mantissa bit 2 or
-above (4 or above for 2 bits), where the MFMA sums them with little error.
+above (4 or above for 2 bits), where the MFMA sums them with little error. It also checks
+that the value plans read every stream in the order the cache format (tests/cache_format.py)
+stores it.
 """
 import os
 import subprocess
 
 import pytest
+
+from tests import cache_format as F
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "mixed_precision_quantized_kvq_amd", "csrc")
@@ -28,3 +32,12 @@ def test_unpack_plans(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.count(": 0 mismatches") == 14, r.stdout
+    # the value plans read each stream in the order the cache format stores it
+    seen = set()
+    for line in r.stdout.splitlines():
+        if line.startswith("value stream order B="):
+            head, vals = line.split(":")
+            b = int(head.split("=")[1])
+            assert [int(x) for x in vals.split()] == F.VALUE_STREAM_POS[b], b
+            seen.add(b)
+    assert seen == set(range(2, 9)), seen

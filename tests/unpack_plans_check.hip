@@ -75,8 +75,18 @@ int check_v(std::mt19937& g) {
   printf("value plan B=%d: %d mismatches\n", B, bad);
   return bad;
 }
+// The value stream order the plans imply: element e = 8 c + u of a stream (chunk c, token u)
+// is read by step 2 c + u / 4, slot u % 4, which takes stream position VSlots::chan of it.
+template <int B>
+void print_stream_order() {
+  printf("value stream order B=%d:", B);
+  for (int e = 0; e < 32; ++e) printf(" %d", VSlots<B>::chan(2 * (e / 8) + (e % 8) / 4, e % 4));
+  printf("\n");
+}
 int main() {
   std::mt19937 g(7);
+  print_stream_order<2>(); print_stream_order<3>(); print_stream_order<4>(); print_stream_order<5>();
+  print_stream_order<6>(); print_stream_order<7>(); print_stream_order<8>();
   int bad = check<2>(g) + check<3>(g) + check<4>(g) + check<5>(g) + check<6>(g) + check<7>(g) + check<8>(g);
   bad += check_v<2>(g) + check_v<3>(g) + check_v<4>(g) + check_v<5>(g) + check_v<6>(g) + check_v<7>(g) +
          check_v<8>(g);
