@@ -41,17 +41,18 @@ def parse():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run only the launches the HBM-counter passes measure: a 256 MiB "
                          "elementwise copy (counter calibration), then 30 decode launches")
+    ap.add_argument("--probe", choices=("decode", "append", "calib"),
+                    help="run only one kind of launch for a profiler pass, after the same 256 MiB "
+                         "copy: 30 split-K decode launches of --workload (rotating caches), 4 "
+                         "prefill appends of prefill_t4k, or 3 whole-model calibrations (K and V)")
+    ap.add_argument("--workload", default=WORKLOAD, help="decode workload of --probe decode")
     return ap.parse_args()
 
 
-def traffic_probe():
-    """The launches behind the committed FETCH_SIZE / WRITE_SIZE summary: torch.add over 64 Mi
-    int32 (256 MiB read + 256 MiB written, a plain copy of known size) 10 times, then 30
-    split-K decode launches over 5 rotating full-size cache instances."""
+def _copy_probe():
+    """torch.add over 64 Mi int32 (256 MiB read + 256 MiB written, a plain copy of known size)
+    10 times: the counter calibration of every profiler pass."""
     import torch
-
-    import mixed_precision_quantized_kvq_amd as kvq
-    import workloads
     dev = torch.device("cuda:0")
     n = 64 << 20
     src = torch.arange(n, dtype=torch.int32, device=dev)
@@ -59,27 +60,73 @@ def traffic_probe():
     for _ in range(10):
         torch.add(src, 1, out=dst)
     torch.cuda.synchronize()
-    del src, dst
-    w = workloads.make(WORKLOAD)
-    s = w["spec"]
-    kb, _ = kvq.allocate_bits(w["alpha_k"], w["beta_k"], w["w_k"], s.k_total, s.b_lo, s.b_hi)
-    vb, _ = kvq.allocate_bits(w["alpha_v"], w["beta_v"], w["w_v"], s.v_total, s.b_lo, s.b_hi)
-    cfg = kvq.Config.make(s.batch, s.n_kv, s.n_q, s.head_dim, s.tokens, s.n_sink, s.n_recent, s.dtype,
-                          s.quant, kb, vb)
-    kd = torch.from_numpy(w["k"].view(np.int16)).to(dev)
-    vd = torch.from_numpy(w["v"].view(np.int16)).to(dev)
-    caches = []
-    for _ in range(5):
-        c = kvq.KVCache(cfg, device=dev)
-        kvq.append(c, kd, vd)
-        caches.append(c)
-    del kd, vd
-    q = torch.from_numpy(w["q"].view(np.int16)).to(dev)
-    ws = torch.zeros(kvq.decode_workspace_bytes(caches[0], s.n_splits), dtype=torch.uint8, device=dev)
-    for i in range(30):
-        kvq.decode_splitk(caches[i % 5], q, s.n_splits, ws)
+
+
+def probe(kind, workload):
+    """The launches behind a committed profiler summary: the copy, then one kind of launch.
+    decode: 30 split-K decode launches of `workload` over rotating full-size caches (5, or 3
+    for the 128k-token context); append: 4 appends of the whole 16 x 4096-token prefill into
+    fresh caches; calib: 3 calibrations + fits of the 288-pair whole-model set, K and V."""
+    import torch
+
+    import mixed_precision_quantized_kvq_amd as kvq
+    import workloads
+    dev = torch.device("cuda:0")
+    _copy_probe()
+    if kind == "decode":
+        w = workloads.make(workload)
+        s = w["spec"]
+        kb, vb = workload_bits(kvq, w)
+        cfg = kvq.Config.make(s.batch, s.n_kv, s.n_q, s.head_dim, s.tokens, s.n_sink, s.n_recent, s.dtype,
+                              s.quant, kb, vb)
+        kd = torch.from_numpy(w["k"].view(np.int16)).to(dev)
+        vd = torch.from_numpy(w["v"].view(np.int16)).to(dev)
+        n_inst = 3 if s.tokens > 65536 else 5
+        caches = []
+        for _ in range(n_inst):
+            c = kvq.KVCache(cfg, device=dev)
+            kvq.append(c, kd, vd)
+            caches.append(c)
+        del kd, vd
+        q = torch.from_numpy(w["q"].view(np.int16)).to(dev)
+        ws = torch.zeros(kvq.decode_workspace_bytes(caches[0], s.n_splits), dtype=torch.uint8, device=dev)
+        for i in range(30):
+            kvq.decode_splitk(caches[i % n_inst], q, s.n_splits, ws)
+    elif kind == "append":
+        w = workloads.make("prefill_t4k")
+        s = w["spec"]
+        xk = torch.from_numpy(np.ascontiguousarray(w["k"][0, :, :s.calib_tokens]).view(np.int16)).to(dev)
+        xv = torch.from_numpy(np.ascontiguousarray(w["v"][0, :, :s.calib_tokens]).view(np.int16)).to(dev)
+        kb, vb = workload_bits(kvq, w, xk, xv)
+        cfg = kvq.Config.make(s.batch, s.n_kv, s.n_q, s.head_dim, s.tokens, s.n_sink, s.n_recent, s.dtype,
+                              s.quant, kb, vb)
+        kd = torch.from_numpy(w["k"].view(np.int16)).to(dev)
+        vd = torch.from_numpy(w["v"].view(np.int16)).to(dev)
+        for _ in range(4):
+            c = kvq.KVCache(cfg, device=dev)
+            kvq.append(c, kd, vd)
+            torch.cuda.synchronize()
+            kvq.cache_check(c)
+            del c
+    else:
+        m = workloads.make_model_calib()
+        s = m["spec"]
+        xk = torch.from_numpy(m["k"].view(np.int16)).to(dev)
+        xv = torch.from_numpy(m["v"].view(np.int16)).to(dev)
+        ws = torch.empty(kvq.calibrate_workspace_bytes(s.pairs, s.tokens, s.head_dim, 2, 8), dtype=torch.uint8,
+                         device=dev)
+        q = kvq.QUANT_HYBRID if s.quant == "hybrid" else kvq.QUANT_ASYM
+        for _ in range(3):
+            kvq.calibrate_fit(xk, s.dtype, kvq.AXIS_KEY, q, 2, 8, workspace=ws)
+            kvq.calibrate_fit(xv, s.dtype, kvq.AXIS_VALUE, q, 2, 8, workspace=ws)
     torch.cuda.synchronize()
-    print("traffic probe done", flush=True)
+    print(f"probe {kind} done", flush=True)
+
+
+def traffic_probe():
+    """The launches behind the committed FETCH_SIZE / WRITE_SIZE summary of the headline
+    decode: the copy, then 30 split-K decode launches of qwen8b_t32k over 5 rotating caches."""
+    probe("decode", WORKLOAD)
 
 
 def decode_bytes(spec, k_bits, v_bits, T, n_splits):
@@ -126,35 +173,94 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(w, k_bits, v_bits, seconds):
-    """Oracle decode timed on the host: the float64 oracle over a sample of (row, KV head)
-    slices of the same workload, BLAS limited to one thread."""
-    from threadpoolctl import threadpool_limits
+def _host_cpu():
+    """CPU model name and the cores this process may run on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return model, avail, os.cpu_count() or avail
 
+
+def _oracle_units(w, k_bits, v_bits, pairs):
     from oracle import kvq_oracle as O
     s = w["spec"]
     G = s.n_q // s.n_kv
-    pairs = [(b, h) for b in range(s.batch) for h in range(s.n_kv)][::4]
-    caches = []
+    units = []
     for b, h in pairs:
         cfg1 = O.CacheConfig(1, 1, G, s.head_dim, w["tokens"], s.n_sink, s.n_recent, s.dtype,
                              s.quant, (k_bits[h],), (v_bits[h],))
-        caches.append((O.build_cache(w["k"][b:b + 1, h:h + 1], w["v"][b:b + 1, h:h + 1], cfg1),
-                       w["q"][b:b + 1, h * G:(h + 1) * G]))
+        units.append((O.build_cache(w["k"][b:b + 1, h:h + 1], w["v"][b:b + 1, h:h + 1], cfg1),
+                      w["q"][b:b + 1, h * G:(h + 1) * G]))
+    return units
+
+
+def _oracle_worker(args):
+    """One process of the all-cores leg: decode its (row, KV head) units, built by the parent,
+    until `seconds` pass (one BLAS thread); returns (decodes done, elapsed)."""
+    units, seconds = args
+    from threadpoolctl import threadpool_limits
+
+    from oracle import kvq_oracle as O
     done = 0
     with threadpool_limits(1):
         t0 = time.perf_counter()
         while True:
-            for oc, q in caches:
+            for oc, q in units:
+                O.decode(oc, q)
+                done += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return done, el
+
+
+def cpu_baseline(w, k_bits, v_bits, seconds):
+    """The float64 oracle's decode timed on the host, over (row, KV head) units of the same
+    workload (each unit's cache built beforehand, outside the timing): first on one core (one
+    process, one BLAS thread), then on every available core up to 16 (one process per core,
+    each decoding its own units with one BLAS thread). The oracle holds its codes unpacked,
+    so a decode is dequantization plus float64 attention."""
+    import multiprocessing as mp
+    from threadpoolctl import threadpool_limits
+
+    from oracle import kvq_oracle as O
+    s = w["spec"]
+    model, avail, n_cpu = _host_cpu()
+    pairs = [(b, h) for b in range(s.batch) for h in range(s.n_kv)]
+    all_units = _oracle_units(w, k_bits, v_bits, pairs)
+    one = all_units[::4]
+    done = 0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        while True:
+            for oc, q in one:
                 O.decode(oc, q)
                 done += 1
             el = time.perf_counter() - t0
             if el >= seconds:
                 break
-    return {"value": done * w["tokens"] / el, "unit": "KV tokens*heads/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{len(pairs)} of {s.batch * s.n_kv} (row, KV head) slices of {WORKLOAD}, "
-                      f"{done} float64 decodes in {el:.1f} s (unpack codes, dequantize, attention)"}
+    res = {"value": done * w["tokens"] / el, "unit": "KV tokens*heads/s", "cores": 1, "kind": "oracle",
+           "sample": f"{len(one)} of {len(pairs)} (row, KV head) units of {WORKLOAD}, {done} float64 decodes "
+                     f"in {el:.1f} s on one core (dequantize + attention; codes held unpacked)",
+           "host_cpu": model, "host_cpus_available": avail, "host_cpus_total": n_cpu}
+    n_proc = max(1, min(16, avail, len(all_units)))
+    if n_proc > 1:
+        per = [all_units[i::n_proc] for i in range(n_proc)]
+        with mp.get_context("spawn").Pool(n_proc) as pool:
+            out = pool.map(_oracle_worker, [(u, seconds) for u in per])
+        res["all_cores"] = {
+            "value": sum(d * w["tokens"] / e for d, e in out), "unit": "KV tokens*heads/s", "cores": n_proc,
+            "sample": f"all {len(pairs)} (row, KV head) units over {n_proc} processes, "
+                      f"{sum(d for d, _ in out)} float64 decodes in {max(e for _, e in out):.1f} s"}
+    return res
 
 
 def workload_bits(kvq, w, xk=None, xv=None):
@@ -229,6 +335,52 @@ def other_configs():
                      "n_splits": s.n_splits, "kv_tokens_heads_per_s": s.batch * s.n_kv * s.tokens / (us * 1e-6)}
         del caches, ws, q
         torch.cuda.empty_cache()
+    # the 32k-token workload on paged caches: 64-token pages dealt to (row, tile) from a pool
+    # in a shuffled order, one permutation per cache instance
+    w = workloads.make("qwen8b_t32k")
+    s = w["spec"]
+    kb, vb = workload_bits(kvq, w)
+    cfg = kvq.Config.make(s.batch, s.n_kv, s.n_q, s.head_dim, s.tokens, s.n_sink, s.n_recent, s.dtype, s.quant,
+                          kb, vb)
+    stride = (32 * max(0, (s.tokens - s.n_sink - s.n_recent) // 32) // 32 + 1) // 2
+    n_pages = s.batch * stride + 64
+    kd = torch.from_numpy(w["k"].view(np.int16)).to(dev)
+    vd = torch.from_numpy(w["v"].view(np.int16)).to(dev)
+    rng = np.random.default_rng(2)
+    caches = []
+    for _ in range(5):
+        c = kvq.cache_init_paged(cfg, n_pages, device=dev)
+        perm = rng.permutation(n_pages)[:s.batch * stride].reshape(s.batch, stride)
+        for b in range(s.batch):
+            c.map_pages(b, 0, perm[b].tolist())
+        kvq.append(c, kd, vd)
+        caches.append(c)
+    torch.cuda.synchronize()
+    for c in caches:
+        kvq.cache_check(c)
+    del kd, vd
+    q = torch.from_numpy(w["q"].view(np.int16)).to(dev)
+    ws = torch.zeros(kvq.decode_workspace_bytes(caches[0], s.n_splits), dtype=torch.uint8, device=dev)
+    for i in range(10):
+        kvq.decode_splitk(caches[i % 5], q, s.n_splits, ws, stream=stream)
+    t_us = []
+    for _ in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(20_000_000)
+        e0.record(stream)
+        for i in range(50):
+            kvq.decode_splitk(caches[i % 5], q, s.n_splits, ws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_us.append(e0.elapsed_time(e1) * 1e3 / 50)
+    us = float(np.median(t_us))
+    nbytes = decode_bytes(s, kb, vb, s.tokens, s.n_splits)
+    res["qwen8b_t32k_paged"] = {"decode_us": us, "bytes_per_launch": nbytes, "achieved_gbs": nbytes / (us * 1e-6) / 1e9,
+                                "frac_of_8tbs": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "n_pages": n_pages,
+                                "page_tokens": 64, "n_splits": s.n_splits,
+                                "kv_tokens_heads_per_s": s.batch * s.n_kv * s.tokens / (us * 1e-6)}
+    del caches, ws, q
+    torch.cuda.empty_cache()
     # multi-token decode on the multi-head 7B-shaped layer: the last 4 tokens of every row at
     # once (4 query rows per KV head), against one query token (1 row per KV head)
     w = workloads.make("mha7b_t8k")
@@ -388,6 +540,9 @@ def main():
         sys.exit(2)
     if args.traffic_probe:
         traffic_probe()
+        return
+    if args.probe:
+        probe(args.probe, args.workload)
         return
     import torch
 

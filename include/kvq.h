@@ -168,6 +168,21 @@ kvq_status kvq_allocate_bits(int32_t n, const double* alpha, const double* beta,
                              const double* w, int32_t total_bits, int32_t b_lo, int32_t b_hi,
                              uint32_t flags, uint8_t* bits_out, double* bits_cont_out);
 
+/* Decision margin of an integer allocation (RateQuant section 3.3): host only, pure.
+ * bits: an allocation of the same inputs (for instance from kvq_allocate_bits). With
+ * key_i(b) = ln(w_i alpha_i beta_i^-b (1 - 1/beta_i)), the marginal key of head i's (b+1)-th
+ * bit evaluated as kvq_allocate_bits does, *margin_out = min over heads with bits_i > b_lo of
+ * key_i(bits_i - 1) minus max over heads with bits_i < b_hi of key_i(bits_i): how far, in log
+ * units, the last bit handed out beat the best bit left. It is >= 0 for a greedy allocation,
+ * 0 exactly at a tie, +inf when no bit was handed out or every head is at b_hi. Model
+ * parameters known only to a relative error e move each key by about (1 + b_hi) e, so two
+ * such inputs can allocate differently only when the margin is below a few times that (fits
+ * computed with differently ordered sums agree to ~1e-13). Same argument rules as
+ * kvq_allocate_bits, plus b_lo <= bits_i <= b_hi. */
+kvq_status kvq_allocation_margin(int32_t n, const double* alpha, const double* beta, const double* w,
+                                 const uint8_t* bits, int32_t b_lo, int32_t b_hi, uint32_t flags,
+                                 double* margin_out);
+
 /* Append n_new tokens to every row (InnerQ techniques (i)-(ii); asynchronous on stream).
  * k_dev, v_dev: [batch][n_kv_heads][n_new][head_dim] 16-bit. Tokens 0..n_sink-1 of a row
  * go to the sink; later tokens enter the recent ring; whenever the ring holds

@@ -21,7 +21,7 @@ __all__ = [
     "decode_workspace_bytes", "decode_attention", "decode_splitk", "decode_merge", "decode_step",
     "decode_multi_workspace_bytes", "decode_multi", "append_ragged", "decode_ragged",
     "cache_check",
-    "region_offset", "last_error",
+    "region_offset", "last_error", "allocation_margin",
     "F16", "BF16", "QUANT_ASYM", "QUANT_HYBRID", "KEY_NORM", "AXIS_KEY", "AXIS_VALUE", "ALLOC_CAP_W",
     "EXPORTS",
 ]
@@ -43,7 +43,7 @@ EXPORTS = ("kvq_cache_bytes", "kvq_cache_init", "kvq_calibrate_workspace_bytes",
            "kvq_decode_attention", "kvq_decode_splitk", "kvq_decode_merge", "kvq_decode_step",
            "kvq_decode_multi_workspace_bytes", "kvq_decode_multi", "kvq_append_ragged", "kvq_decode_ragged",
            "kvq_cache_check", "kvq_cache_bytes_paged", "kvq_cache_init_paged", "kvq_cache_map_pages",
-           "kvq_region_offset", "kvq_last_error")
+           "kvq_region_offset", "kvq_allocation_margin", "kvq_last_error")
 
 
 class KvqError(RuntimeError):
@@ -125,6 +125,7 @@ def lib():
             "kvq_decode_ragged": (I32, [KP, ctypes.POINTER(I32), P, P, I32, ctypes.c_float, P, SZ, P]),
             "kvq_cache_check": (I32, [KP, P]),
             "kvq_region_offset": (U64, [CP, I32, I32, I32, ctypes.POINTER(U64)]),
+            "kvq_allocation_margin": (I32, [I32, D, D, D, ctypes.POINTER(ctypes.c_uint8), I32, I32, U32, D]),
             "kvq_last_error": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -184,6 +185,17 @@ def allocate_bits(alpha, beta, w, total_bits: int, b_lo: int, b_hi: int, cap: bo
     _check(lib().kvq_allocate_bits(n, _darr(alpha), _darr(beta), _darr(w), int(total_bits),
                                    int(b_lo), int(b_hi), ALLOC_CAP_W if cap else 0, out, cont))
     return [int(v) for v in out], [float(v) for v in cont]
+
+
+def allocation_margin(alpha, beta, w, bits, b_lo: int, b_hi: int, cap: bool = False) -> float:
+    """Decision margin of an integer allocation (ln units): smallest key handed a bit minus the
+    largest key left without one."""
+    n = len(alpha)
+    b = (ctypes.c_uint8 * n)(*[int(x) for x in bits])
+    m = ctypes.c_double(0.0)
+    _check(lib().kvq_allocation_margin(n, _darr(alpha), _darr(beta), _darr(w), b, int(b_lo), int(b_hi),
+                                       ALLOC_CAP_W if cap else 0, ctypes.byref(m)))
+    return float(m.value)
 
 
 # ------------------------------------------------------------------------- device calls --

@@ -36,8 +36,10 @@ SOURCES = {
 def _compile(name, extra):
     src = os.path.join(CSRC, name)
     obj = os.path.join(BUILD, name + ".o")
-    lang = ["-x", "hip"] if name.endswith(".hip") else ["-x", "hip"]
-    cmd = [HIPCC] + COMMON + extra + lang + ["-c", src, "-o", obj]
+    # every source, the host-only .cpp files included, is compiled as HIP: those call the HIP
+    # runtime and launch through the .hip files' launchers, and one language keeps the
+    # runtime headers' configuration identical across objects
+    cmd = [HIPCC] + COMMON + extra + ["-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile {name} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

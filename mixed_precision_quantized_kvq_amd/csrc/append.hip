@@ -3,6 +3,7 @@
 // Built with -ffp-contract=off: the quantizer must round exactly as quant_device.h states.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "code_plans.h"
@@ -11,6 +12,8 @@
 
 namespace kvq {
 namespace {
+
+constexpr int kFlushWgPerCu = 4;  // persistent flush workgroups per compute unit
 
 // Token counts of row b for this append (uniform, or the row's own when ragged).
 __device__ __forceinline__ RowAppend row_append(const AppendPlan& p, int b) {
@@ -84,153 +87,219 @@ __device__ __forceinline__ void pack_value_stream(const uint8_t (*codes)[36], in
   }
 }
 
-// One workgroup per (flushed block, head, row); 2*D threads: thread i < D handles key group
-// i = (token tt of the block) * (D/32) + channel group g, thread D + c handles value channel c.
-// Value codes are staged in LDS and then written, one (decode lane, stream) per thread, in the
-// decode kernel's value order.
+// Flush of 32-token blocks leaving the recent window. One item is one block of one (row, KV
+// head); items are numbered ((row * H + head) * kmax + k), block k of the row's flushed ones
+// (kmax: the most any row flushes; a ragged row's items past its own count are skipped). The
+// grid is persistent: workgroup w takes items w, w + gridDim.x, ... With 2*D threads, the 32
+// input rows of keys and of values of an item (2 x 8 KB at D = 128) are staged in LDS; the
+// loads of the workgroup's next item are issued into registers before the current item is
+// quantized, and reach LDS after it, so each workgroup keeps a block's loads in flight while
+// it computes. From the stage, thread i < D quantizes key group i = (token tt of the block) *
+// (D/32) + channel group g, and thread D + c value channel c over the block's 32 tokens;
+// value codes go through LDS once more, to be written one (decode lane, stream) per thread in
+// the decode kernel's value order.
 // ASYM: the instantiation for asymmetric caches. The hybrid choice's float64 errors of both
-// variants need about twice the registers (166 against 78), so an asymmetric cache runs at
-// twice the occupancy without that code.
+// variants need about twice the registers, so an asymmetric cache runs at twice the
+// occupancy without that code.
 template <bool ASYM>
-__global__ __launch_bounds__(256) void append_flush_kernel(const AppendPlan p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ASYM ? 4 : 2))) void append_flush_kernel(
+    const AppendPlan p, int kmax) {
   const bool hybrid = !ASYM && p.hybrid != 0;
-  __shared__ alignas(4) uint8_t vcodes[128][36];  // [channel][token of the block], rows padded to 36 bytes
-  const int h = blockIdx.y, b = blockIdx.z;
-  const RowAppend ra = row_append(p, b);
-  if ((int)blockIdx.x >= (ra.body1 - ra.body0) / kGroup) return;  // ragged: this row flushes fewer blocks
-  const int j = ra.body0 / kGroup + blockIdx.x;                    // body block index
+  __shared__ alignas(16) uint16_t stage[2][kGroup][128];  // [keys | values][token of the block][channel]
+  __shared__ alignas(4) uint8_t vcodes[128][36];          // [channel][token of the block], rows padded to 36 bytes
   const int D = p.D, Gd = D / kGroup;
-  const uint64_t* off = p.off + ((size_t)b * p.H + h) * kRegions;
-  const size_t in_off = ((size_t)b * p.H + h) * p.n_new * D;
-  const uint16_t* kin = reinterpret_cast<const uint16_t*>(p.k_in) + in_off;
-  const uint16_t* vin = reinterpret_cast<const uint16_t*>(p.v_in) + in_off;
-  const int tid = threadIdx.x;
-  const bool is_key = tid < D;
-  const int bits = is_key ? p.k_bits[h] : p.v_bits[h];
-  const int vbits = p.v_bits[h];
-  const int tile = j >> 1, jj = j & 1;
-  // paged caches: the tile's page in this head's pools; an unmapped tile writes nothing and
-  // sets flag bit 1 (uniform over the workgroup, so no barrier is skipped by part of it)
-  int ptile = tile;
-  if (p.pages) {
-    ptile = p.pages[(size_t)b * p.page_stride + tile];
-    if (ptile < 0 || ptile >= p.n_pages) {
-      if (tid == 0) atomicOr(p.range_flag, 2u);
-      return;
-    }
-  }
-  const int pj = 2 * ptile + jj;  // the block's slot in the body region or pools
-  bool sym = false;
-  if (bits == 16) {
-    // unquantized head: the block's rows are copied
-    if (is_key) {
-      const int tt = tid / Gd, g = tid % Gd;
-      const uint16_t* src = token_row(p, ra.len0, p.blob + off[RK], kin, p.n_sink + j * kGroup + tt) + g * kGroup;
-      uint4* dst = reinterpret_cast<uint4*>(p.blob + off[KC]) + ((size_t)(pj * kGroup + tt) * D + g * kGroup) / 8;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) dst[v] = reinterpret_cast<const uint4*>(src)[v];
-    } else {
-      const int c = tid - D;
-      uint16_t* dst = reinterpret_cast<uint16_t*>(p.blob + off[VC]);
-#pragma unroll
-      for (int k = 0; k < 32; ++k)
-        dst[(size_t)(pj * kGroup + k) * D + c] = token_row(p, ra.len0, p.blob + off[RV], vin, p.n_sink + j * kGroup + k)[c];
-    }
-  } else {
-    float x[32];
-    if (is_key) {
-      const int tt = tid / Gd, g = tid % Gd;
-      load_row32(token_row(p, ra.len0, p.blob + off[RK], kin, p.n_sink + j * kGroup + tt) + g * kGroup, p.dtype, x);
-      if (p.key_norm) {  // the group holds k_c / n_c (IEEE fp32 division)
-        const float* kn = reinterpret_cast<const float*>(p.blob + off[KN]) + g * kGroup;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) x[i] = x[i] / kn[i];
+  const int n_items = p.B * p.H * kmax;
+  // Coordinates of an item; false for an item past its ragged row's flush count.
+  auto item = [&](int it, int& b, int& h, int& j, RowAppend& ra) {
+    const int k = it % kmax;
+    h = (it / kmax) % p.H;
+    b = it / (kmax * p.H);
+    ra = row_append(p, b);
+    j = ra.body0 / kGroup + k;
+    return k < (ra.body1 - ra.body0) / kGroup;
+  };
+  // Loads of an item's key and value rows: a block is 4 D 16-byte pieces per tensor, so
+  // thread t fetches pieces t and t + 2 D of each; a row still in the ring comes from the
+  // cache, a new one from the input.
+  uint4 rk0, rk1, rv0, rv1;
+  const int ltid = threadIdx.x;  // the loads' thread index (their addresses are cheap)
+  auto issue = [&](int it) {
+    int b, h, j;
+    RowAppend ra;
+    item(it, b, h, j, ra);
+    const uint64_t* off = p.off + ((size_t)b * p.H + h) * kRegions;
+    const size_t in_off = ((size_t)b * p.H + h) * p.n_new * D;
+    const uint16_t* kin = reinterpret_cast<const uint16_t*>(p.k_in) + in_off;
+    const uint16_t* vin = reinterpret_cast<const uint16_t*>(p.v_in) + in_off;
+    const int t0 = p.n_sink + j * kGroup + ltid / (D / 8), t1 = t0 + kGroup / 2, c8 = ltid % (D / 8);
+    rk0 = reinterpret_cast<const uint4*>(token_row(p, ra.len0, p.blob + off[RK], kin, t0))[c8];
+    rk1 = reinterpret_cast<const uint4*>(token_row(p, ra.len0, p.blob + off[RK], kin, t1))[c8];
+    rv0 = reinterpret_cast<const uint4*>(token_row(p, ra.len0, p.blob + off[RV], vin, t0))[c8];
+    rv1 = reinterpret_cast<const uint4*>(token_row(p, ra.len0, p.blob + off[RV], vin, t1))[c8];
+  };
+  auto to_lds = [&]() {
+    const int tt = ltid / (D / 8), c8 = ltid % (D / 8);
+    reinterpret_cast<uint4*>(&stage[0][tt][0])[c8] = rk0;
+    reinterpret_cast<uint4*>(&stage[0][tt + kGroup / 2][0])[c8] = rk1;
+    reinterpret_cast<uint4*>(&stage[1][tt][0])[c8] = rv0;
+    reinterpret_cast<uint4*>(&stage[1][tt + kGroup / 2][0])[c8] = rv1;
+  };
+  int it = blockIdx.x;
+  if (it >= n_items) return;  // uniform over the workgroup
+  issue(it);
+  to_lds();
+  __syncthreads();
+  while (true) {
+    const int nxt = it + (int)gridDim.x;
+    if (nxt < n_items) issue(nxt);  // in flight while this item is quantized
+    // The thread index, opaque to the compiler for this iteration: every address below derives
+    // from it, and hoisting those of all widths out of the loop would hold hundreds of
+    // registers across it.
+    int tid = threadIdx.x;
+    __asm__ __volatile__("" : "+v"(tid));
+    int b, h, j;
+    RowAppend ra;
+    const bool live = item(it, b, h, j, ra);
+    const uint64_t* off = p.off + ((size_t)b * p.H + h) * kRegions;
+    const bool is_key = tid < D;
+    const int bits = is_key ? p.k_bits[h] : p.v_bits[h];
+    const int vbits = p.v_bits[h];
+    const int tile = j >> 1, jj = j & 1;
+    // paged caches: the tile's page in this head's pools; an unmapped tile writes nothing and
+    // sets flag bit 1 (uniform over the workgroup, as are live and every branch on bits below)
+    int ptile = tile;
+    bool mapped = true;
+    if (live && p.pages) {
+      ptile = p.pages[(size_t)b * p.page_stride + tile];
+      if (ptile < 0 || ptile >= p.n_pages) {
+        if (tid == 0) atomicOr(p.range_flag, 2u);
+        mapped = false;
       }
-    } else {
-      const int c = tid - D;
-#pragma unroll
-      for (int k = 0; k < 32; ++k)
-        x[k] = widen16(token_row(p, ra.len0, p.blob + off[RV], vin, p.n_sink + j * kGroup + k)[c], p.dtype);
     }
-    if (out_of_range(x)) atomicOr(p.range_flag, 1u);
-    // the width is uniform over each wavefront (keys: wavefronts 0, 1; values: 2, 3)
-    auto group = [&](auto bc) {
-      constexpr int B = decltype(bc)::value;
-      uint32_t w[B];
-      const GroupQ q = quantize_pack<B>(x, hybrid, w);
-      sym = q.sym;
-      const uint32_t meta = (uint32_t)q.s_bits | ((uint32_t)q.z_bits << 16);
+    const int pj = 2 * ptile + jj;  // the block's slot in the body region or pools
+    const bool work = live && mapped;
+    bool sym = false;
+    if (work && bits == 16) {
+      // unquantized head: the block's rows are copied
       if (is_key) {
         const int tt = tid / Gd, g = tid % Gd;
-        const int W = Gd * B;  // words per token
-        const int t_in_tile = jj * kGroup + tt;
-        uint32_t* kc = reinterpret_cast<uint32_t*>(p.blob + off[KC]) + (size_t)ptile * kTile * W;
+        uint4* dst = reinterpret_cast<uint4*>(p.blob + off[KC]) + ((size_t)(pj * kGroup + tt) * D + g * kGroup) / 8;
 #pragma unroll
-        for (int k = 0; k < B; ++k) {
-          const int wi = g * B + k;
-          const int qc = wi >> 2, nq = min(4, W - 4 * qc);
-          kc[256 * qc + t_in_tile * nq + (wi - 4 * qc)] = w[k];
-        }
-        reinterpret_cast<uint32_t*>(p.blob + off[KM])[(size_t)(pj * kGroup + tt) * Gd + g] = meta;
+        for (int v = 0; v < 4; ++v) dst[v] = reinterpret_cast<const uint4*>(&stage[0][tt][g * kGroup])[v];
       } else {
         const int c = tid - D;
-        // codes of the 32 tokens, four to a word (the rows of vcodes are 36 bytes apart)
+        uint16_t* dst = reinterpret_cast<uint16_t*>(p.blob + off[VC]);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          uint32_t v4 = 0u;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int pos = (4 * m + u) * B, wi = pos >> 5, o = pos & 31;
-            uint32_t cd = w[wi] >> o;
-            if (o + B > 32) cd |= w[wi + 1] << (32 - o);
-            v4 |= (cd & ((1u << B) - 1u)) << (8 * u);
-          }
-          reinterpret_cast<uint32_t*>(vcodes[c])[m] = v4;
-        }
-        // (s|z) of channel c = 16 nb + n for this block, at [tile][block][n][nb]
-        reinterpret_cast<uint32_t*>(p.blob + off[VM])[(size_t)ptile * 2 * D + jj * D + (c & 15) * (D / 16) + (c >> 4)] =
-            meta;
+        for (int k = 0; k < 32; ++k) dst[(size_t)(pj * kGroup + k) * D + c] = stage[1][k][c];
       }
-    };
-    switch (bits) {
-      case 2: group(std::integral_constant<int, 2>{}); break;
-      case 3: group(std::integral_constant<int, 3>{}); break;
-      case 4: group(std::integral_constant<int, 4>{}); break;
-      case 5: group(std::integral_constant<int, 5>{}); break;
-      case 6: group(std::integral_constant<int, 6>{}); break;
-      case 7: group(std::integral_constant<int, 7>{}); break;
-      default: group(std::integral_constant<int, 8>{}); break;
+    } else if (work) {
+      float x[32];
+      if (is_key) {
+        const int tt = tid / Gd, g = tid % Gd;
+        const uint4* s4 = reinterpret_cast<const uint4*>(&stage[0][tt][g * kGroup]);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint4 u = s4[v];
+          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            x[v * 8 + 2 * k] = widen16((uint16_t)(w[k] & 0xFFFFu), p.dtype);
+            x[v * 8 + 2 * k + 1] = widen16((uint16_t)(w[k] >> 16), p.dtype);
+          }
+        }
+        if (p.key_norm) {  // the group holds k_c / n_c (IEEE fp32 division)
+          const float* kn = reinterpret_cast<const float*>(p.blob + off[KN]) + g * kGroup;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) x[i] = x[i] / kn[i];
+        }
+      } else {
+        const int c = tid - D;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) x[k] = widen16(stage[1][k][c], p.dtype);
+      }
+      if (out_of_range(x)) atomicOr(p.range_flag, 1u);
+      // the width is uniform over each wavefront (keys: wavefronts 0, 1; values: 2, 3)
+      auto group = [&](auto bc) {
+        constexpr int B = decltype(bc)::value;
+        uint32_t w[B];
+        const GroupQ q = quantize_pack<B>(x, hybrid, w);
+        sym = q.sym;
+        const uint32_t meta = (uint32_t)q.s_bits | ((uint32_t)q.z_bits << 16);
+        if (is_key) {
+          const int tt = tid / Gd, g = tid % Gd;
+          const int W = Gd * B;  // words per token
+          const int t_in_tile = jj * kGroup + tt;
+          uint32_t* kc = reinterpret_cast<uint32_t*>(p.blob + off[KC]) + (size_t)ptile * kTile * W;
+#pragma unroll
+          for (int k = 0; k < B; ++k) {
+            const int wi = g * B + k;
+            const int qc = wi >> 2, nq = min(4, W - 4 * qc);
+            kc[256 * qc + t_in_tile * nq + (wi - 4 * qc)] = w[k];
+          }
+          reinterpret_cast<uint32_t*>(p.blob + off[KM])[(size_t)(pj * kGroup + tt) * Gd + g] = meta;
+        } else {
+          const int c = tid - D;
+          // codes of the 32 tokens, four to a word (the rows of vcodes are 36 bytes apart)
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            uint32_t v4 = 0u;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int pos = (4 * m + u) * B, wi = pos >> 5, o = pos & 31;
+              uint32_t cd = w[wi] >> o;
+              if (o + B > 32) cd |= w[wi + 1] << (32 - o);
+              v4 |= (cd & ((1u << B) - 1u)) << (8 * u);
+            }
+            reinterpret_cast<uint32_t*>(vcodes[c])[m] = v4;
+          }
+          // (s|z) of channel c = 16 nb + n for this block, at [tile][block][n][nb]
+          reinterpret_cast<uint32_t*>(p.blob + off[VM])[(size_t)ptile * 2 * D + jj * D + (c & 15) * (D / 16) + (c >> 4)] =
+              meta;
+        }
+      };
+      switch (bits) {
+        case 2: group(std::integral_constant<int, 2>{}); break;
+        case 3: group(std::integral_constant<int, 3>{}); break;
+        case 4: group(std::integral_constant<int, 4>{}); break;
+        case 5: group(std::integral_constant<int, 5>{}); break;
+        case 6: group(std::integral_constant<int, 6>{}); break;
+        case 7: group(std::integral_constant<int, 7>{}); break;
+        default: group(std::integral_constant<int, 8>{}); break;
+      }
+      if (hybrid) {
+        // flag bit i of this block's key (value) words = group i of thread i (D + i)
+        const unsigned long long m = __ballot(sym);
+        if ((tid & 63) == 0) {
+          uint32_t* fl = reinterpret_cast<uint32_t*>(p.blob + off[FL]) + (size_t)pj * 2 * Gd;
+          const int wbase = (is_key ? 0 : Gd) + ((is_key ? tid : tid - D) >> 5);
+          fl[wbase] = (uint32_t)m;
+          fl[wbase + 1] = (uint32_t)(m >> 32);
+        }
+      }
     }
-  }
-  if (hybrid && bits != 16) {
-    // flag bit i of this block's key (value) words = group i of thread i (D + i)
-    const unsigned long long m = __ballot(sym);
-    if ((tid & 63) == 0) {
-      uint32_t* fl = reinterpret_cast<uint32_t*>(p.blob + off[FL]) + (size_t)pj * 2 * Gd;
-      const int wbase = (is_key ? 0 : Gd) + ((is_key ? tid : tid - D) >> 5);
-      fl[wbase] = (uint32_t)m;
-      fl[wbase + 1] = (uint32_t)(m >> 32);
+    __syncthreads();  // vcodes complete; every read of the stage done
+    if (work && vbits != 16 && !is_key) {
+      // value streams of this block: 32 decode lanes (g4 = 2 jj + jp, n) x D/32 streams each
+      const int xv = tid - D, nv = D / 32;
+      const int lane_local = xv / nv, vg = xv % nv;
+      const int jp = lane_local >> 4, n = lane_local & 15;
+      const int lane = (2 * jj + jp) * 16 + n;
+      uint32_t* dst = reinterpret_cast<uint32_t*>(p.blob + off[VC]) + (size_t)ptile * 2 * D * vbits +
+                      ((size_t)lane * nv + vg) * vbits;
+      switch (vbits) {
+        case 2: pack_value_stream<2>(vcodes, vg, jp, n, dst); break;
+        case 3: pack_value_stream<3>(vcodes, vg, jp, n, dst); break;
+        case 4: pack_value_stream<4>(vcodes, vg, jp, n, dst); break;
+        case 5: pack_value_stream<5>(vcodes, vg, jp, n, dst); break;
+        case 6: pack_value_stream<6>(vcodes, vg, jp, n, dst); break;
+        case 7: pack_value_stream<7>(vcodes, vg, jp, n, dst); break;
+        default: pack_value_stream<8>(vcodes, vg, jp, n, dst); break;
+      }
     }
-  }
-  if (vbits == 16) return;  // uniform over the workgroup
-  __syncthreads();
-  if (!is_key) {
-    // value streams of this block: 32 decode lanes (g4 = 2 jj + jp, n) x D/32 streams each
-    const int x = tid - D, nv = D / 32;
-    const int lane_local = x / nv, vg = x % nv;
-    const int jp = lane_local >> 4, n = lane_local & 15;
-    const int lane = (2 * jj + jp) * 16 + n;
-    uint32_t* dst = reinterpret_cast<uint32_t*>(p.blob + off[VC]) + (size_t)ptile * 2 * D * vbits +
-                    ((size_t)lane * nv + vg) * vbits;
-    switch (vbits) {
-      case 2: pack_value_stream<2>(vcodes, vg, jp, n, dst); break;
-      case 3: pack_value_stream<3>(vcodes, vg, jp, n, dst); break;
-      case 4: pack_value_stream<4>(vcodes, vg, jp, n, dst); break;
-      case 5: pack_value_stream<5>(vcodes, vg, jp, n, dst); break;
-      case 6: pack_value_stream<6>(vcodes, vg, jp, n, dst); break;
-      case 7: pack_value_stream<7>(vcodes, vg, jp, n, dst); break;
-      default: pack_value_stream<8>(vcodes, vg, jp, n, dst); break;
-    }
+    if (nxt >= n_items) break;
+    to_lds();         // the next item's rows, in flight since the top of this iteration
+    __syncthreads();  // vcodes free again; the stage holds the next item
+    it = nxt;
   }
 }
 
@@ -320,11 +389,17 @@ int launch_append_flush(const AppendPlan& p, void* stream) {
     nblk = max(nblk, (a.body1 - a.body0) / kGroup);
   }
   if (nblk <= 0) return (int)hipSuccess;
-  dim3 grid(nblk, p.H, p.B);
+  // persistent grid: a few workgroups per compute unit, each walking many items
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  const long long items = (long long)p.B * p.H * nblk;
+  const unsigned grid = (unsigned)std::min<long long>(items, (long long)kFlushWgPerCu * cus);
   if (p.hybrid)
-    hipLaunchKernelGGL(append_flush_kernel<false>, grid, dim3(2 * p.D), 0, (hipStream_t)stream, p);
+    hipLaunchKernelGGL(append_flush_kernel<false>, dim3(grid), dim3(2 * p.D), 0, (hipStream_t)stream, p, nblk);
   else
-    hipLaunchKernelGGL(append_flush_kernel<true>, grid, dim3(2 * p.D), 0, (hipStream_t)stream, p);
+    hipLaunchKernelGGL(append_flush_kernel<true>, dim3(grid), dim3(2 * p.D), 0, (hipStream_t)stream, p, nblk);
   return (int)hipGetLastError();
 }
 

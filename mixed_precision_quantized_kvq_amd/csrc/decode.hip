@@ -31,6 +31,7 @@
 
 #include <math.h>
 
+
 #include "code_plans.h"  // slot plans and code unpacking (shared with the append kernel)
 #include "kvq_internal.h"
 
@@ -143,23 +144,26 @@ __device__ __forceinline__ u32x4 ones_chunk(int kk) {
 
 template <int D>
 struct Smem {
-  // rows of the 4 query slots are padded by 4 words so that the 4 distinct addresses of an
+  // Query operands, one copy per wavefront: each wavefront builds its own, so no workgroup
+  // barrier stands between the start of the launch and its first tiles' compute.
+  // Rows of the 4 query slots are padded by 4 words so that the 4 distinct addresses of an
   // operand read fall in different LDS banks
   // (16-byte alignment lets operand reads use one ds_read_b64 with an immediate offset)
-  alignas(16) uint32_t qA[kMaxG][D / 2 + 4];      // key-MFMA A operand: fp16 q * 2^(Eq - e), slot order
-  alignas(16) uint32_t qW[kMaxG][D / 2 + 4];      // 16-bit-row A operand: q in the cache dtype
-  alignas(16) float qsum[kMaxG][D / 32];          // sum of q over each key group, times the softmax scale
-  float qn[kMaxG][D];                             // packed-key query: q, or q * n with key normalization
+  alignas(16) uint32_t qA[kWaves][kMaxG][D / 2 + 4];  // key-MFMA A operand: fp16 q * 2^(Eq - e), slot order
+  alignas(16) uint32_t qW[kWaves][kMaxG][D / 2 + 4];  // 16-bit-row A operand: q in the cache dtype
+  alignas(16) float qsum[kWaves][kMaxG][D / 32];      // sum of q over each key group, times the softmax scale
   alignas(16) uint32_t pw[kWaves][2][kMaxG][36];  // per wave: hi/lo, query, 2 blocks x 16 words (+4 pad)
   // packed-body weights per wave: [32-token block][hi/lo][query][token], fp16, rows padded to
   // 40 halves; plus 32 zero halves for the operand rows of the other block
   alignas(16) uint16_t pv[kWaves][2][2][kMaxG][40];
   alignas(16) uint16_t zero16[32];
-  float red_o[kWaves][kMaxG][D];
+  union {
+    alignas(16) float qn[kWaves][kMaxG][D];  // prologue: packed-key query, q or q * n with key normalization
+    float red_o[kWaves][kMaxG][D];           // epilogue: the wavefronts' partial outputs
+  };
   float red_m[kWaves][kMaxG];
   float red_l[kWaves][kMaxG];
   float new_s[kMaxG];  // fused decode step: scores of the appended token (log2 units)
-  float qmax[kWaves];
 };
 
 template <int D>
@@ -228,6 +232,46 @@ __device__ __forceinline__ void softmax_body(Smem<D>& sm, int wave, int lane, bo
   softmax_tile<D, true>(valid, sc, st, dst, kMaxG * 40, 40, pscl, false);
 }
 
+// The fp16 key-MFMA A operand of a wavefront, in slot order: slot (g * 8 + s) * 4 + k of query
+// row i holds q_i of channel 32 g + chan(s, k) times 2^(Eq - exp(s, k)) (q means q * n with
+// key normalization), from the wavefront's packed-key query in LDS. Lane l writes slots l,
+// l + 64, ... of every row; their (s, k) is (l / 4 % 8, l % 4) whatever the row and group, so
+// the slot plan is read once per lane, from compile-time constants.
+template <int D, int B>
+__device__ __forceinline__ void build_key_operand(Smem<D>& sm, int wave, int lane, int Eq) {
+  const int s = (lane >> 2) & 7, k = lane & 3;
+  int ch = 0, e = 0;
+#pragma unroll
+  for (int ss = 0; ss < 8; ++ss)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      if (s == ss && k == kk) {
+        ch = Slots<B>::chan(ss, kk);
+        e = Slots<B>::exp(ss, kk);
+      }
+#pragma unroll
+  for (int idx = lane; idx < kMaxG * D; idx += 64) {
+    const int i = idx / D, slot = idx % D, g = slot / 32;
+    const float qv = sm.qn[wave][i][g * 32 + ch];
+    reinterpret_cast<uint16_t*>(sm.qA[wave][i])[slot] = (uint16_t)f2h(__builtin_ldexpf(qv, Eq - e));
+  }
+  wave_lds_sync();
+}
+// The same for a width known only at run time (16-bit keys have no packed operand).
+template <int D>
+__device__ __forceinline__ void build_key_operand_rt(Smem<D>& sm, int wave, int lane, int Eq, int kb) {
+  switch (kb) {
+    case 2: build_key_operand<D, 2>(sm, wave, lane, Eq); break;
+    case 3: build_key_operand<D, 3>(sm, wave, lane, Eq); break;
+    case 4: build_key_operand<D, 4>(sm, wave, lane, Eq); break;
+    case 5: build_key_operand<D, 5>(sm, wave, lane, Eq); break;
+    case 6: build_key_operand<D, 6>(sm, wave, lane, Eq); break;
+    case 7: build_key_operand<D, 7>(sm, wave, lane, Eq); break;
+    case 8: build_key_operand<D, 8>(sm, wave, lane, Eq); break;
+    default: break;
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // Quantized body tiles
 // ---------------------------------------------------------------------------------------
@@ -273,10 +317,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t region_rsrc(const char* blob, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(blob + off[r]), (short)0,
                                            (int)(uint32_t)(off[r + 1] - off[r]), 0x00020000);
 }
+// The body regions with zero length: every load through them returns zeros without reading
+// memory, whatever its offsets (the bounds check fails for any offset).
+__device__ __forceinline__ BodySrc body_src_empty(const DecodePlan& p, const uint64_t* off) {
+  auto empty = [&](int r) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p.blob + off[r]), (short)0, 0, 0x00020000);
+  };
+  return BodySrc{empty(KC), empty(KM), empty(VC), empty(VM), nullptr, 0};
+}
 // paged = false drops the page lookups at compile time (contiguous caches)
-__device__ __forceinline__ BodySrc body_src(const DecodePlan& p, const uint64_t* off, bool paged) {
+__device__ __forceinline__ BodySrc body_src(const DecodePlan& p, const uint64_t* off, bool paged, int b) {
   return BodySrc{region_rsrc(p.blob, off, KC), region_rsrc(p.blob, off, KM), region_rsrc(p.blob, off, VC),
-                 region_rsrc(p.blob, off, VM), paged && p.pages ? p.pages + (size_t)blockIdx.z * p.page_stride : nullptr,
+                 region_rsrc(p.blob, off, VM), paged && p.pages ? p.pages + (size_t)b * p.page_stride : nullptr,
                  p.n_pages};
 }
 // Cache policy of the body loads: non-temporal (nt). Every packed byte is read once per
@@ -296,7 +348,9 @@ template <int D, int KB>
 __device__ __forceinline__ void load_k(KTile<D, KB>& t, const BodySrc& src, int tile, int lane) {
   constexpr int W = KTile<D, KB>::W;
   const int pg = body_page(src.pages, src.n_pages, tile);
-  const uint32_t soff = (uint32_t)pg * (kTile * W * 4);
+  // the tile offset is uniform: keep it in a scalar register, or the compiler may wrap every
+  // load in a loop over the distinct values of a vector register
+  const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)pg * (kTile * W * 4));
 #pragma unroll
   for (int q = 0; q < (W + 3) / 4; ++q) {
     const int nq = (W - 4 * q) < 4 ? (W - 4 * q) : 4;  // 4, or 2 for the last chunk
@@ -306,7 +360,8 @@ __device__ __forceinline__ void load_k(KTile<D, KB>& t, const BodySrc& src, int 
     else
       bload2(src.kc, voff, soff, &t.w[4 * q]);
   }
-  const uint32_t msoff = (uint32_t)pg * (kTile * (D / 32) * 4), mvoff = (uint32_t)lane * (D / 32) * 4;
+  const uint32_t msoff = __builtin_amdgcn_readfirstlane((uint32_t)pg * (kTile * (D / 32) * 4));
+  const uint32_t mvoff = (uint32_t)lane * (D / 32) * 4;
   if constexpr (D == 128)
     bload4(src.km, mvoff, msoff, t.m);
   else
@@ -321,7 +376,8 @@ template <int D, int VB>
 __device__ __forceinline__ void load_v(VTile<D, VB>& t, const BodySrc& src, int tile, int lane) {
   constexpr int NB = D / 16, NW = (NB / 2) * VB;
   const int pg = body_page(src.pages, src.n_pages, tile);
-  const uint32_t soff = (uint32_t)pg * (2 * D * VB * 4), voff = (uint32_t)lane * NW * 4;
+  const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)pg * (2 * D * VB * 4));
+  const uint32_t voff = (uint32_t)lane * NW * 4;
   if constexpr (NW % 4 == 0) {
 #pragma unroll
     for (int x = 0; x < NW; x += 4) bload4(src.vc, voff + 4 * x, soff, &t.w[x]);
@@ -329,7 +385,7 @@ __device__ __forceinline__ void load_v(VTile<D, VB>& t, const BodySrc& src, int 
 #pragma unroll
     for (int x = 0; x < NW; x += 2) bload2(src.vc, voff + 4 * x, soff, &t.w[x]);
   }
-  const uint32_t msoff = (uint32_t)pg * (2 * D * 4);
+  const uint32_t msoff = __builtin_amdgcn_readfirstlane((uint32_t)pg * (2 * D * 4));
   const uint32_t mvoff = (uint32_t)((lane >> 5) * D + (lane & 15) * NB) * 4;
 #pragma unroll
   for (int x = 0; x < NB; x += 4) bload4(src.vm, mvoff + 4 * x, msoff, &t.m[x]);
@@ -337,7 +393,7 @@ __device__ __forceinline__ void load_v(VTile<D, VB>& t, const BodySrc& src, int 
 
 // Scores (log2 units) of the lane's token for the 4 query slots.
 template <int D, int KB>
-__device__ __forceinline__ void key_phase(const Smem<D>& sm, const KTile<D, KB>& t, int lane, float kscale,
+__device__ __forceinline__ void key_phase(const Smem<D>& sm, int wave, const KTile<D, KB>& t, int lane, float kscale,
                                           float (&sc)[kMaxG]) {
   const int qi = lane & 3;
   constexpr int NG = D / 32;
@@ -349,7 +405,7 @@ __device__ __forceinline__ void key_phase(const Smem<D>& sm, const KTile<D, KB>&
   for (int s = 0; s < 8; ++s)
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.qA[qi][(g * 8 + s) * 2]);
+      const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.qA[wave][qi][(g * 8 + s) * 2]);
       acc[g] = mfma_f16(a, unpack_step<KB>(t.w, g * KB, s), acc[g]);
     }
   // fp16 s, z straight into mixed-precision FMAs: sum_g s_g acc_g and sum_g z_g qsum_g
@@ -360,7 +416,7 @@ __device__ __forceinline__ void key_phase(const Smem<D>& sm, const KTile<D, KB>&
 #pragma unroll
     for (int i = 0; i < kMaxG; ++i) {
       t1[i] = g == 0 ? sg * acc[g][i] : __builtin_fmaf(sg, acc[g][i], t1[i]);
-      t2[i] = g == 0 ? zg * sm.qsum[i][0] : __builtin_fmaf(zg, sm.qsum[i][g], t2[i]);
+      t2[i] = g == 0 ? zg * sm.qsum[wave][i][0] : __builtin_fmaf(zg, sm.qsum[wave][i][g], t2[i]);
     }
   }
 #pragma unroll
@@ -436,14 +492,14 @@ __device__ __forceinline__ float value_pscale(int tb) {
 // ---------------------------------------------------------------------------------------
 // q.K^T of 16-bit rows: lane = token, its key row x (D values, 16-byte pieces) in registers
 template <int D, bool BF16>
-__device__ __forceinline__ void key_phase_16(const Smem<D>& sm, const uint4 (&x)[D / 8], int lane, float scale_log2,
-                                             float (&sc)[kMaxG]) {
+__device__ __forceinline__ void key_phase_16(const Smem<D>& sm, int wave, const uint4 (&x)[D / 8], int lane,
+                                             float scale_log2, float (&sc)[kMaxG]) {
   const int qi = lane & 3;
   float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int v = 0; v < D / 8; ++v) {
-    const u32x2 a0 = *reinterpret_cast<const u32x2*>(&sm.qW[qi][4 * v]);
-    const u32x2 a1 = *reinterpret_cast<const u32x2*>(&sm.qW[qi][4 * v + 2]);
+    const u32x2 a0 = *reinterpret_cast<const u32x2*>(&sm.qW[wave][qi][4 * v]);
+    const u32x2 a1 = *reinterpret_cast<const u32x2*>(&sm.qW[wave][qi][4 * v + 2]);
     acc = mfma16<BF16>(a0, u32x2{x[v].x, x[v].y}, acc);
     acc = mfma16<BF16>(a1, u32x2{x[v].z, x[v].w}, acc);
   }
@@ -541,11 +597,11 @@ __device__ __forceinline__ void rows16_compute(Smem<D>& sm, const DecodePlan& p,
   issue_barrier();
   float sc[kMaxG];
   if (p.dtype == KVQ_BF16) {
-    key_phase_16<D, true>(sm, x, lane, p.scale_log2, sc);
+    key_phase_16<D, true>(sm, wave, x, lane, p.scale_log2, sc);
     softmax_rows16<D>(sm, wave, lane, valid, sc, st, lane & 31, 1.0f, true);
     value_phase_16<D, true>(sm, wave, lane, n_valid, r.v, st);
   } else {
-    key_phase_16<D, false>(sm, x, lane, p.scale_log2, sc);
+    key_phase_16<D, false>(sm, wave, x, lane, p.scale_log2, sc);
     softmax_rows16<D>(sm, wave, lane, valid, sc, st, lane & 31, 1.0f, false);
     value_phase_16<D, false>(sm, wave, lane, n_valid, r.v, st);
   }
@@ -607,7 +663,7 @@ __device__ __forceinline__ void win_compute_t(Smem<D>& sm, const DecodePlan& p, 
   float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int s = 0; s < D / 32; ++s) {
-    const u32x4 a = i < kMaxG ? *reinterpret_cast<const u32x4*>(&sm.qW[i][16 * s + 4 * j]) : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 a = i < kMaxG ? *reinterpret_cast<const u32x4*>(&sm.qW[wave][i][16 * s + 4 * j]) : u32x4{0u, 0u, 0u, 0u};
     acc = mfma_k32<BF16>(a, w.k[s], acc);
   }
   float sc[kMaxG];
@@ -669,15 +725,15 @@ __device__ __forceinline__ void win_compute(Smem<D>& sm, const DecodePlan& p, co
 // Quantized keys and values, both widths fixed: the loads of the next tile are issued before
 // the current tile is computed.
 template <int D, int KB, int VB, bool PAGED, class Prologue, class WindowIssue, class Window>
-__device__ __forceinline__ void body_loop(Smem<D>& sm, const DecodePlan& p, const uint64_t* off, int body, int t0,
-                                          int t1, int lane, int wave, Prologue prologue, WindowIssue window_issue,
-                                          Window window, WaveState<D>& st) {
+__device__ __forceinline__ void body_loop(Smem<D>& sm, const DecodePlan& p, const uint64_t* off, int b, int body,
+                                          int t0, int t1, int lane, int wave, Prologue prologue,
+                                          WindowIssue window_issue, Window window, WaveState<D>& st) {
   // paged caches: lane i holds the page of this wavefront's tile number pbase + i (loaded 64 at
   // a time), and each tile's page is read out of that register, so the loads of the next tile
   // never wait for a page-table lookup. src then carries no table: load_k / load_v take the
   // page as the tile slot.
-  const BodySrc src = body_src(p, off, false);
-  const int32_t* row_pages = PAGED ? p.pages + (size_t)blockIdx.z * p.page_stride : nullptr;
+  const BodySrc src = body_src(p, off, false, b);
+  const int32_t* row_pages = PAGED ? p.pages + (size_t)b * p.page_stride : nullptr;
   int pv = 0, pbase = -kWavePages;
   auto page_of = [&](int t) -> int {
     if constexpr (!PAGED) {
@@ -694,51 +750,58 @@ __device__ __forceinline__ void body_loop(Smem<D>& sm, const DecodePlan& p, cons
   };
   int tile = t0 + wave;
   const bool any = tile < t1;
-  // two register buffers: the next tile is in flight while this one is computed
+  // Two register buffers, each always in the same registers: a buffer is refilled while the
+  // other one is computed. The wavefront's first two tiles are in flight before the query
+  // prologue runs. Every fetch is issued, so the compiler's load counts stay fixed and no
+  // wait covers a load still needed in flight; a fetch past the wavefront's last tile goes
+  // through zero-length descriptors and reads nothing.
+  const BodySrc nul = body_src_empty(p, off);
   KTile<D, KB> kt[2];
   VTile<D, VB> vt[2];
+  auto fetch = [&](KTile<D, KB>& kd, VTile<D, VB>& vd, int t) {
+    const bool live = t < t1;
+    const BodySrc& s = live ? src : nul;
+    const int pg = page_of(live ? t : t0 + wave);
+    load_k<D, KB>(kd, s, pg, lane);
+    load_v<D, VB>(vd, s, pg, lane);
+  };
   WinUnit<D> wt;
   window_issue(wt);
-  if (any) {  // the first tile is in flight while the query operands are prepared
-    const int pg = page_of(tile);
-    load_k<D, KB>(kt[0], src, pg, lane);
-    load_v<D, VB>(vt[0], src, pg, lane);
-  }
+  fetch(kt[0], vt[0], tile);
+  fetch(kt[1], vt[1], tile + kWaves);
   issue_barrier();
-  const float kscale = prologue();
+  const int Eq = prologue();
+  build_key_operand<D, KB>(sm, wave, lane, Eq);
+  const float kscale = __builtin_ldexpf(p.scale_log2, 24 - Eq);
   window(wt);
   if (!any) return;
   const float pscl = value_pscale<VB>(lane & 31);
-  auto run = [&](const KTile<D, KB>& kcur, const VTile<D, VB>& vcur, KTile<D, KB>& kfree, VTile<D, VB>& vfree) {
-    // the next tile (or, past the end, this one again) is always fetched, so both buffers
-    // keep fixed registers and the loads stay in flight while this tile is computed
-    const int next = tile + kWaves;
-    const int fetch = next < t1 ? next : tile;
-    const int pg = page_of(fetch);
-    load_k<D, KB>(kfree, src, pg, lane);
-    load_v<D, VB>(vfree, src, pg, lane);
-    issue_barrier();
+  auto step = [&](const KTile<D, KB>& kcur, const VTile<D, VB>& vcur) {
     float sc[kMaxG];
-    key_phase<D, KB>(sm, kcur, lane, kscale, sc);
+    key_phase<D, KB>(sm, wave, kcur, lane, kscale, sc);
     softmax_body<D>(sm, wave, lane, tile * kTile + lane < body, sc, st, pscl);
     value_phase<D, VB>(sm, wave, vcur, lane, min(2, (body - tile * kTile) / 32), st);
     wave_lds_sync();
-    tile = next;
+    tile += kWaves;
   };
-  while (true) {
-    run(kt[0], vt[0], kt[1], vt[1]);
+  step(kt[0], vt[0]);
+  while (tile < t1) {
+    fetch(kt[0], vt[0], tile + kWaves);  // buffer 0 is free: the tile after this one
+    issue_barrier();
+    step(kt[1], vt[1]);
     if (tile >= t1) break;
-    run(kt[1], vt[1], kt[0], vt[0]);
-    if (tile >= t1) break;
+    fetch(kt[1], vt[1], tile + kWaves);
+    issue_barrier();
+    step(kt[0], vt[0]);
   }
 }
 
 template <int D, int KB>
-__device__ __forceinline__ void key_tile_q(const Smem<D>& sm, const BodySrc& src, int tile, int lane,
+__device__ __forceinline__ void key_tile_q(const Smem<D>& sm, int wave, const BodySrc& src, int tile, int lane,
                                            float kscale, float (&sc)[kMaxG]) {
   KTile<D, KB> t;
   load_k<D, KB>(t, src, tile, lane);
-  key_phase<D, KB>(sm, t, lane, kscale, sc);
+  key_phase<D, KB>(sm, wave, t, lane, kscale, sc);
 }
 
 template <int D, int VB>
@@ -753,13 +816,14 @@ __device__ __forceinline__ void value_tile_q(Smem<D>& sm, int wave, const BodySr
 // Body tiles of heads with a 16-bit key or value side (one phase 16-bit, the other packed
 // or 16-bit); no prefetch.
 template <int D>
-__device__ __forceinline__ void mixed_body_loop(Smem<D>& sm, const DecodePlan& p, const uint64_t* off, int body, int t0,
-                                                int t1, int lane, int wave, float kscale, WaveState<D>& st) {
-  const int kb = head_bits(p.k_bits, blockIdx.y), vb = head_bits(p.v_bits, blockIdx.y);
+__device__ __forceinline__ void mixed_body_loop(Smem<D>& sm, const DecodePlan& p, const uint64_t* off, int b, int h,
+                                                int body, int t0, int t1, int lane, int wave, float kscale,
+                                                WaveState<D>& st) {
+  const int kb = head_bits(p.k_bits, h), vb = head_bits(p.v_bits, h);
   const bool bf16 = p.dtype == KVQ_BF16;
   const uint16_t* kr = reinterpret_cast<const uint16_t*>(p.blob + off[KC]);
   const uint16_t* vr = reinterpret_cast<const uint16_t*>(p.blob + off[VC]);
-  const BodySrc src = body_src(p, off, true);
+  const BodySrc src = body_src(p, off, true, b);
   for (int tile = t0 + wave; tile < t1; tile += kWaves) {
     const int tok = tile * kTile + lane;
     const bool valid = tok < body;
@@ -767,13 +831,13 @@ __device__ __forceinline__ void mixed_body_loop(Smem<D>& sm, const DecodePlan& p
     const int pg = body_page(src.pages, src.n_pages, tile);
     float sc[kMaxG];
     switch (kb) {
-      case 2: key_tile_q<D, 2>(sm, src, tile, lane, kscale, sc); break;
-      case 3: key_tile_q<D, 3>(sm, src, tile, lane, kscale, sc); break;
-      case 4: key_tile_q<D, 4>(sm, src, tile, lane, kscale, sc); break;
-      case 5: key_tile_q<D, 5>(sm, src, tile, lane, kscale, sc); break;
-      case 6: key_tile_q<D, 6>(sm, src, tile, lane, kscale, sc); break;
-      case 7: key_tile_q<D, 7>(sm, src, tile, lane, kscale, sc); break;
-      case 8: key_tile_q<D, 8>(sm, src, tile, lane, kscale, sc); break;
+      case 2: key_tile_q<D, 2>(sm, wave, src, tile, lane, kscale, sc); break;
+      case 3: key_tile_q<D, 3>(sm, wave, src, tile, lane, kscale, sc); break;
+      case 4: key_tile_q<D, 4>(sm, wave, src, tile, lane, kscale, sc); break;
+      case 5: key_tile_q<D, 5>(sm, wave, src, tile, lane, kscale, sc); break;
+      case 6: key_tile_q<D, 6>(sm, wave, src, tile, lane, kscale, sc); break;
+      case 7: key_tile_q<D, 7>(sm, wave, src, tile, lane, kscale, sc); break;
+      case 8: key_tile_q<D, 8>(sm, wave, src, tile, lane, kscale, sc); break;
       default:
         uint4 x[D / 8];
         const uint4* r4 = reinterpret_cast<const uint4*>(kr + ((size_t)pg * kTile + (valid ? lane : 0)) * D);
@@ -781,9 +845,9 @@ __device__ __forceinline__ void mixed_body_loop(Smem<D>& sm, const DecodePlan& p
         for (int v = 0; v < D / 8; ++v) x[v] = r4[v];
         issue_barrier();
         if (bf16)
-          key_phase_16<D, true>(sm, x, lane, p.scale_log2, sc);
+          key_phase_16<D, true>(sm, wave, x, lane, p.scale_log2, sc);
         else
-          key_phase_16<D, false>(sm, x, lane, p.scale_log2, sc);
+          key_phase_16<D, false>(sm, wave, x, lane, p.scale_log2, sc);
         break;
     }
     const int nblk = n_valid / 32;
@@ -843,71 +907,76 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   auto grow = [&](int r) { return ((size_t)b * p.Q + r / G) * p.Hq + (size_t)h * G + r % G; };
   const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q);
 
-  // ---- q operands in LDS: raw 16-bit copy, the per-group sums of q, and the fp16 key
-  // operand in slot order with q scaled by 2^Eq so that max|q| * 2^Eq lies in [2^14, 2^15)
-  // (q means q * n for the packed keys of a cache with key normalization).
-  // Returns the key-score factor scale_log2 * 2^(24 - Eq). Every wavefront calls it once.
+  // ---- q operands, built by every wavefront for itself in its LDS slice: the raw 16-bit
+  // copy, the per-group sums of q, and the fp16 key operand in slot order with q scaled by
+  // 2^Eq so that max|q| * 2^Eq lies in [2^14, 2^15) (q means q * n for the packed keys of a
+  // cache with key normalization). The query loads are issued first, before the region
+  // table is read; the body and window loads follow as soon as the table is in. No barrier
+  // stands between a wavefront's start and its first tile.
+  constexpr int E = kMaxG * D / 64;  // consecutive query elements per lane (8 or 4): one 16- or 8-byte load
+  const int i0 = (lane * E) / D, c0 = (lane * E) % D;
+  // (rows past R read row R - 1 and are zeroed: no lane skips the load, so the compiler's
+  // count of loads in flight stays exact)
+  // Only loads are issued here; their values are first used in the prologue, after the window
+  // and body loads, so no wait for them stands in front of those.
+  const bool q_live = i0 < R;
+  uint32_t qw[E / 2];  // the lane's E 16-bit query elements, two to a word
+  {
+    const uint16_t* src = q + grow(q_live ? i0 : R - 1) * D + c0;
+    if constexpr (E == 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src);
+      qw[0] = v.x; qw[1] = v.y; qw[2] = v.z; qw[3] = v.w;
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(src);
+      qw[0] = v.x; qw[1] = v.y;
+    }
+  }
   // the region table of this (row, head), read once into scalar registers ahead of anything
   // the compiler must treat as a possible store
   const uint64_t* tab = p.off + ((size_t)b * p.H + h) * kRegions;
   uint64_t off[kRegions];
 #pragma unroll
   for (int r = 0; r < kRegions; ++r) off[r] = tab[r];
-  // the query loads are issued first, so they return ahead of the window and body loads
-  // issued next and the prologue does not wait for those
-  constexpr int E = kMaxG * D / kThreads;  // consecutive elements per thread (2 or 1)
-  const int i0 = (tid * E) / D;
-  uint32_t qraw[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) qraw[e] = i0 < R ? q[grow(i0) * D + (tid * E + e) % D] : 0u;
   // per-channel key norms (caches with key normalization, packed key heads): the packed keys
   // hold k / n, so the packed-key operand is built from q * n
+  // (only caches with norms load them: these loads are issued behind the region table, with
+  // the body loads' flood, and the prologue would wait for them)
   const bool use_norm = p.key_norm && kb != 16;
-  float knv[E];
+  float knraw[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    knv[e] = use_norm ? reinterpret_cast<const float*>(p.blob + off[KN])[(tid * E + e) % D] : 1.0f;
+  for (int e = 0; e < E; ++e) knraw[e] = 1.0f;
+  if (use_norm) {
+    const float* kn = reinterpret_cast<const float*>(p.blob + off[KN]) + c0;
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(kn + e);
+      knraw[e] = v.x; knraw[e + 1] = v.y; knraw[e + 2] = v.z; knraw[e + 3] = v.w;
+    }
+  }
   issue_barrier();
-  auto prologue = [&]() -> float {
+  // Returns Eq; the caller builds the key operand for its width (build_key_operand) and scores
+  // with the factor scale_log2 * 2^(24 - Eq). Every wavefront calls it once.
+  auto prologue = [&]() -> int {
     float qmax = 0.0f, qs = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int c = (tid * E + e) % D;
-      const uint32_t raw = qraw[e];
-      reinterpret_cast<uint16_t*>(sm.qW[i0])[c] = (uint16_t)raw;
-      const float v = widen(raw, p.dtype) * knv[e];
-      sm.qn[i0][c] = v;
+      const uint32_t qh = q_live ? (qw[e / 2] >> (16 * (e & 1))) & 0xFFFFu : 0u;
+      reinterpret_cast<uint16_t*>(sm.qW[wave][i0])[c0 + e] = (uint16_t)qh;
+      const float v = widen(qh, p.dtype) * knraw[e];
+      sm.qn[wave][i0][c0 + e] = v;
       qmax = fmaxf(qmax, fabsf(v));
       qs += v;
     }
     // a 32-channel group spans 32 / E aligned lanes
 #pragma unroll
     for (int o2 = 16 / E; o2 >= 1; o2 >>= 1) qs += __shfl_xor(qs, o2, 64);
-    if ((tid * E) % 32 == 0) sm.qsum[i0][((tid * E) % D) / 32] = qs * p.scale_log2;
-    if (tid < 32) sm.zero16[tid] = 0;
+    if (c0 % 32 == 0) sm.qsum[wave][i0][c0 / 32] = qs * p.scale_log2;
+    if (lane < 32) sm.zero16[lane] = 0;
     qmax = wave_max(qmax);
-    if (lane == 0) sm.qmax[wave] = qmax;
-    __syncthreads();
-    qmax = fmaxf(fmaxf(sm.qmax[0], sm.qmax[1]), fmaxf(sm.qmax[2], sm.qmax[3]));
+    wave_lds_sync();
     int qe = 0;
     if (qmax > 0.0f) (void)frexpf(qmax, &qe);
-    const int Eq = 15 - qe;
-    for (int idx = tid; idx < kMaxG * D; idx += kThreads) {
-      const int i = idx / D, slot = idx % D;  // slot = (g * 8 + s) * 4 + k
-      const int g = slot / 32, s = (slot / 4) % 8, k = slot % 4;
-      int ch = 0, e = 0;
-      switch (kb) {
-#define KVQ_SLOT(B_) \
-  case B_: ch = Slots<B_>::chan(s, k); e = Slots<B_>::exp(s, k); break;
-        KVQ_SLOT(2) KVQ_SLOT(3) KVQ_SLOT(4) KVQ_SLOT(5) KVQ_SLOT(6) KVQ_SLOT(7) KVQ_SLOT(8)
-#undef KVQ_SLOT
-        default: break;
-      }
-      const float qv = sm.qn[i][g * 32 + ch];
-      reinterpret_cast<uint16_t*>(sm.qA[i])[slot] = (uint16_t)f2h(__builtin_ldexpf(qv, Eq - e));
-    }
-    __syncthreads();
-    return __builtin_ldexpf(p.scale_log2, 24 - Eq);
+    return 15 - qe;
   };
 
   WaveState<D> st;
@@ -976,7 +1045,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   } else if (kb <= 4 && vb <= 4) {
     // the widths the allocator hands out in {2,3,4}: prefetching loop per combination
 #define KVQ_BODY(KB_, VB_) \
-  case KB_ * 16 + VB_: body_loop<D, KB_, VB_, PAGED>(sm, p, off, body, t0, t1, lane, wave, prologue, window_issue, window, st); break;
+  case KB_ * 16 + VB_: body_loop<D, KB_, VB_, PAGED>(sm, p, off, b, body, t0, t1, lane, wave, prologue, window_issue, window, st); break;
     switch (kb * 16 + vb) {
       KVQ_BODY(2, 2) KVQ_BODY(2, 3) KVQ_BODY(2, 4) KVQ_BODY(3, 2) KVQ_BODY(3, 3) KVQ_BODY(3, 4)
       KVQ_BODY(4, 2) KVQ_BODY(4, 3) KVQ_BODY(4, 4)
@@ -987,9 +1056,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // wider codes or a 16-bit side: one phase at a time
     WinUnit<D> wt;
     window_issue(wt);
-    const float kscale = prologue();
+    const int Eq = prologue();
+    build_key_operand_rt<D>(sm, wave, lane, Eq, kb);
+    const float kscale = __builtin_ldexpf(p.scale_log2, 24 - Eq);
     window(wt);
-    mixed_body_loop<D>(sm, p, off, body, t0, t1, lane, wave, kscale, st);
+    mixed_body_loop<D>(sm, p, off, b, h, body, t0, t1, lane, wave, kscale, st);
   } else {
     (void)prologue();  // not reached: the host launches the WIDE instantiation for such heads
   }
@@ -1030,7 +1101,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int hh = 0; hh < D / 64; ++hh) {
       const int c = (D / 64) * lane + hh;
-      acc = __builtin_fmaf(widen(reinterpret_cast<const uint16_t*>(sm.qW[wave])[c], p.dtype),
+      acc = __builtin_fmaf(widen(reinterpret_cast<const uint16_t*>(sm.qW[wave][wave])[c], p.dtype),
                            widen(nk[c], p.dtype), acc);
     }
 #pragma unroll

@@ -345,3 +345,52 @@ extern "C" kvq_status kvq_allocate_bits(int32_t n, const double* alpha, const do
   if (bits_cont_out) waterfill(n, alpha, beta, w.data(), total, b_lo, b_hi, bits_cont_out);
   return KVQ_OK;
 }
+
+// Decision margin of an integer allocation (RateQuant section 3.3): the smallest marginal key
+// that was handed a bit minus the largest key left without one. The greedy hands bits in key
+// order, so the margin of its result is >= 0, and 0 exactly where a tie was broken by index.
+extern "C" kvq_status kvq_allocation_margin(int32_t n, const double* alpha, const double* beta,
+                                            const double* w_in, const uint8_t* bits, int32_t b_lo,
+                                            int32_t b_hi, uint32_t flags, double* margin_out) {
+  using kvq::fail;
+  if (n < 1 || n > 1000000) return fail(KVQ_ERR_ARG, "n must be in 1..1e6");
+  if (!alpha || !beta || !w_in || !bits || !margin_out) return fail(KVQ_ERR_ARG, "NULL array");
+  if (!(2 <= b_lo && b_lo <= b_hi && b_hi <= 8)) return fail(KVQ_ERR_ARG, "need 2 <= b_lo <= b_hi <= 8");
+  if (flags & ~(uint32_t)KVQ_ALLOC_CAP_W) return fail(KVQ_ERR_ARG, "unknown flags");
+  for (int i = 0; i < n; ++i) {
+    if (!(std::isfinite(alpha[i]) && alpha[i] >= 0.0))
+      return fail(KVQ_ERR_ARG, "alpha must be finite and >= 0");
+    if (!(std::isfinite(beta[i]) && beta[i] > 1.0))
+      return fail(KVQ_ERR_ARG, "beta must be finite and > 1");
+    if (!(std::isfinite(w_in[i]) && w_in[i] > 0.0))
+      return fail(KVQ_ERR_ARG, "w must be finite and > 0");
+    if (bits[i] < b_lo || bits[i] > b_hi) return fail(KVQ_ERR_ARG, "bits outside [b_lo, b_hi]");
+  }
+  std::vector<double> w(w_in, w_in + n);
+  if (flags & KVQ_ALLOC_CAP_W) {
+    double mean = 0.0;
+    for (int i = 0; i < n; ++i) mean += w[i];
+    mean /= n;
+    for (int i = 0; i < n; ++i) w[i] = std::min(w[i], 5.0 * mean);
+  }
+  const double inf = std::numeric_limits<double>::infinity();
+  double taken = inf, left = -inf;
+  bool any_taken = false, any_left = false;
+  for (int i = 0; i < n; ++i) {
+    if (bits[i] > b_lo) {
+      taken = std::min(taken, marginal_key(w[i], alpha[i], beta[i], bits[i] - 1));
+      any_taken = true;
+    }
+    if (bits[i] < b_hi) {
+      left = std::max(left, marginal_key(w[i], alpha[i], beta[i], bits[i]));
+      any_left = true;
+    }
+  }
+  if (!any_taken || !any_left)
+    *margin_out = inf;
+  else if (taken == -inf && left == -inf)
+    *margin_out = 0.0;  // only heads with nothing to gain (alpha = 0) took and missed bits
+  else
+    *margin_out = taken - left;
+  return KVQ_OK;
+}

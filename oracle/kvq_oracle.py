@@ -558,6 +558,25 @@ def allocate_greedy(alpha, beta, w, total, b_lo, b_hi, cap=False):
     return bits
 
 
+def allocation_margin(alpha, beta, w, bits, b_lo, b_hi, cap=False):
+    """Decision margin of an integer allocation (ln units): the smallest marginal key that
+    received a bit minus the largest key left without one (keys as in allocate_greedy). The
+    greedy hands out bits in key order, so its allocation has margin >= 0; a margin near 0
+    means inputs perturbed by a tiny relative error may allocate differently. +inf when no bit
+    was handed out or every head is at b_hi; 0 when only alpha = 0 heads took and missed bits."""
+    check_alloc_args(alpha, beta, w, sum(bits), b_lo, b_hi)
+    if cap:
+        w = cap_weights(w)
+    taken = [marginal_key(w[i], alpha[i], beta[i], bits[i] - 1) for i in range(len(bits)) if bits[i] > b_lo]
+    left = [marginal_key(w[i], alpha[i], beta[i], bits[i]) for i in range(len(bits)) if bits[i] < b_hi]
+    if not taken or not left:
+        return math.inf
+    lo, hi = min(taken), max(left)
+    if lo == -math.inf and hi == -math.inf:
+        return 0.0
+    return lo - hi
+
+
 def objective(alpha, beta, w, bits):
     return sum(wi * ai * bi ** (-b) for ai, bi, wi, b in zip(alpha, beta, w, bits))
 

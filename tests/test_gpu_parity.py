@@ -325,6 +325,94 @@ def test_calibrate_matches_oracle(axis, quant):
     assert got[0][2] == 0.0 and got[1][2] == 4.0
 
 
+@pytest.mark.parametrize("axis", [0, 1])
+def test_calibrate_fit_fallback_for_poor_fits(axis):
+    """The RateQuant page's fallback (section W.10) through the library: two heads of plain
+    N(0,1) data fit well; a head of values a few bf16 ulps apart (its scale rounds to zero at
+    the high widths, so D(b) grows with b) fits beta <= 1 and takes the well-fitted heads'
+    mean; a head of four levels plus small noise (exact grids at the even widths only) fits
+    with R^2 < 0.96 and takes min(beta, that mean). alpha, beta and R^2 match the oracle's,
+    and the allocation from them is the oracle's, with a decision margin far above the
+    calibration's rounding."""
+    say(f"case: calibration fallback heads, axis={axis}")
+    rng = np.random.default_rng(55)
+    n, D = 512, 128
+    normal = [rng.normal(size=(n, D)) for _ in range(2)]
+    tiny = 2.0 ** -13 + rng.integers(0, 5, size=(n, D)) * 2.0 ** -20
+    zigzag = rng.integers(0, 4, size=(n, D)) / 3.0 + rng.normal(0.0, 1e-3, size=(n, D))
+    x = workloads.to_raw16(np.stack(normal + [tiny, zigzag]).astype(np.float32), "bf16")
+    Ds = [O.calib_distortion(x[h], "bf16", axis, 2, 8, False) for h in range(4)]
+    raw_fits = [O.fit_one(list(range(2, 9)), list(d)) for d in Ds]
+    assert raw_fits[2][1] <= 1.0 and raw_fits[3][2] < 0.96          # the crafted heads are poor fits
+    ref = O.fit_heads(list(range(2, 9)), Ds)
+    bbar = (ref[1][0] + ref[1][1]) / 2
+    assert ref[1][2] == bbar and ref[1][3] == min(raw_fits[3][1], bbar)
+    got = kvq.calibrate_fit(to_dev(x), "bf16", axis, kvq.QUANT_ASYM, 2, 8)
+    for g, r in zip(got, ref):
+        assert np.allclose(np.array(g), r, rtol=1e-13, atol=0), (g, r)
+    w = [1.0, 0.7, 1.3, 2.0]
+    want = O.allocate_greedy(list(ref[0]), list(ref[1]), w, 12, 2, 4)
+    bits, _ = kvq.allocate_bits(got[0], got[1], w, 12, 2, 4)
+    assert kvq.allocation_margin(ref[0], ref[1], w, want, 2, 4) > 1e-9
+    assert bits == want
+
+
+@pytest.mark.parametrize("quant,dtype", [("asym", "fp16"), ("hybrid", "fp16"), ("hybrid", "bf16")])
+def test_edge_groups_constant_zero_negative_zero_and_range_limit(quant, dtype):
+    """Groups the quantizer treats specially, through append and decode: constant groups and
+    all-zero groups (s = 0, every code 0), groups of -0 and groups whose minimum is -0 (the
+    zero is stored as +0), and groups reaching the input limit |x| = 2^14 (largest s and z).
+    Keys are groups of 32 channels of a token, values groups of 32 tokens of a channel (InnerQ
+    page, abstract and "Core claim"); hybrid caches also choose the symmetric variant per group
+    (technique (i)). The logical content must match the oracle bit for bit (zeros compared
+    as bits, so -0 and +0 differ) and decode must stay within tolerance per KV head."""
+    say(f"case: edge groups {quant} {dtype}")
+    B, H, D, T, ns, nr = 1, 3, 128, 400, 2, 32
+    kb, vb = (2, 3, 8), (2, 4, 8)
+    ocfg = O.CacheConfig(B, H, H, D, 512, ns, nr, dtype, quant, kb, vb)
+    rng = np.random.default_rng(58)
+    k = O.widen16(workloads.random_raw16(rng, (B, H, T, D), dtype), dtype)
+    v = O.widen16(workloads.random_raw16(rng, (B, H, T, D), dtype), dtype)
+    k[:, :, 40, 0:32] = 1.5                                   # constant key group
+    k[:, :, 41, 32:64] = 0.0                                  # all +0
+    k[:, :, 42, 64:96] = -0.0                                 # all -0
+    k[:, :, 43, 96:128] = np.abs(k[:, :, 43, 96:128])
+    k[:, :, 43, 100] = -0.0                                   # minimum is -0
+    k[:, :, 44, 0:32] = -2.0                                  # negative constant
+    k[:, 1, 50, 0:32] = np.where(np.arange(32) % 2, 16384.0, -16384.0)   # the input limit
+    k[:, 1, 51, 32:64] = 16384.0
+    k[:, 1, 52] = np.clip(np.round(k[:, 1, 52] * 5000.0), -16384.0, 16384.0)
+    blk = slice(ns + 32, ns + 64)                             # value block 1 of the body
+    v[:, :, blk, 5] = 0.75                                    # constant value group
+    v[:, :, blk, 6] = 0.0
+    v[:, :, blk, 7] = -0.0
+    v[:, :, blk, 8] = np.abs(v[:, :, blk, 8])
+    v[:, :, ns + 40, 8] = -0.0
+    v[:, 2, ns + 64:ns + 96, 9] = np.where(np.arange(32) % 3, 16384.0, -16384.0)
+    v[:, 2, ns + 96:ns + 128, 10] = -16384.0
+    kr, vr = workloads.to_raw16(k, dtype), workloads.to_raw16(v, dtype)
+    q = O.widen16(workloads.random_raw16(rng, (B, H, D), dtype), dtype)
+    q[:, 1] *= 1e-4                                           # keep head 1's scores moderate
+    qr = workloads.to_raw16(q, dtype)
+    oc = O.build_cache(kr, vr, ocfg)
+    for h in range(H):                                        # the oracle took the special paths
+        e = oc.heads[h]
+        t = lambda tok: tok - ns                               # body index of a sequence token
+        assert e["k_s"][0, t(40), 0] == 0 and e["k_s"][0, t(41), 1] == 0 and e["k_s"][0, t(42), 2] == 0
+        assert e["k_z"][0, t(42), 2].view(np.uint16) == 0 and e["k_z"][0, t(43), 3].view(np.uint16) == 0
+        assert e["v_s"][0, 1, 5] == 0 and e["v_z"][0, 1, 7].view(np.uint16) == 0
+    assert np.abs(O.widen16(kr[0, 1], dtype)).max() == 16384.0
+    cache = gpu_cache(ocfg, kr, vr, chunks=[100, 1, 299])     # cache_check: no range flag at 2^14
+    assert_regions_equal(cache, oc)
+    want = O.decode(oc, qr)
+    for ns_ in (1, 3):
+        got = gpu_decode(cache, qr, ns_)
+        for h in range(H):
+            ok, err, bound = within_tol(got[:, h], want[:, h])
+            say(f"    n_splits={ns_} head {h}: max err {err:.3e} (bound {bound:.3e})")
+            assert ok
+
+
 def test_range_flag_on_append_and_calibrate():
     say("case: out-of-range inputs")
     rng = np.random.default_rng(60)
@@ -736,3 +824,116 @@ def test_paged_unmapped_tile_is_flagged():
         cache.map_pages(0, 0, [8])
     with pytest.raises(kvq.KvqError, match="ERR_ARG"):
         cache.map_pages(0, (O.body_len(400, 2, 8) // 32 + 1) // 2, [0])
+
+
+def _paged_twin(ocfg, rng, extra_pages=9):
+    """A paged cache for ocfg with every tile of every row mapped to a page dealt from a pool
+    in shuffled order; returns (cache, table)."""
+    stride = (O.body_len(ocfg.capacity, ocfg.n_sink, ocfg.n_recent) // 32 + 1) // 2
+    n_pages = ocfg.batch * stride + extra_pages
+    table = rng.permutation(n_pages)[:ocfg.batch * stride].astype(np.int32).reshape(ocfg.batch, stride)
+    cache = kvq.cache_init_paged(lib_cfg(kvq, ocfg), n_pages, device=DEV)
+    for b in range(ocfg.batch):
+        cache.map_pages(b, 0, table[b].tolist())
+    return cache, table
+
+
+def test_paged_long_rows_and_every_entry_point():
+    """Paged caches through every call that takes one, each checked against a contiguous twin
+    (bit for bit) and the oracle: a long row (more than 64 tiles per wavefront at one split,
+    so the wavefront reloads its page register), a head that is 16-bit on both sides, fused
+    decode steps across a block flush, and multi-token decode."""
+    say("case: paged long rows, 16-bit head, decode_step, decode_multi")
+    rng = np.random.default_rng(720)
+    B, H, D, T = 2, 3, 128, 20700
+    kb, vb = (3, 16, 2), (2, 16, 4)
+    ocfg = O.CacheConfig(B, H, H, D, T + 40, 4, 64, "bf16", "hybrid", kb, vb)
+    k = workloads.random_raw16(rng, (B, H, T + 34, D), "bf16", 2.0)
+    v = workloads.random_raw16(rng, (B, H, T + 34, D), "bf16")
+    q = workloads.random_raw16(rng, (B, H, D), "bf16")
+    ref = gpu_cache(ocfg, k[:, :, :T], v[:, :, :T], chunks=[5000, 15700])
+    paged, table = _paged_twin(ocfg, rng)
+    for a, n in ((0, 5000), (5000, 15700)):
+        kvq.append(paged, to_dev(k[:, :, a:a + n]), to_dev(v[:, :, a:a + n]))
+    torch.cuda.synchronize()
+    kvq.cache_check(paged)
+    oc = O.build_cache(k[:, :, :T], v[:, :, :T], ocfg)
+    assert oc.body >= 20000
+    assert_paged_regions_equal(paged, oc, table, table.shape[1])
+    for ns in (1, 3):
+        got = gpu_decode(paged, q, ns)
+        assert np.array_equal(got, gpu_decode(ref, q, ns)), ns
+        ok, err, bound = within_tol(got, O.decode(oc, q))
+        say(f"    paged decode n_splits={ns}: max err {err:.3e} (bound {bound:.3e})")
+        assert ok
+    # fused decode steps: 34 one-token steps, one of which flushes a block into a page
+    ws = torch.zeros(kvq.decode_workspace_bytes(ref, 2), dtype=torch.uint8, device=DEV)
+    ws2 = torch.zeros_like(ws)
+    for i in range(34):
+        t = T + i
+        qs = workloads.random_raw16(rng, (B, H, D), "bf16")
+        o1 = torch.empty((B, H, D), dtype=torch.float32, device=DEV)
+        o2 = torch.empty_like(o1)
+        kvq.decode_step(ref, to_dev(k[:, :, t:t + 1]), to_dev(v[:, :, t:t + 1]), to_dev(qs), o1, 2, ws)
+        kvq.decode_step(paged, to_dev(k[:, :, t:t + 1]), to_dev(v[:, :, t:t + 1]), to_dev(qs), o2, 2, ws2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), i
+        if i in (0, 33):
+            want = O.decode(O.build_cache(k[:, :, :t + 1], v[:, :, :t + 1], ocfg), qs)
+            ok, err, bound = within_tol(o2.cpu().numpy().astype(np.float64), want)
+            say(f"    paged decode_step {i}: max err {err:.3e} (bound {bound:.3e})")
+            assert ok
+    kvq.cache_check(paged)
+    # multi-token decode of the last 3 tokens (G = 1, so 3 query rows per KV head)
+    qm = workloads.random_raw16(rng, (B, 3, H, D), "bf16")
+    outs = []
+    for c in (ref, paged):
+        out = torch.empty((B, 3, H, D), dtype=torch.float32, device=DEV)
+        wsm = torch.zeros(kvq.decode_multi_workspace_bytes(c, 3, 3), dtype=torch.uint8, device=DEV)
+        kvq.decode_multi(c, to_dev(qm), out, 3, wsm)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy().astype(np.float64))
+    assert np.array_equal(outs[0], outs[1])
+    want = O.decode_multi(O.build_cache(k, v, ocfg), qm)
+    ok, err, bound = within_tol(outs[1], want)
+    say(f"    paged decode_multi: max err {err:.3e} (bound {bound:.3e})")
+    assert ok
+
+
+def test_paged_ragged_rows():
+    """Ragged appends and decodes on a paged cache equal those on a contiguous cache, and each
+    row matches the oracle's one-row cache."""
+    say("case: paged ragged rows")
+    rng = np.random.default_rng(730)
+    B, H, D = 3, 2, 64
+    ocfg = O.CacheConfig(B, H, 2 * H, D, 1500, 2, 40, "fp16", "asym", (3, 4), (2, 3))
+    n_max = 700
+    k = workloads.random_raw16(rng, (B, H, 2 * n_max, D), "fp16")
+    v = workloads.random_raw16(rng, (B, H, 2 * n_max, D), "fp16")
+    q = workloads.random_raw16(rng, (B, 2 * H, D), "fp16")
+    ref = kvq.KVCache(lib_cfg(kvq, ocfg), device=DEV)
+    paged, _ = _paged_twin(ocfg, rng)
+    lens = [0] * B
+    for n_new in ([700, 3, 650], [1, 697, 0]):
+        for c in (ref, paged):
+            kk = np.stack([k[b, :, lens[b]:lens[b] + n_max] for b in range(B)])
+            vv = np.stack([v[b, :, lens[b]:lens[b] + n_max] for b in range(B)])
+            kvq.append_ragged(c, lens, n_new, to_dev(np.ascontiguousarray(kk)), to_dev(np.ascontiguousarray(vv)))
+        lens = [l + n for l, n in zip(lens, n_new)]
+    torch.cuda.synchronize()
+    kvq.cache_check(ref)
+    kvq.cache_check(paged)
+    outs = []
+    for c in (ref, paged):
+        out = torch.empty((B, 2 * H, D), dtype=torch.float32, device=DEV)
+        ws = torch.zeros(kvq.decode_workspace_bytes(c, 4), dtype=torch.uint8, device=DEV)
+        kvq.decode_ragged(c, lens, to_dev(q), out, 4, ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy().astype(np.float64))
+    assert np.array_equal(outs[0], outs[1])
+    for b in range(B):
+        c1 = O.CacheConfig(1, H, 2 * H, D, 1500, 2, 40, "fp16", "asym", (3, 4), (2, 3))
+        oc = O.build_cache(k[b:b + 1, :, :lens[b]], v[b:b + 1, :, :lens[b]], c1)
+        ok, err, bound = within_tol(outs[1][b:b + 1], O.decode(oc, q[b:b + 1]))
+        say(f"    paged ragged row {b} ({lens[b]} tokens): max err {err:.3e} (bound {bound:.3e})")
+        assert ok

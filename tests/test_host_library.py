@@ -26,7 +26,7 @@ def _header_functions():
 
 def test_library_exports_every_declared_function():
     names = _header_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     assert sorted(kvq.EXPORTS) == names
     L = ctypes.CDLL(kvq.lib_path())
     for n in names:
@@ -218,3 +218,35 @@ def test_paged_cache_sizes_and_checks():
     h = kvq._Cache()
     assert kvq.lib().kvq_cache_init_paged(ctypes.byref(h), ctypes.byref(cfg), 10, None, n1, None) == -1
     assert kvq.lib().kvq_cache_map_pages(ctypes.byref(h), 0, 0, 1, None, None) == -1
+
+
+def test_allocation_margin_matches_oracle_and_flags_near_ties():
+    rng = np.random.default_rng(23)
+    for trial in range(300):
+        n = int(rng.integers(2, 30))
+        b_lo, b_hi = [(2, 4), (2, 8), (3, 6)][trial % 3]
+        total = int(rng.integers(n * b_lo, n * b_hi + 1))
+        a, bt, w = _rand_model(rng, n)
+        cap = trial % 5 == 0
+        bits, _ = kvq.allocate_bits(a, bt, w, total, b_lo, b_hi, cap=cap)
+        m = kvq.allocation_margin(a, bt, w, bits, b_lo, b_hi, cap=cap)
+        want = O.allocation_margin(a, bt, w, bits, b_lo, b_hi, cap=cap)
+        assert m == want or (np.isinf(m) and np.isinf(want)), (trial, m, want)
+        assert m >= 0.0
+        if 1e-9 < m < np.inf:
+            # a relative perturbation far below the margin cannot change the allocation
+            a2 = [x * (1 + 1e-13) if i % 2 else x for i, x in enumerate(a)]
+            assert kvq.allocate_bits(a2, bt, w, total, b_lo, b_hi, cap=cap)[0] == bits
+    # a near tie: head 1's marginal gain sits 1e-14 relative above head 0's, so the one spare
+    # bit goes to head 1, the margin is about 1e-14, and a 1e-13 change of alpha_1 flips it
+    a, bt, w = [1.0, 1.0 + 1e-14, 0.5], [4.0, 4.0, 4.0], [1.0, 1.0, 1.0]
+    bits, _ = kvq.allocate_bits(a, bt, w, 7, 2, 4)
+    assert bits == [2, 3, 2]
+    m = kvq.allocation_margin(a, bt, w, bits, 2, 4)
+    assert 0.0 < m < 1e-12
+    assert kvq.allocate_bits([1.0, 1.0 - 1e-13, 0.5], bt, w, 7, 2, 4)[0] == [3, 2, 2]
+    # an exact tie (identical heads) has margin 0; all heads at b_lo or at b_hi: +inf
+    assert kvq.allocation_margin([1.0] * 3, [4.0] * 3, [1.0] * 3, [3, 2, 2], 2, 4) == 0.0
+    assert kvq.allocation_margin([1.0] * 3, [4.0] * 3, [1.0] * 3, [2, 2, 2], 2, 4) == float("inf")
+    with pytest.raises(kvq.KvqError):
+        kvq.allocation_margin([1.0], [4.0], [1.0], [5], 2, 4)

@@ -298,3 +298,30 @@ def _group_err(g, bits, hyb):
         d = float(xi) - yi
         tot = tot + d * d
     return tot
+
+
+def test_allocation_margin_equals_log_ratio_of_objective_changes():
+    # the margin of a greedy allocation is ln(smallest objective increase from taking back one
+    # handed-out bit / largest objective decrease from handing out one more), both measured
+    # with the objective sum w a beta^-b itself (RateQuant page, section 3.3)
+    rng = np.random.default_rng(17)
+    for trial in range(200):
+        n = int(rng.integers(2, 7))
+        b_lo, b_hi = (2, 4) if trial % 2 else (2, 8)
+        total = int(rng.integers(n * b_lo + 1, n * b_hi))
+        a = list(rng.uniform(0.5, 2.0, n))
+        bt = list(rng.uniform(3.6, 5.3, n))
+        w = list(rng.lognormal(0.0, 1.0, n))
+        bits = O.allocate_greedy(a, bt, w, total, b_lo, b_hi)
+        base = O.objective(a, bt, w, bits)
+        up, down = [], []
+        for i in range(n):
+            if bits[i] > b_lo:
+                v = list(bits); v[i] -= 1
+                up.append(O.objective(a, bt, w, v) - base)
+            if bits[i] < b_hi:
+                v = list(bits); v[i] += 1
+                down.append(base - O.objective(a, bt, w, v))
+        m = O.allocation_margin(a, bt, w, bits, b_lo, b_hi)
+        assert m >= 0.0
+        assert abs(m - math.log(min(up) / max(down))) < 1e-6, (trial, m)
