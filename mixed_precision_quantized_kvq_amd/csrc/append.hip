@@ -3,7 +3,6 @@
 // Built with -ffp-contract=off: the quantizer must round exactly as quant_device.h states.
 #include <hip/hip_runtime.h>
 
-#include <algorithm>
 #include <type_traits>
 
 #include "code_plans.h"
@@ -12,8 +11,6 @@
 
 namespace kvq {
 namespace {
-
-constexpr int kFlushWgPerCu = 4;  // persistent flush workgroups per compute unit
 
 // Token counts of row b for this append (uniform, or the row's own when ragged).
 __device__ __forceinline__ RowAppend row_append(const AppendPlan& p, int b) {
@@ -42,264 +39,303 @@ __device__ __forceinline__ const uint16_t* token_row(const AppendPlan& p, int le
   return in + (size_t)(t - len0) * p.D;
 }
 
-__device__ __forceinline__ void load_row32(const uint16_t* src, int dtype, float (&x)[32]) {
-  const uint4* s4 = reinterpret_cast<const uint4*>(src);
+// Range check on raw 16-bit elements (two to a word): |x| <= 2^14 and not NaN is
+// (bits & 0x7FFF) <= the bits of 2^14, since non-negative values order like their patterns
+// and infinities and NaNs lie above every finite value.
+__device__ __forceinline__ bool raw_out_of_range(const uint32_t (&w)[16], int dtype) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const uint4 u = s4[v];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  for (int k = 1; k < 16; ++k) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[k] & 0x7FFF7FFFu));
+  const unsigned lim = dtype == KVQ_BF16 ? 0x4680u : 0x7400u;  // 16384 in bf16 / fp16
+  return max((unsigned)m.x, (unsigned)m.y) > lim;
+}
+// The same test on fp32 values (keys divided by their norms).
+__device__ __forceinline__ bool f32_out_of_range(const float (&x)[32]) {
+  uint32_t m = 0u;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[v * 8 + 2 * k] = widen16((uint16_t)(w[k] & 0xFFFFu), dtype);
-      x[v * 8 + 2 * k + 1] = widen16((uint16_t)(w[k] >> 16), dtype);
-    }
+  for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+  return m > 0x46800000u;  // 16384.0f
+}
+
+__device__ __forceinline__ void widen_words(const uint32_t (&w)[16], int dtype, float (&x)[32]) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    x[2 * k] = widen16((uint16_t)(w[k] & 0xFFFFu), dtype);
+    x[2 * k + 1] = widen16((uint16_t)(w[k] >> 16), dtype);
   }
 }
 
-// Value stream of one decode lane: the 32 codes of virtual stream vg of lane (g4, n) of the
-// block's half of the tile (g4 = 2 * (block % 2) + jp). Stream position chan(s, k) holds the
-// code of token 16 kk + 8 jp + u of channel 16 nb + n, with chunk c = s / 2, nb = 2 vg + c / 2,
-// kk = c % 2, u = 4 (s % 2) + k: the order the decode kernel's value plan reads.
+// Codes (as patterns, quant_device.h) of a group: the asymmetric quantizer, or the hybrid
+// choice by float64 squared error (strictly lower wins, ties to asymmetric). The hybrid pass
+// scores both variants element by element without keeping their codes, then forms the
+// winner's codes; the symmetric form is the asymmetric one with zero 0 (x - 0 = x exactly).
 template <int B>
-__device__ __forceinline__ void pack_value_stream(const uint8_t (*codes)[36], int vg, int jp, int n,
-                                                  uint32_t* dst) {
-  uint64_t acc = 0;
-  int nbits = 0, w = 0;
+__device__ __forceinline__ GroupQ quantize_patterns(const float (&x)[32], bool hybrid, uint32_t (&cb)[32]) {
+  const GroupQ a = asym_params(x, B);
+  FastForm f = fast_form<false>(a);
+  if (hybrid) {
+    const GroupQ sq = sym_params(x, B);
+    const FastForm fs = fast_form<true>(sq);
+    const double sa = (double)a.s, za = (double)a.z, ss = (double)sq.s, zs = (double)sq.z;
+    double ea = 0.0, es = 0.0;
 #pragma unroll
-  for (int qpos = 0; qpos < kGroup; ++qpos) {
-    int s = 0, k = 0;
-#pragma unroll
-    for (int ss = 0; ss < 8; ++ss)
-#pragma unroll
-      for (int kk4 = 0; kk4 < 4; ++kk4)
-        if (VSlots<B>::chan(ss, kk4) == qpos) {
-          s = ss;
-          k = kk4;
-        }
-    const int c = s >> 1, nb = 2 * vg + (c >> 1), kk = c & 1, u = 4 * (s & 1) + k;
-    acc |= (uint64_t)codes[16 * nb + n][16 * kk + 8 * jp + u] << nbits;
-    nbits += B;
-    if (nbits >= 32) {
-      dst[w++] = (uint32_t)acc;
-      acc >>= 32;
-      nbits -= 32;
+    for (int i = 0; i < 32; ++i) {
+      const double xd = (double)x[i];
+      const double da = xd - __fma_rn((double)(code_pattern<false>(x[i], f) - kTwo23Bits), sa, za);
+      const double ds = xd - __fma_rn((double)(code_pattern<true>(x[i], fs) - kTwo23Bits), ss, zs);
+      const double qa = da * da, qs = ds * ds;
+      ea = ea + qa;
+      es = es + qs;
     }
+    if (es < ea) {
+      f = fs;
+      f.z = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) cb[i] = code_pattern<false>(x[i], f);
+      return sq;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) cb[i] = code_pattern<false>(x[i], f);
+  return a;
+}
+
+// Value streams. Decode lane (g4, n) of a tile (g4 = 2 * block + jp) holds D/32 streams of 32
+// codes; stream vg holds channels 16 nb + n for nb = 2 vg, 2 vg + 1 and, of each, the tokens
+// 16 kk + 8 jp + u (kk = 0, 1; u = 0..7) of the block, element e = 8 (2 (nb % 2) + kk) + u at
+// stream position vpos(e), the order in which the decode kernel's value plan reads them.
+template <int B>
+__host__ __device__ constexpr int vpos(int e) {
+  return VSlots<B>::chan(2 * (e >> 3) + ((e & 7) >> 2), e & 3);
+}
+// Bit of token k of a channel of parity P (nb % 2) in its stream for jp = (k >> 3) & 1.
+template <int B, int P>
+__host__ __device__ constexpr int vbit(int k) {
+  return vpos<B>(8 * (2 * P + (k >> 4)) + (k & 7)) * B;
+}
+// Widths whose parity-1 positions are the parity-0 ones plus 16: each channel then owns whole
+// words of its two streams (the first or second B/2 words).
+template <int B>
+__host__ __device__ constexpr bool split_halves() {
+  for (int e = 0; e < 16; ++e)
+    if (vpos<B>(e + 16) != vpos<B>(e) + 16 || vpos<B>(e) >= 16) return false;
+  return true;
+}
+template <int B, int P>
+struct HalfTotals {  // constant parts of the two streams' words once a channel's patterns are in
+  uint32_t v[2][B];
+  constexpr HalfTotals() : v() {
+    for (int k = 0; k < 32; ++k) {
+      const int bit = vbit<B, P>(k), wi = bit >> 5, off = bit & 31, jp = (k >> 3) & 1;
+      v[jp][wi] += kTwo23Bits << off;
+      if (off + B > 32) v[jp][wi + 1] += kTwo23Bits >> (32 - off);
+    }
+  }
+};
+// This channel's codes in its two streams (s0: jp = 0, s1: jp = 1), zeros elsewhere.
+template <int B, int P>
+__device__ __forceinline__ void pack_value_halves(const uint32_t (&cb)[32], uint32_t (&s0)[B], uint32_t (&s1)[B]) {
+  constexpr HalfTotals<B, P> t{};
+#pragma unroll
+  for (int w = 0; w < B; ++w) {
+    s0[w] = 0u - t.v[0][w];
+    s1[w] = 0u - t.v[1][w];
+  }
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    if ((k >> 3) & 1) add_at<B, B>(s1, vbit<B, P>(k), cb[k]);
+    else add_at<B, B>(s0, vbit<B, P>(k), cb[k]);
   }
 }
 
-// Flush of 32-token blocks leaving the recent window. One item is one block of one (row, KV
-// head); items are numbered ((row * H + head) * kmax + k), block k of the row's flushed ones
-// (kmax: the most any row flushes; a ragged row's items past its own count are skipped). The
-// grid is persistent: workgroup w takes items w, w + gridDim.x, ... With 2*D threads, the 32
-// input rows of keys and of values of an item (2 x 8 KB at D = 128) are staged in LDS; the
-// loads of the workgroup's next item are issued into registers before the current item is
-// quantized, and reach LDS after it, so each workgroup keeps a block's loads in flight while
-// it computes. From the stage, thread i < D quantizes key group i = (token tt of the block) *
-// (D/32) + channel group g, and thread D + c value channel c over the block's 32 tokens;
-// value codes go through LDS once more, to be written one (decode lane, stream) per thread in
-// the decode kernel's value order.
-// ASYM: the instantiation for asymmetric caches. The hybrid choice's float64 errors of both
-// variants need about twice the registers, so an asymmetric cache runs at twice the
-// occupancy without that code.
-template <bool ASYM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ASYM ? 4 : 2))) void append_flush_kernel(
-    const AppendPlan p, int kmax) {
+// Store of a value thread's codes. Thread xv = channel c = 16 nb + n sits in lane c % 64 of
+// its wavefront, so the other channel of its streams (parity 1 - P) is 16 lanes away, in the
+// paired 16-lane row.
+template <int B>
+__device__ __forceinline__ void store_value_streams(const uint32_t (&cb)[32], int c, int jj, int D, uint32_t* vc) {
+  const int n = c & 15, nb = c >> 4, P = nb & 1, vg = nb >> 1, nv = D / 32;
+  // words of stream vg of decode lane (2 jj + jp) * 16 + n
+  auto dst = [&](int jp) { return vc + ((size_t)(((2 * jj + jp) * 16 + n) * nv + vg)) * B; };
+  uint32_t s0[B], s1[B];
+  if constexpr (split_halves<B>()) {
+    pack_value_halves<B, 0>(cb, s0, s1);
+    uint32_t* d0 = dst(0) + P * (B / 2);
+    uint32_t* d1 = dst(1) + P * (B / 2);
+#pragma unroll
+    for (int w = 0; w < B / 2; ++w) {
+      d0[w] = s0[w];
+      d1[w] = s1[w];
+    }
+  } else {
+    if (P) pack_value_halves<B, 1>(cb, s0, s1);
+    else pack_value_halves<B, 0>(cb, s0, s1);
+    // or in the paired row's halves (16-lane rows 0 <-> 1, 2 <-> 3)
+#pragma unroll
+    for (int w = 0; w < B; ++w) {
+      const auto x0 = __builtin_amdgcn_permlane16_swap(s0[w], s0[w], false, false);
+      const auto x1 = __builtin_amdgcn_permlane16_swap(s1[w], s1[w], false, false);
+      s0[w] = x0[0] | x0[1];
+      s1[w] = x1[0] | x1[1];
+    }
+    uint32_t* d = dst(P);
+#pragma unroll
+    for (int w = 0; w < B; ++w) d[w] = P ? s1[w] : s0[w];
+  }
+}
+
+// Flush of 32-token blocks leaving the recent window: one workgroup per (block, KV head, row),
+// 2*D threads (D is a template parameter, so row strides are immediate load offsets). Thread i < D quantizes key group i = (token tt of the block) * (D/32) + channel
+// group g; thread D + c quantizes value channel c over the block's 32 tokens and writes its
+// codes straight into the two value streams that hold them (no LDS, no barrier).
+template <int D, bool ASYM>
+__global__ __launch_bounds__(2 * D) void append_flush_kernel(const AppendPlan p) {
+  constexpr int Gd = D / kGroup;
   const bool hybrid = !ASYM && p.hybrid != 0;
-  __shared__ alignas(16) uint16_t stage[2][kGroup][128];  // [keys | values][token of the block][channel]
-  __shared__ alignas(4) uint8_t vcodes[128][36];          // [channel][token of the block], rows padded to 36 bytes
-  const int D = p.D, Gd = D / kGroup;
-  const int n_items = p.B * p.H * kmax;
-  // Coordinates of an item; false for an item past its ragged row's flush count.
-  auto item = [&](int it, int& b, int& h, int& j, RowAppend& ra) {
-    const int k = it % kmax;
-    h = (it / kmax) % p.H;
-    b = it / (kmax * p.H);
-    ra = row_append(p, b);
-    j = ra.body0 / kGroup + k;
-    return k < (ra.body1 - ra.body0) / kGroup;
-  };
-  // Loads of an item's key and value rows: a block is 4 D 16-byte pieces per tensor, so
-  // thread t fetches pieces t and t + 2 D of each; a row still in the ring comes from the
-  // cache, a new one from the input.
-  uint4 rk0, rk1, rv0, rv1;
-  const int ltid = threadIdx.x;  // the loads' thread index (their addresses are cheap)
-  auto issue = [&](int it) {
-    int b, h, j;
-    RowAppend ra;
-    item(it, b, h, j, ra);
-    const uint64_t* off = p.off + ((size_t)b * p.H + h) * kRegions;
-    const size_t in_off = ((size_t)b * p.H + h) * p.n_new * D;
-    const uint16_t* kin = reinterpret_cast<const uint16_t*>(p.k_in) + in_off;
-    const uint16_t* vin = reinterpret_cast<const uint16_t*>(p.v_in) + in_off;
-    const int t0 = p.n_sink + j * kGroup + ltid / (D / 8), t1 = t0 + kGroup / 2, c8 = ltid % (D / 8);
-    rk0 = reinterpret_cast<const uint4*>(token_row(p, ra.len0, p.blob + off[RK], kin, t0))[c8];
-    rk1 = reinterpret_cast<const uint4*>(token_row(p, ra.len0, p.blob + off[RK], kin, t1))[c8];
-    rv0 = reinterpret_cast<const uint4*>(token_row(p, ra.len0, p.blob + off[RV], vin, t0))[c8];
-    rv1 = reinterpret_cast<const uint4*>(token_row(p, ra.len0, p.blob + off[RV], vin, t1))[c8];
-  };
-  auto to_lds = [&]() {
-    const int tt = ltid / (D / 8), c8 = ltid % (D / 8);
-    reinterpret_cast<uint4*>(&stage[0][tt][0])[c8] = rk0;
-    reinterpret_cast<uint4*>(&stage[0][tt + kGroup / 2][0])[c8] = rk1;
-    reinterpret_cast<uint4*>(&stage[1][tt][0])[c8] = rv0;
-    reinterpret_cast<uint4*>(&stage[1][tt + kGroup / 2][0])[c8] = rv1;
-  };
-  int it = blockIdx.x;
-  if (it >= n_items) return;  // uniform over the workgroup
-  issue(it);
-  to_lds();
-  __syncthreads();
-  while (true) {
-    const int nxt = it + (int)gridDim.x;
-    if (nxt < n_items) issue(nxt);  // in flight while this item is quantized
-    // The thread index, opaque to the compiler for this iteration: every address below derives
-    // from it, and hoisting those of all widths out of the loop would hold hundreds of
-    // registers across it.
-    int tid = threadIdx.x;
-    __asm__ __volatile__("" : "+v"(tid));
-    int b, h, j;
-    RowAppend ra;
-    const bool live = item(it, b, h, j, ra);
-    const uint64_t* off = p.off + ((size_t)b * p.H + h) * kRegions;
-    const bool is_key = tid < D;
-    const int bits = is_key ? p.k_bits[h] : p.v_bits[h];
-    const int vbits = p.v_bits[h];
-    const int tile = j >> 1, jj = j & 1;
-    // paged caches: the tile's page in this head's pools; an unmapped tile writes nothing and
-    // sets flag bit 1 (uniform over the workgroup, as are live and every branch on bits below)
-    int ptile = tile;
-    bool mapped = true;
-    if (live && p.pages) {
-      ptile = p.pages[(size_t)b * p.page_stride + tile];
-      if (ptile < 0 || ptile >= p.n_pages) {
-        if (tid == 0) atomicOr(p.range_flag, 2u);
-        mapped = false;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const RowAppend ra = row_append(p, b);
+  if ((int)blockIdx.x >= (ra.body1 - ra.body0) / kGroup) return;  // ragged: this row flushes fewer blocks
+  const int j = ra.body0 / kGroup + blockIdx.x;                    // body block index
+  // the region table of this (row, head), read into scalar registers before any store
+  const uint64_t* tab = p.off + ((size_t)b * p.H + h) * kRegions;
+  uint64_t off[kRegions];
+#pragma unroll
+  for (int r = 0; r < kRegions; ++r) off[r] = tab[r];
+  const size_t in_off = ((size_t)b * p.H + h) * p.n_new * D;
+  const uint16_t* kin = reinterpret_cast<const uint16_t*>(p.k_in) + in_off;
+  const uint16_t* vin = reinterpret_cast<const uint16_t*>(p.v_in) + in_off;
+  const int tid = threadIdx.x;
+  const bool is_key = tid < D;
+  const int bits = is_key ? p.k_bits[h] : p.v_bits[h];
+  const int tile = j >> 1, jj = j & 1;
+  // paged caches: the tile's page in this head's pools; an unmapped tile writes nothing and
+  // sets flag bit 1
+  int ptile = tile;
+  if (p.pages) {
+    ptile = p.pages[(size_t)b * p.page_stride + tile];
+    if (ptile < 0 || ptile >= p.n_pages) {
+      if (tid == 0) atomicOr(p.range_flag, 2u);
+      return;
+    }
+  }
+  const int pj = 2 * ptile + jj;  // the block's slot in the body region or pools
+  const int t0 = p.n_sink + j * kGroup;  // first token of the block
+  // the block's value rows: consecutive rows of the input or of the ring unless the block
+  // straddles the append or the ring's end (uniform)
+  const int slot0 = (t0 - p.n_sink) % (p.n_recent + kGroup);
+  const bool in_ring = t0 + kGroup <= ra.len0 && slot0 + kGroup <= p.n_recent + kGroup;
+  const bool in_input = t0 >= ra.len0;
+  const uint16_t* vrows = in_ring    ? reinterpret_cast<const uint16_t*>(p.blob + off[RV]) + (size_t)slot0 * D
+                          : in_input ? vin + (size_t)(t0 - ra.len0) * D
+                                     : nullptr;
+  if (bits == 16) {
+    // unquantized head: the block's rows are copied
+    if (is_key) {
+      const int tt = tid / Gd, g = tid % Gd;
+      const uint16_t* src = token_row(p, ra.len0, p.blob + off[RK], kin, t0 + tt) + g * kGroup;
+      uint4* dst = reinterpret_cast<uint4*>(p.blob + off[KC]) + ((size_t)(pj * kGroup + tt) * D + g * kGroup) / 8;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dst[v] = reinterpret_cast<const uint4*>(src)[v];
+    } else {
+      const int c = tid - D;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(p.blob + off[VC]);
+#pragma unroll
+      for (int k = 0; k < 32; ++k)
+        dst[(size_t)(pj * kGroup + k) * D + c] = token_row(p, ra.len0, p.blob + off[RV], vin, t0 + k)[c];
+    }
+    return;
+  }
+  // the group's 32 raw elements, two to a word
+  uint32_t raw[16];
+  if (is_key) {
+    const int tt = tid / Gd, g = tid % Gd;
+    const uint4* s4 = reinterpret_cast<const uint4*>(token_row(p, ra.len0, p.blob + off[RK], kin, t0 + tt) + g * kGroup);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint4 u = s4[v];
+      raw[4 * v] = u.x;
+      raw[4 * v + 1] = u.y;
+      raw[4 * v + 2] = u.z;
+      raw[4 * v + 3] = u.w;
+    }
+  } else {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    const int c = tid - D;
+    if (vrows) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const u16x2 e = {vrows[(2 * k) * D + c], vrows[(2 * k + 1) * D + c]};
+        raw[k] = __builtin_bit_cast(uint32_t, e);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const u16x2 e = {token_row(p, ra.len0, p.blob + off[RV], vin, t0 + 2 * k)[c],
+                         token_row(p, ra.len0, p.blob + off[RV], vin, t0 + 2 * k + 1)[c]};
+        raw[k] = __builtin_bit_cast(uint32_t, e);
       }
     }
-    const int pj = 2 * ptile + jj;  // the block's slot in the body region or pools
-    const bool work = live && mapped;
-    bool sym = false;
-    if (work && bits == 16) {
-      // unquantized head: the block's rows are copied
-      if (is_key) {
-        const int tt = tid / Gd, g = tid % Gd;
-        uint4* dst = reinterpret_cast<uint4*>(p.blob + off[KC]) + ((size_t)(pj * kGroup + tt) * D + g * kGroup) / 8;
+  }
+  float x[32];
+  widen_words(raw, p.dtype, x);
+  bool bad;
+  if (is_key && p.key_norm) {  // the group holds k_c / n_c (IEEE fp32 division)
+    const float* kn = reinterpret_cast<const float*>(p.blob + off[KN]) + (tid % Gd) * kGroup;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) dst[v] = reinterpret_cast<const uint4*>(&stage[0][tt][g * kGroup])[v];
-      } else {
-        const int c = tid - D;
-        uint16_t* dst = reinterpret_cast<uint16_t*>(p.blob + off[VC]);
+    for (int i = 0; i < 32; ++i) x[i] = x[i] / kn[i];
+    bad = f32_out_of_range(x);
+  } else {
+    bad = raw_out_of_range(raw, p.dtype);
+  }
+  if (bad) atomicOr(p.range_flag, 1u);
+  bool sym = false;
+  // the width is uniform over each wavefront (keys: wavefronts 0, 1; values: 2, 3)
+  auto group = [&](auto bc) {
+    constexpr int B = decltype(bc)::value;
+    uint32_t cb[32];
+    const GroupQ q = quantize_patterns<B>(x, hybrid, cb);
+    sym = q.sym;
+    const uint32_t meta = (uint32_t)q.s_bits | ((uint32_t)q.z_bits << 16);
+    if (is_key) {
+      uint32_t w[B];
+      pack_patterns<B>(cb, w);
+      const int tt = tid / Gd, g = tid % Gd;
+      const int W = Gd * B;  // words per token
+      const int t_in_tile = jj * kGroup + tt;
+      uint32_t* kc = reinterpret_cast<uint32_t*>(p.blob + off[KC]) + (size_t)ptile * kTile * W;
 #pragma unroll
-        for (int k = 0; k < 32; ++k) dst[(size_t)(pj * kGroup + k) * D + c] = stage[1][k][c];
+      for (int k = 0; k < B; ++k) {
+        const int wi = g * B + k;
+        const int qc = wi >> 2, nq = min(4, W - 4 * qc);
+        kc[256 * qc + t_in_tile * nq + (wi - 4 * qc)] = w[k];
       }
-    } else if (work) {
-      float x[32];
-      if (is_key) {
-        const int tt = tid / Gd, g = tid % Gd;
-        const uint4* s4 = reinterpret_cast<const uint4*>(&stage[0][tt][g * kGroup]);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint4 u = s4[v];
-          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            x[v * 8 + 2 * k] = widen16((uint16_t)(w[k] & 0xFFFFu), p.dtype);
-            x[v * 8 + 2 * k + 1] = widen16((uint16_t)(w[k] >> 16), p.dtype);
-          }
-        }
-        if (p.key_norm) {  // the group holds k_c / n_c (IEEE fp32 division)
-          const float* kn = reinterpret_cast<const float*>(p.blob + off[KN]) + g * kGroup;
-#pragma unroll
-          for (int i = 0; i < 32; ++i) x[i] = x[i] / kn[i];
-        }
-      } else {
-        const int c = tid - D;
-#pragma unroll
-        for (int k = 0; k < 32; ++k) x[k] = widen16(stage[1][k][c], p.dtype);
-      }
-      if (out_of_range(x)) atomicOr(p.range_flag, 1u);
-      // the width is uniform over each wavefront (keys: wavefronts 0, 1; values: 2, 3)
-      auto group = [&](auto bc) {
-        constexpr int B = decltype(bc)::value;
-        uint32_t w[B];
-        const GroupQ q = quantize_pack<B>(x, hybrid, w);
-        sym = q.sym;
-        const uint32_t meta = (uint32_t)q.s_bits | ((uint32_t)q.z_bits << 16);
-        if (is_key) {
-          const int tt = tid / Gd, g = tid % Gd;
-          const int W = Gd * B;  // words per token
-          const int t_in_tile = jj * kGroup + tt;
-          uint32_t* kc = reinterpret_cast<uint32_t*>(p.blob + off[KC]) + (size_t)ptile * kTile * W;
-#pragma unroll
-          for (int k = 0; k < B; ++k) {
-            const int wi = g * B + k;
-            const int qc = wi >> 2, nq = min(4, W - 4 * qc);
-            kc[256 * qc + t_in_tile * nq + (wi - 4 * qc)] = w[k];
-          }
-          reinterpret_cast<uint32_t*>(p.blob + off[KM])[(size_t)(pj * kGroup + tt) * Gd + g] = meta;
-        } else {
-          const int c = tid - D;
-          // codes of the 32 tokens, four to a word (the rows of vcodes are 36 bytes apart)
-#pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            uint32_t v4 = 0u;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const int pos = (4 * m + u) * B, wi = pos >> 5, o = pos & 31;
-              uint32_t cd = w[wi] >> o;
-              if (o + B > 32) cd |= w[wi + 1] << (32 - o);
-              v4 |= (cd & ((1u << B) - 1u)) << (8 * u);
-            }
-            reinterpret_cast<uint32_t*>(vcodes[c])[m] = v4;
-          }
-          // (s|z) of channel c = 16 nb + n for this block, at [tile][block][n][nb]
-          reinterpret_cast<uint32_t*>(p.blob + off[VM])[(size_t)ptile * 2 * D + jj * D + (c & 15) * (D / 16) + (c >> 4)] =
-              meta;
-        }
-      };
-      switch (bits) {
-        case 2: group(std::integral_constant<int, 2>{}); break;
-        case 3: group(std::integral_constant<int, 3>{}); break;
-        case 4: group(std::integral_constant<int, 4>{}); break;
-        case 5: group(std::integral_constant<int, 5>{}); break;
-        case 6: group(std::integral_constant<int, 6>{}); break;
-        case 7: group(std::integral_constant<int, 7>{}); break;
-        default: group(std::integral_constant<int, 8>{}); break;
-      }
-      if (hybrid) {
-        // flag bit i of this block's key (value) words = group i of thread i (D + i)
-        const unsigned long long m = __ballot(sym);
-        if ((tid & 63) == 0) {
-          uint32_t* fl = reinterpret_cast<uint32_t*>(p.blob + off[FL]) + (size_t)pj * 2 * Gd;
-          const int wbase = (is_key ? 0 : Gd) + ((is_key ? tid : tid - D) >> 5);
-          fl[wbase] = (uint32_t)m;
-          fl[wbase + 1] = (uint32_t)(m >> 32);
-        }
-      }
+      reinterpret_cast<uint32_t*>(p.blob + off[KM])[(size_t)(pj * kGroup + tt) * Gd + g] = meta;
+    } else {
+      const int c = tid - D;
+      store_value_streams<B>(cb, c, jj, D, reinterpret_cast<uint32_t*>(p.blob + off[VC]) + (size_t)ptile * 2 * D * B);
+      // (s|z) of channel c = 16 nb + n for this block, at [tile][block][n][nb]
+      reinterpret_cast<uint32_t*>(p.blob + off[VM])[(size_t)ptile * 2 * D + jj * D + (c & 15) * (D / 16) + (c >> 4)] =
+          meta;
     }
-    __syncthreads();  // vcodes complete; every read of the stage done
-    if (work && vbits != 16 && !is_key) {
-      // value streams of this block: 32 decode lanes (g4 = 2 jj + jp, n) x D/32 streams each
-      const int xv = tid - D, nv = D / 32;
-      const int lane_local = xv / nv, vg = xv % nv;
-      const int jp = lane_local >> 4, n = lane_local & 15;
-      const int lane = (2 * jj + jp) * 16 + n;
-      uint32_t* dst = reinterpret_cast<uint32_t*>(p.blob + off[VC]) + (size_t)ptile * 2 * D * vbits +
-                      ((size_t)lane * nv + vg) * vbits;
-      switch (vbits) {
-        case 2: pack_value_stream<2>(vcodes, vg, jp, n, dst); break;
-        case 3: pack_value_stream<3>(vcodes, vg, jp, n, dst); break;
-        case 4: pack_value_stream<4>(vcodes, vg, jp, n, dst); break;
-        case 5: pack_value_stream<5>(vcodes, vg, jp, n, dst); break;
-        case 6: pack_value_stream<6>(vcodes, vg, jp, n, dst); break;
-        case 7: pack_value_stream<7>(vcodes, vg, jp, n, dst); break;
-        default: pack_value_stream<8>(vcodes, vg, jp, n, dst); break;
-      }
+  };
+  switch (bits) {
+    case 2: group(std::integral_constant<int, 2>{}); break;
+    case 3: group(std::integral_constant<int, 3>{}); break;
+    case 4: group(std::integral_constant<int, 4>{}); break;
+    case 5: group(std::integral_constant<int, 5>{}); break;
+    case 6: group(std::integral_constant<int, 6>{}); break;
+    case 7: group(std::integral_constant<int, 7>{}); break;
+    default: group(std::integral_constant<int, 8>{}); break;
+  }
+  if (hybrid) {
+    // flag bit i of this block's key (value) words = group i of thread i (D + i)
+    const unsigned long long m = __ballot(sym);
+    if ((tid & 63) == 0) {
+      uint32_t* fl = reinterpret_cast<uint32_t*>(p.blob + off[FL]) + (size_t)pj * 2 * Gd;
+      const int wbase = (is_key ? 0 : Gd) + ((is_key ? tid : tid - D) >> 5);
+      fl[wbase] = (uint32_t)m;
+      fl[wbase + 1] = (uint32_t)(m >> 32);
     }
-    if (nxt >= n_items) break;
-    to_lds();         // the next item's rows, in flight since the top of this iteration
-    __syncthreads();  // vcodes free again; the stage holds the next item
-    it = nxt;
   }
 }
 
@@ -389,17 +425,15 @@ int launch_append_flush(const AppendPlan& p, void* stream) {
     nblk = max(nblk, (a.body1 - a.body0) / kGroup);
   }
   if (nblk <= 0) return (int)hipSuccess;
-  // persistent grid: a few workgroups per compute unit, each walking many items
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus < 1)
-    cus = 256;
-  const long long items = (long long)p.B * p.H * nblk;
-  const unsigned grid = (unsigned)std::min<long long>(items, (long long)kFlushWgPerCu * cus);
-  if (p.hybrid)
-    hipLaunchKernelGGL(append_flush_kernel<false>, dim3(grid), dim3(2 * p.D), 0, (hipStream_t)stream, p, nblk);
-  else
-    hipLaunchKernelGGL(append_flush_kernel<true>, dim3(grid), dim3(2 * p.D), 0, (hipStream_t)stream, p, nblk);
+  dim3 grid(nblk, p.H, p.B);
+  hipStream_t s = (hipStream_t)stream;
+  if (p.D == 128) {
+    if (p.hybrid) hipLaunchKernelGGL((append_flush_kernel<128, false>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((append_flush_kernel<128, true>), grid, dim3(256), 0, s, p);
+  } else {
+    if (p.hybrid) hipLaunchKernelGGL((append_flush_kernel<64, false>), grid, dim3(128), 0, s, p);
+    else hipLaunchKernelGGL((append_flush_kernel<64, true>), grid, dim3(128), 0, s, p);
+  }
   return (int)hipGetLastError();
 }
 

@@ -181,4 +181,86 @@ __device__ __forceinline__ void pack_group(const float (&x)[32], const GroupQ& q
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// The append kernel's forms of the same quantizer: identical codes, scales, zeros and
+// choices, in fewer instructions.
+//
+// Rounding by addition. With t = fl32(fl32(x - z) * r) (asymmetric) or fl32(x * r)
+// (symmetric), and M = 2^23 + a (a = 0, or 2^(b-1) for the symmetric offset), fl32(t + M) is
+// M + rint(t) whenever M + t lies in [2^23, 2^24): the spacing there is 1 and IEEE addition
+// rounds to the nearest integer with ties to the even one, which is rint's tie rule because M
+// is even. Its fp32 bit pattern is 0x4B000000 + a + rint(t), so the code plus 0x4B000000 comes
+// out of one addition, and the clamp of rint(t) to its range is an unsigned clamp of the
+// pattern (positive floats order like their patterns, so a sum that falls below 2^23 clamps
+// to the lowest code). |t| stays far below 2^22 for inputs within the range limit.
+constexpr uint32_t kTwo23Bits = 0x4B000000u;  // fp32 bit pattern of 2^23
+
+struct FastForm {
+  float r;          // 1 / s, or 0 when s == 0 (every t is 0: the zero level)
+  float z;          // the zero subtracted before the product (asymmetric only)
+  float m;          // 2^23 + a
+  uint32_t lo, hi;  // pattern range of the codes
+};
+
+template <bool SYM>
+__device__ __forceinline__ FastForm fast_form(const GroupQ& q) {
+  FastForm f;
+  f.r = q.zero ? 0.0f : q.r;
+  f.z = q.z;
+  f.m = 8388608.0f + (float)q.add;
+  f.lo = kTwo23Bits + (uint32_t)((int)q.lo + q.add);
+  f.hi = kTwo23Bits + (uint32_t)((int)q.hi + q.add);
+  return f;
+}
+
+// code + 0x4B000000 of element x (code_of's value)
+template <bool SYM>
+__device__ __forceinline__ uint32_t code_pattern(float x, const FastForm& f) {
+  const float t = SYM ? x * f.r : (x - f.z) * f.r;
+  const uint32_t u = __float_as_uint(t + f.m);
+  return min(max(u, f.lo), f.hi);
+}
+
+// The squared errors of group_sse from code patterns take c s + z as one fused operation:
+// c s is exact in float64 (an 8-bit integer times an fp16 value), so the fused sum rounds
+// once, as the separate product and sum do.
+
+// What the patterns' constant 0x4B000000 adds to word k when element i's pattern is added in
+// at stream bit i * B (mod 2^32; a code that crosses into the next word adds its top there).
+__host__ __device__ constexpr uint32_t magic_in_word(int B, int i, int k) {
+  const int pos = i * B, wi = pos >> 5, off = pos & 31;
+  uint32_t c = 0u;
+  if (wi == k) c += kTwo23Bits << off;
+  if (off + B > 32 && wi + 1 == k) c += kTwo23Bits >> (32 - off);
+  return c;
+}
+
+template <int B>
+struct MagicTotals {  // v[k]: the constant part of word k once all 32 patterns are added in
+  uint32_t v[B];
+  constexpr MagicTotals() : v() {
+    for (int k = 0; k < B; ++k)
+      for (int i = 0; i < 32; ++i) v[k] += magic_in_word(B, i, k);
+  }
+};
+
+// Adds pattern u at stream bit `bit` of w (bit fields do not overlap, so adding is or-ing up
+// to the constant parts, which the caller takes out once).
+template <int N, int B>
+__device__ __forceinline__ void add_at(uint32_t (&w)[N], int bit, uint32_t u) {
+  const int wi = bit >> 5, off = bit & 31;
+  w[wi] += u << off;
+  if (off + B > 32) w[wi + 1] += u >> (32 - off);
+}
+
+// The 32 codes packed at stream bits [i B, i B + B) of w (pack_group's words).
+template <int B>
+__device__ __forceinline__ void pack_patterns(const uint32_t (&cb)[32], uint32_t (&w)[B]) {
+  constexpr MagicTotals<B> mt{};
+#pragma unroll
+  for (int k = 0; k < B; ++k) w[k] = 0u - mt.v[k];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) add_at<B, B>(w, i * B, cb[i]);
+}
+
 }  // namespace kvq
