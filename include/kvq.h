@@ -207,6 +207,18 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q_dev, float
                                 int32_t n_splits, float scale, void* workspace_dev,
                                 size_t ws_bytes, void* stream);
 
+/* kvq_decode_attention without a workspace, for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid hipMalloc): the split
+ * partials go to a static device array of 4 MiB that the library holds on every GPU it runs
+ * on until the process ends (looked up once per device, on the first call there). Nothing is
+ * allocated or freed. A call whose partials, kvq_decode_workspace_bytes(cache, n_splits),
+ * exceed 4 MiB returns KVQ_ERR_ARG and enqueues nothing. Every call on one GPU uses that
+ * GPU's array: calls that overlap on one GPU (other streams, other threads) race and must be
+ * serialized by the caller. The array needs no initialization. Otherwise the same arguments,
+ * rules, kernels and results as kvq_decode_attention. */
+kvq_status kvq_decode_attention_noalloc(const kvq_cache* cache, const void* q_dev, float* out_dev,
+                                        int32_t n_splits, float scale, void* stream);
+
 /* The two launches of kvq_decode_attention, for callers that schedule or time them apart:
  * kvq_decode_splitk writes the n_splits partials (m, l, o) of every query head into the
  * workspace; kvq_decode_merge combines them into out_dev. Same arguments and rules as

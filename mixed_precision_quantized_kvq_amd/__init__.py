@@ -21,7 +21,7 @@ __all__ = [
     "decode_workspace_bytes", "decode_attention", "decode_splitk", "decode_merge", "decode_step",
     "decode_multi_workspace_bytes", "decode_multi", "append_ragged", "decode_ragged",
     "cache_check",
-    "region_offset", "last_error", "allocation_margin",
+    "region_offset", "last_error", "allocation_margin", "decode_attention_noalloc",
     "F16", "BF16", "QUANT_ASYM", "QUANT_HYBRID", "KEY_NORM", "AXIS_KEY", "AXIS_VALUE", "ALLOC_CAP_W",
     "EXPORTS",
 ]
@@ -43,7 +43,7 @@ EXPORTS = ("kvq_cache_bytes", "kvq_cache_init", "kvq_calibrate_workspace_bytes",
            "kvq_decode_attention", "kvq_decode_splitk", "kvq_decode_merge", "kvq_decode_step",
            "kvq_decode_multi_workspace_bytes", "kvq_decode_multi", "kvq_append_ragged", "kvq_decode_ragged",
            "kvq_cache_check", "kvq_cache_bytes_paged", "kvq_cache_init_paged", "kvq_cache_map_pages",
-           "kvq_region_offset", "kvq_allocation_margin", "kvq_last_error")
+           "kvq_region_offset", "kvq_allocation_margin", "kvq_decode_attention_noalloc", "kvq_last_error")
 
 
 class KvqError(RuntimeError):
@@ -116,6 +116,7 @@ def lib():
             "kvq_append": (I32, [KP, P, P, I32, P]),
             "kvq_decode_workspace_bytes": (SZ, [KP, I32]),
             "kvq_decode_attention": (I32, [KP, P, P, I32, ctypes.c_float, P, SZ, P]),
+            "kvq_decode_attention_noalloc": (I32, [KP, P, P, I32, ctypes.c_float, P]),
             "kvq_decode_splitk": (I32, [KP, P, I32, ctypes.c_float, P, SZ, P]),
             "kvq_decode_merge": (I32, [KP, P, I32, P, SZ, P]),
             "kvq_decode_step": (I32, [KP, P, P, I32, P, P, I32, ctypes.c_float, P, SZ, P]),
@@ -283,6 +284,17 @@ def decode_attention(cache: KVCache, q, out, n_splits: int, workspace, scale: fl
     _check(lib().kvq_decode_attention(ctypes.byref(cache.handle), _dptr(q), _dptr(out), int(n_splits),
                                       float(scale), _dptr(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream)))
+
+
+def decode_attention_noalloc(cache: KVCache, q, out, n_splits: int, scale: float = 0.0, stream=None):
+    """decode_attention with the split partials in the library's static device scratch (no
+    workspace argument; nothing is allocated)."""
+    import torch
+    c = cache.cfg
+    assert q.is_contiguous() and out.is_contiguous() and out.dtype == torch.float32
+    assert tuple(q.shape) == (c.batch, c.n_q_heads, c.head_dim) and tuple(out.shape) == tuple(q.shape)
+    _check(lib().kvq_decode_attention_noalloc(ctypes.byref(cache.handle), _dptr(q), _dptr(out), int(n_splits),
+                                              float(scale), _stream(stream)))
 
 
 def decode_multi_workspace_bytes(cache: KVCache, n_splits: int, n_qtok: int) -> int:

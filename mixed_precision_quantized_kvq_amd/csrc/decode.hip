@@ -31,6 +31,7 @@
 
 #include <math.h>
 
+#include <mutex>
 
 #include "code_plans.h"  // slot plans and code unpacking (shared with the append kernel)
 #include "kvq_internal.h"
@@ -1228,6 +1229,33 @@ int launch_decode_splitk(const DecodePlan& p, void* stream) {
       hipLaunchKernelGGL((decode_kernel<64, false, false>), grid, dim3(kThreads), 0, s, p);
   }
   return (int)hipGetLastError();
+}
+
+// Split partials of kvq_decode_attention_noalloc: a file-scope device array instead of a
+// caller workspace, for callers that cannot allocate. Every GPU the library runs on holds its
+// own copy, at its own address, until the process ends; host code reaches it only through the
+// address hipGetSymbolAddress returns for the current device.
+constexpr size_t kStaticScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+int static_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {  // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = kStaticScratchBytes;
+  return 0;
 }
 
 int launch_decode_merge(const DecodePlan& p, void* stream) {

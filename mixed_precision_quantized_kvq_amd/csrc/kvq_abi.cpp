@@ -523,6 +523,23 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q_dev, float
   return check_launch(launch_decode_merge(p, stream), "merge launch");
 }
 
+kvq_status kvq_decode_attention_noalloc(const kvq_cache* cache, const void* q_dev, float* out_dev,
+                                        int32_t n_splits, float scale, void* stream) {
+  if (!q_dev || !out_dev) return fail(KVQ_ERR_ARG, "NULL pointer");
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  const size_t need = kvq_decode_workspace_bytes(cache, n_splits);
+  if (need == 0) return fail(KVQ_ERR_ARG, last_error());
+  void* ws = nullptr;
+  size_t cap = 0;
+  const int e = static_scratch(&ws, &cap);
+  if (e != (int)hipSuccess) return hip_fail((hipError_t)e, "static decode scratch");
+  if (need > cap)
+    return fail(KVQ_ERR_ARG, "the split partials need " + std::to_string(need) + " bytes; the static scratch holds " +
+                                 std::to_string(cap) + " (use kvq_decode_attention with a workspace)");
+  return kvq_decode_attention(cache, q_dev, out_dev, n_splits, scale, ws, cap, stream);
+}
+
 size_t kvq_calibrate_workspace_bytes(int32_t n_heads, int32_t n_tokens, int32_t head_dim,
                                      int32_t b_lo, int32_t b_hi) {
   if (n_heads < 1 || n_tokens < 1 || head_dim < 32 || head_dim % kGroup || b_hi < b_lo) return 0;

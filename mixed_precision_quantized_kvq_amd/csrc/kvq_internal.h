@@ -167,5 +167,8 @@ struct DecodePlan {
 int launch_decode_splitk(const DecodePlan& p, void* stream);
 
 int launch_decode_merge(const DecodePlan& p, void* stream);
+// Device address and size of this device's static decode scratch (set up on first use per
+// device); returns a hipError_t as int.
+int static_scratch(void** ptr, size_t* bytes);
 
 }  // namespace kvq
