@@ -287,8 +287,8 @@ def other_configs():
     """The other full-size workloads, one GPU: split-K decode time of the 8k-token Llama-shaped
     layer, of the 128k-token context and of the 32k-token workload with per-channel key
     normalization (caches rotated so their reads come from HBM, launches back to back behind
-    a spin kernel, HIP events on the launch stream), decode + merge of one and of four query
-    tokens per row on the multi-head 7B-shaped layer, a ragged serving step (rows of 32767,
+    a spin kernel, HIP events on the launch stream), decode + merge of one and of several query
+    tokens per row on the multi-head 7B-shaped layer and on the 32k-token GQA workload, a ragged serving step (rows of 32767,
     28000, 20000 and 12000 tokens; host loop, append + decode + merge), and the ingest rate of the 16 x
     4096-token prefill (calibration, allocation, then one append of every token), with and
     without key normalization."""
@@ -381,47 +381,54 @@ def other_configs():
                                 "kv_tokens_heads_per_s": s.batch * s.n_kv * s.tokens / (us * 1e-6)}
     del caches, ws, q
     torch.cuda.empty_cache()
-    # multi-token decode on the multi-head 7B-shaped layer: the last 4 tokens of every row at
-    # once (4 query rows per KV head), against one query token (1 row per KV head)
-    w = workloads.make("mha7b_t8k")
-    s = w["spec"]
-    kb, vb = workload_bits(kvq, w)
-    cfg = kvq.Config.make(s.batch, s.n_kv, s.n_q, s.head_dim, s.tokens, s.n_sink, s.n_recent, s.dtype, s.quant,
-                          kb, vb)
-    kd = torch.from_numpy(w["k"].view(np.int16)).to(dev)
-    vd = torch.from_numpy(w["v"].view(np.int16)).to(dev)
-    caches = []
-    for _ in range(5):
-        c = kvq.KVCache(cfg, device=dev)
-        kvq.append(c, kd, vd)
-        caches.append(c)
-    del kd, vd
-    qm = torch.from_numpy(w["q_multi"].view(np.int16)).to(dev)
-    nbytes = decode_bytes(s, kb, vb, s.tokens, s.n_splits)
-    multi = {"k_bits": kb, "v_bits": vb, "n_splits": s.n_splits, "bytes_per_launch_q1": nbytes}
-    for Q in (1, 4):
-        q = qm[:, 4 - Q:].contiguous()
-        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
-        ws = torch.zeros(kvq.decode_multi_workspace_bytes(caches[0], s.n_splits, Q), dtype=torch.uint8, device=dev)
-        for i in range(10):
-            kvq.decode_multi(caches[i % 5], q, out, s.n_splits, ws, stream=stream)
-        t_us = []
-        for _ in range(4):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda._sleep(20_000_000)
-            e0.record(stream)
-            for i in range(50):
+    # multi-token decode (decode + merge launches): the last Q tokens of every row at once.
+    # The multi-head 7B-shaped layer has 1 query head per KV head (Q = 4: 4 query rows per KV
+    # head, the single-query kernel's tile); the 32k-token GQA workload has 4 (Q = 2, 4: 8 and
+    # 16 rows, the 16-row tile), against one query token per row
+    for name, qs in (("mha7b_t8k", (1, 4)), ("qwen8b_t32k", (1, 2, 4))):
+        w = workloads.make(name)
+        s = w["spec"]
+        kb, vb = workload_bits(kvq, w)
+        cfg = kvq.Config.make(s.batch, s.n_kv, s.n_q, s.head_dim, s.tokens, s.n_sink, s.n_recent, s.dtype, s.quant,
+                              kb, vb)
+        kd = torch.from_numpy(w["k"].view(np.int16)).to(dev)
+        vd = torch.from_numpy(w["v"].view(np.int16)).to(dev)
+        caches = []
+        for _ in range(5):
+            c = kvq.KVCache(cfg, device=dev)
+            kvq.append(c, kd, vd)
+            caches.append(c)
+        del kd, vd
+        qsrc = w["q_multi"] if "q_multi" in w else workloads.random_raw16(
+            np.random.default_rng(4242), (s.batch, 4, s.n_q, s.head_dim), s.dtype)
+        qm = torch.from_numpy(qsrc.view(np.int16)).to(dev)
+        nbytes = decode_bytes(s, kb, vb, s.tokens, s.n_splits)
+        multi = {"k_bits": kb, "v_bits": vb, "n_splits": s.n_splits, "query_heads_per_kv_head": s.n_q // s.n_kv,
+                 "bytes_per_launch_q1": nbytes}
+        for Q in qs:
+            q = qm[:, 4 - Q:].contiguous()
+            out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+            ws = torch.zeros(kvq.decode_multi_workspace_bytes(caches[0], s.n_splits, Q), dtype=torch.uint8,
+                             device=dev)
+            for i in range(10):
                 kvq.decode_multi(caches[i % 5], q, out, s.n_splits, ws, stream=stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            t_us.append(e0.elapsed_time(e1) * 1e3 / 50)
-        us = float(np.median(t_us))
-        multi[f"q{Q}_us"] = us
-        multi[f"q{Q}_query_tokens_per_s"] = s.batch * Q / (us * 1e-6)
-        multi[f"q{Q}_frac_of_8tbs"] = nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS
-    res["mha7b_t8k_multi_token"] = multi
-    del caches, qm
-    torch.cuda.empty_cache()
+            t_us = []
+            for _ in range(4):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda._sleep(20_000_000)
+                e0.record(stream)
+                for i in range(50):
+                    kvq.decode_multi(caches[i % 5], q, out, s.n_splits, ws, stream=stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t_us.append(e0.elapsed_time(e1) * 1e3 / 50)
+            us = float(np.median(t_us))
+            multi[f"q{Q}_us"] = us
+            multi[f"q{Q}_query_tokens_per_s"] = s.batch * Q / (us * 1e-6)
+            multi[f"q{Q}_frac_of_8tbs"] = nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS
+        res[name + "_multi_token"] = multi
+        del caches, qm
+        torch.cuda.empty_cache()
     # ragged serving step on the 32k-token workload: the four rows hold 32767, 28000, 20000 and
     # 12000 tokens; one step appends one token to every row and decodes one query per row
     w = workloads.make("qwen8b_t32k")

@@ -250,9 +250,9 @@ kvq_status kvq_decode_ragged(const kvq_cache* cache, const int32_t* row_len, con
  * speculative decode; the InnerQ Algorithm 1 structure per query token). q_dev:
  * [batch][n_qtok][n_q_heads][head_dim] 16-bit, out_dev: same shape fp32. Query token i of a
  * row is the (len - n_qtok + i)-th token and attends causally: to tokens 0 .. len - n_qtok + i.
- * The n_qtok x G query rows of a KV head share one pass over its cache, so they fill the
- * MFMA rows a single query leaves empty: n_qtok * (n_q_heads / n_kv_heads) <= 4, else
- * KVQ_ERR_UNSUPPORTED. The newest n_qtok - 1 tokens must still be in the 16-bit window
+ * The n_qtok x G query rows of a KV head share one pass over its cache: up to 4 rows run on the
+ * single-query kernel's 4-row MFMA tile, 5 to 16 rows (for instance 4 GQA heads x 4 tokens) on
+ * a 16-row tile; n_qtok * (n_q_heads / n_kv_heads) > 16 returns KVQ_ERR_UNSUPPORTED. The newest n_qtok - 1 tokens must still be in the 16-bit window
  * (true when n_recent >= n_qtok - 1), else KVQ_ERR_UNSUPPORTED. n_qtok == 1 is exactly
  * kvq_decode_attention. Workspace: kvq_decode_multi_workspace_bytes(cache, n_splits, n_qtok)
  * bytes; other arguments and rules as for kvq_decode_attention. */

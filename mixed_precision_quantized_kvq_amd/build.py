@@ -30,6 +30,7 @@ SOURCES = {
     "calib.hip": EXACT,
     # MFMA accumulators in ordinary VGPRs: no accumulator-register copies in the decode loop
     "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "decode_dense.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -309,8 +309,8 @@ size_t kvq_decode_multi_workspace_bytes(const kvq_cache* cache, int32_t n_splits
     set_error("n_splits must be in 1..256");
     return 0;
   }
-  if (n_qtok < 1 || n_qtok > kMaxQueryRows) {
-    set_error("n_qtok must be in 1..4");
+  if (n_qtok < 1 || n_qtok * (cache->cfg.n_q_heads / cache->cfg.n_kv_heads) > kMaxDenseRows) {
+    set_error("n_qtok must be >= 1 and n_qtok * (query heads per KV head) <= 16");
     return 0;
   }
   const kvq_config& c = cache->cfg;
@@ -496,8 +496,9 @@ kvq_status kvq_decode_multi(const kvq_cache* cache, const void* q_dev, int32_t n
   if (st != KVQ_OK) return st;
   const kvq_config& c = cache->cfg;
   if (n_qtok < 1) return fail(KVQ_ERR_ARG, "n_qtok must be >= 1");
-  if (n_qtok * (c.n_q_heads / c.n_kv_heads) > kMaxQueryRows)
-    return fail(KVQ_ERR_UNSUPPORTED, "n_qtok * (query heads per KV head) must be <= 4");
+  const int rows = n_qtok * (c.n_q_heads / c.n_kv_heads);
+  if (rows > kMaxDenseRows)
+    return fail(KVQ_ERR_UNSUPPORTED, "n_qtok * (query heads per KV head) must be <= 16");
   if (cache->len < n_qtok) return fail(KVQ_ERR_ARG, "the cache holds fewer tokens than n_qtok");
   DecodePlan p;
   st = decode_plan(cache, q_dev, out_dev, n_splits, scale, ws, ws_bytes, p, n_qtok);
@@ -506,7 +507,9 @@ kvq_status kvq_decode_multi(const kvq_cache* cache, const void* q_dev, int32_t n
   // not have been quantized into the body yet
   if (p.body > 0 && p.n_win < n_qtok - 1)
     return fail(KVQ_ERR_UNSUPPORTED, "n_qtok - 1 exceeds the tokens of the recent window");
-  st = check_launch(launch_decode_splitk(p, stream), "decode launch");
+  // up to 4 rows: the single-query kernel's 4-row tile; more: the 16-row tile
+  st = check_launch(rows <= kMaxQueryRows ? launch_decode_splitk(p, stream) : launch_decode_dense(p, stream),
+                    "decode launch");
   if (st != KVQ_OK) return st;
   return check_launch(launch_decode_merge(p, stream), "merge launch");
 }

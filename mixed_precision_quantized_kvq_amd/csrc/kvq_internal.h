@@ -20,6 +20,7 @@ constexpr int kTile = 64;         // body tokens per key tile (one wavefront, on
 #endif
 constexpr int kWinTile = KVQ_WIN_TILE;
 constexpr int kMaxQueryRows = 4;  // query rows per KV head in one decode launch (heads x tokens)
+constexpr int kMaxDenseRows = 16;  // the same for the multi-token launch with the 16-row tile
 constexpr int kMaxRaggedRows = 64;  // rows of a ragged call (per-row lengths travel as kernel arguments)
 constexpr int kRegions = 10;
 constexpr uint64_t kAlign = 256;  // every region starts on a 256-byte boundary
@@ -167,6 +168,9 @@ struct DecodePlan {
 int launch_decode_splitk(const DecodePlan& p, void* stream);
 
 int launch_decode_merge(const DecodePlan& p, void* stream);
+// Multi-token decode with up to kMaxDenseRows query rows per KV head: writes the split
+// partials, like launch_decode_splitk.
+int launch_decode_dense(const DecodePlan& p, void* stream);
 // Device address and size of this device's static decode scratch (set up on first use per
 // device); returns a hipError_t as int.
 int static_scratch(void** ptr, size_t* bytes);

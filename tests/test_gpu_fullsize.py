@@ -116,6 +116,35 @@ def test_full_size_multi_token():
         say(f"    row {b} head {h}: {Q} query tokens within tolerance")
 
 
+def test_full_size_multi_token_gqa():
+    # the 32k-token GQA workload: the last 4 tokens of every row decoded at once by its 4 query
+    # heads (16 rows per KV head, the 16-row tile), in the benchmark's launch configuration;
+    # sampled (row, KV head) slices against the oracle
+    name = "qwen8b_t32k"
+    say(f"case: full-size 4-token decode on {name}")
+    w = workloads.make(name)
+    s = w["spec"]
+    kb, vb, _ = _bits(w)
+    ocfg = oracle_cfg(w, kb, vb)
+    cache = kvq.KVCache(lib_cfg(kvq, ocfg), device=DEV)
+    kvq.append(cache, to_dev(w["k"]), to_dev(w["v"]))
+    Q = 4
+    qm = workloads.random_raw16(np.random.default_rng(4242), (s.batch, Q, s.n_q, s.head_dim), s.dtype)
+    out = torch.empty(qm.shape, dtype=torch.float32, device=DEV)
+    ws = torch.zeros(kvq.decode_multi_workspace_bytes(cache, s.n_splits, Q), dtype=torch.uint8, device=DEV)
+    kvq.decode_multi(cache, to_dev(qm), out, s.n_splits, ws)
+    got = out.cpu().numpy()
+    G = s.n_q // s.n_kv
+    B, H = s.batch, s.n_kv
+    for b, h in sorted({(0, 0), (B - 1, H - 1), (B // 2, H // 2)}):
+        oc1 = O.build_cache(w["k"][b:b + 1, h:h + 1], w["v"][b:b + 1, h:h + 1], head_slice_cfg(ocfg, h))
+        want = O.decode_multi(oc1, qm[b:b + 1, :, h * G:(h + 1) * G])[0]
+        for i in range(Q):
+            ok, err, bound = within_tol(got[b, i, h * G:(h + 1) * G], want[i])
+            assert ok, (b, h, i, err, bound)
+        say(f"    row {b} head {h}: {Q} query tokens x {G} heads within tolerance")
+
+
 def test_full_size_decode_steps():
     # the benchmark's step: prefill T - 1 tokens of the 32k workload, then one-token decode
     # steps (append + decode + merge in one call) up to and across the next block flush;

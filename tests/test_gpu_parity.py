@@ -604,10 +604,10 @@ def test_multi_token_decode_rejects():
     k = workloads.random_raw16(rng, (1, 2, 300, 64), "bf16")
     cache = gpu_cache(ocfg, k, k)
     ws = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)
-    q3 = torch.zeros((1, 3, 4, 64), dtype=torch.int16, device=DEV)
-    out = torch.zeros((1, 3, 4, 64), dtype=torch.float32, device=DEV)
-    with pytest.raises(kvq.KvqError) as e:  # 2 query heads per KV head x 3 tokens > 4 rows
-        kvq.decode_multi(cache, q3, out, 2, ws)
+    q9 = torch.zeros((1, 9, 4, 64), dtype=torch.int16, device=DEV)
+    out9 = torch.zeros((1, 9, 4, 64), dtype=torch.float32, device=DEV)
+    with pytest.raises(kvq.KvqError) as e:  # 2 query heads per KV head x 9 tokens > 16 rows
+        kvq.decode_multi(cache, q9, out9, 2, ws)
     assert e.value.status == -5
     # n_recent = 0: after a flush the window holds fewer than Q - 1 tokens
     ocfg1 = O.CacheConfig(1, 2, 2, 64, 400, 2, 0, "bf16", "asym", (2, 2), (2, 2))
@@ -617,6 +617,78 @@ def test_multi_token_decode_rejects():
     with pytest.raises(kvq.KvqError) as e:
         kvq.decode_multi(cache1, q4, out4, 2, ws)
     assert e.value.status == -5
+
+
+# The 16-row tile: 5 to 16 query rows per KV head (GQA heads x query tokens) in one pass.
+# Every width 2..8 and 16-bit sides on either side, windows only, several split counts.
+DENSE_CASES = [
+    # G, Q, D, T, dtype, quant, k_bits, v_bits
+    (4, 4, 128, 1333, "bf16", "hybrid", (3, 2, 4), (2, 3, 4)),
+    (4, 2, 128, 700, "fp16", "asym", (2, 4, 3), (4, 2, 2)),
+    (2, 3, 64, 300, "fp16", "hybrid", (3, 16, 2), (2, 4, 16)),
+    (1, 16, 128, 500, "bf16", "asym", (5, 6, 7), (8, 5, 6)),
+    (4, 3, 128, 900, "bf16", "hybrid", (8, 7, 16), (7, 16, 3)),
+    (4, 4, 64, 21, "fp16", "asym", (2, 3, 4), (4, 3, 2)),     # window tokens only
+    (2, 8, 128, 2100, "fp16", "hybrid", (16, 3, 2), (16, 2, 5)),
+]
+
+
+@pytest.mark.parametrize("G,Q,D,T,dtype,quant,kb,vb", DENSE_CASES,
+                         ids=[f"G{c[0]}Q{c[1]}D{c[2]}T{c[3]}-{c[5]}" for c in DENSE_CASES])
+def test_multi_token_decode_16_row_tile(G, Q, D, T, dtype, quant, kb, vb):
+    say(f"case: 16-row multi-token decode G={G} Q={Q} D={D} T={T} {dtype} {quant} K{kb} V{vb}")
+    assert 4 < G * Q <= 16
+    rng = np.random.default_rng(900 + 10 * G + Q + T)
+    ocfg = O.CacheConfig(2, 3, 3 * G, D, T + 8, 4, 40, dtype, quant, kb, vb)
+    k = workloads.random_raw16(rng, (2, 3, T, D), dtype, 2.0)
+    v = workloads.random_raw16(rng, (2, 3, T, D), dtype)
+    q = workloads.random_raw16(rng, (2, Q, 3 * G, D), dtype)
+    oc = O.build_cache(k, v, ocfg)
+    cache = gpu_cache(ocfg, k, v)
+    want = O.decode_multi(oc, q)
+    qd = to_dev(q)
+    for ns in (1, 3, 16):
+        out = torch.full((2, Q, 3 * G, D), float("nan"), dtype=torch.float32, device=DEV)
+        ws = torch.zeros(kvq.decode_multi_workspace_bytes(cache, ns, Q), dtype=torch.uint8, device=DEV)
+        kvq.decode_multi(cache, qd, out, ns, ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        worst = 0.0
+        for i in range(Q):  # each query token against its own output scale
+            ok, err, bound = within_tol(got[:, i], want[:, i])
+            worst = max(worst, err / bound)
+            assert ok, (ns, i, err, bound)
+        say(f"    n_splits={ns}: worst error / bound {worst:.3e}")
+
+
+def test_multi_token_decode_16_row_tile_key_norm_and_paged():
+    # key norms folded into all 16 rows; a paged twin gives bit-identical outputs
+    say("case: 16-row multi-token decode, key normalization, contiguous and paged")
+    rng = np.random.default_rng(930)
+    G, Q, T, D = 4, 4, 2500, 128
+    ocfg = O.CacheConfig(2, 2, 2 * G, D, T, 4, 40, "bf16", "hybrid", (3, 2), (2, 4), key_norm=True)
+    k = outlier_keys(rng, (2, 2, T, D), "bf16")
+    v = workloads.random_raw16(rng, (2, 2, T, D), "bf16")
+    q = workloads.random_raw16(rng, (2, Q, 2 * G, D), "bf16")
+    oc = O.build_cache(k, v, ocfg, norm_tokens=700)
+    cache = gpu_cache(ocfg, k, v, chunks=[700, T - 700])
+    paged, _ = _paged_twin(ocfg, rng)
+    for a, n in ((0, 700), (700, T - 700)):
+        kvq.append(paged, to_dev(k[:, :, a:a + n]), to_dev(v[:, :, a:a + n]))
+    torch.cuda.synchronize()
+    kvq.cache_check(paged)
+    want = O.decode_multi(oc, q)
+    outs = []
+    for c in (cache, paged):
+        out = torch.empty((2, Q, 2 * G, D), dtype=torch.float32, device=DEV)
+        ws = torch.zeros(kvq.decode_multi_workspace_bytes(c, 5, Q), dtype=torch.uint8, device=DEV)
+        kvq.decode_multi(c, to_dev(q), out, 5, ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    for i in range(Q):
+        ok, err, bound = within_tol(outs[0][:, i], want[:, i])
+        assert ok, (i, err, bound)
 
 
 # ------------------------------------------------------------------------------------------

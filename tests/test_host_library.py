@@ -170,16 +170,17 @@ def test_multi_and_ragged_host_checks():
     cfg = kvq.Config.make(2, 2, 4, 64, 100, 2, 8, "bf16", "asym", (2, 2), (2, 2))  # G = 2
     h = _fake_cache(cfg, 50)
     p = ctypes.c_void_p(4096)
-    # multi-token decode: G * Q = 2 * 3 > 4 rows
-    assert L.kvq_decode_multi(ctypes.byref(h), p, 3, p, 2, 0.0, p, 1 << 20, None) == -5
-    assert "<= 4" in kvq.last_error()
+    # multi-token decode: G * Q = 2 * 9 > 16 rows
+    assert L.kvq_decode_multi(ctypes.byref(h), p, 9, p, 2, 0.0, p, 1 << 20, None) == -5
+    assert "<= 16" in kvq.last_error()
     # more query tokens than cached tokens
     h.len = 1
     assert L.kvq_decode_multi(ctypes.byref(h), p, 2, p, 2, 0.0, p, 1 << 20, None) == -1
     h.len = 50
     # workspace sizes grow with the query tokens
     assert L.kvq_decode_multi_workspace_bytes(ctypes.byref(h), 4, 2) > L.kvq_decode_workspace_bytes(ctypes.byref(h), 4)
-    assert L.kvq_decode_multi_workspace_bytes(ctypes.byref(h), 4, 5) == 0
+    assert L.kvq_decode_multi_workspace_bytes(ctypes.byref(h), 4, 8) > 0
+    assert L.kvq_decode_multi_workspace_bytes(ctypes.byref(h), 4, 9) == 0
     # ragged append: n_new above the input slots, a row past the capacity, negative lengths
     assert L.kvq_append_ragged(ctypes.byref(h), i32([0, 0]), i32([5, 1]), p, p, 4, None) == -1
     assert L.kvq_append_ragged(ctypes.byref(h), i32([98, 0]), i32([4, 1]), p, p, 4, None) == -3
