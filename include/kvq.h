@@ -49,7 +49,7 @@ typedef enum {
   KVQ_ERR_RANGE = -4,       /* a quantized input was non-finite or |x| > 2^14 */
   KVQ_ERR_UNSUPPORTED = -5, /* a configuration this build does not implement */
   KVQ_ERR_DEVICE = -6,      /* a HIP call failed; kvq_last_error() has HIP's message */
-  KVQ_ERR_PAGE = -7         /* paged cache: an append reached a tile with no page mapped */
+  KVQ_ERR_PAGE = -7         /* paged cache: an append or decode reached a tile with no page mapped */
 } kvq_status;
 
 typedef enum { KVQ_F16 = 0, KVQ_BF16 = 1 } kvq_dtype;
@@ -111,10 +111,11 @@ kvq_status kvq_cache_init(kvq_cache* cache, const kvq_config* cfg, void* dev_mem
  * tile, so paged and contiguous caches hold the same codes and decode to the same outputs.
  * The page table (int32 [batch][page_stride], page_stride = the tiles of a row holding
  * `capacity` tokens) lives in the blob; kvq_cache_init_paged sets every entry to -1
- * (unmapped). Mapping a tile to a page already in use by another (row, tile) is the caller's
- * error; the library does not detect it. A flush into an unmapped tile writes nothing and sets
- * a sticky flag that kvq_cache_check reports as KVQ_ERR_PAGE; decode reads of an unmapped tile
- * stay inside the pools but return meaningless values. All other calls (append, ragged,
+ * (unmapped). kvq_cache_map_pages rejects one page given to two tiles of the same call;
+ * a page shared with a (row, tile) mapped by another call is the caller's error (the library
+ * keeps no host copy of the table). A flush into an unmapped tile writes nothing, and a decode
+ * that reads one gets meaningless values for it (the read stays inside the pools); both set a
+ * sticky flag that kvq_cache_check reports as KVQ_ERR_PAGE. All other calls (append, ragged,
  * multi-token, decode, step) take paged caches as they are.
  * Motivation: a fixed bit budget per token and head is what lets serving engines hand out
  * cache memory in fixed-size blocks (NOVA-KV page, "If this is right"); the page mechanics
@@ -130,7 +131,7 @@ kvq_status kvq_cache_init_paged(kvq_cache* cache, const kvq_config* cfg, int32_t
                                 size_t bytes, void* stream);
 
 /* Map tiles first_tile .. first_tile + n_tiles - 1 of `row` to pages[0 .. n_tiles - 1]
- * (host array; each entry in [0, n_pages), or -1 to unmap). Tile t holds body tokens
+ * (host array; each entry in [0, n_pages), or -1 to unmap; no page twice). Tile t holds body tokens
  * 64t .. 64t + 63 of the row, i.e. tokens n_sink + 64t .. of the sequence; a row holding T
  * tokens needs its first ceil(body(T) / 64) tiles mapped, body(T) as in the decode
  * description. Copies synchronously on `stream` (host order with earlier work on it). */
@@ -275,7 +276,7 @@ kvq_status kvq_decode_step(kvq_cache* cache, const void* k_dev, const void* v_de
                            void* workspace_dev, size_t ws_bytes, void* stream);
 
 /* Synchronize `stream`, read the sticky flags; KVQ_ERR_RANGE if an input was out of range,
- * else KVQ_ERR_PAGE if a paged cache's append reached an unmapped tile. */
+ * else KVQ_ERR_PAGE if a paged cache's append or decode reached an unmapped tile. */
 kvq_status kvq_cache_check(const kvq_cache* cache, void* stream);
 
 /* Byte offset, from the blob start, of region `region` (0..9: key codes, key meta, value

@@ -58,11 +58,17 @@ __device__ __forceinline__ bool f32_out_of_range(const float (&x)[32]) {
   return m > 0x46800000u;  // 16384.0f
 }
 
-__device__ __forceinline__ void widen_words(const uint32_t (&w)[16], int dtype, float (&x)[32]) {
+template <bool BF16>
+__device__ __forceinline__ void widen_words(const uint32_t (&w)[16], float (&x)[32]) {
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    x[2 * k] = widen16((uint16_t)(w[k] & 0xFFFFu), dtype);
-    x[2 * k + 1] = widen16((uint16_t)(w[k] >> 16), dtype);
+    if constexpr (BF16) {
+      x[2 * k] = __uint_as_float(w[k] << 16);
+      x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    } else {
+      x[2 * k] = widen16((uint16_t)(w[k] & 0xFFFFu), KVQ_F16);
+      x[2 * k + 1] = widen16((uint16_t)(w[k] >> 16), KVQ_F16);
+    }
   }
 }
 
@@ -276,8 +282,10 @@ __global__ __launch_bounds__(2 * D) void append_flush_kernel(const AppendPlan p)
       }
     }
   }
+  // the dtype is uniform: one widening per launch, not both and a select per element
   float x[32];
-  widen_words(raw, p.dtype, x);
+  if (p.dtype == KVQ_BF16) widen_words<true>(raw, x);
+  else widen_words<false>(raw, x);
   bool bad;
   if (is_key && p.key_norm) {  // the group holds k_c / n_c (IEEE fp32 division)
     const float* kn = reinterpret_cast<const float*>(p.blob + off[KN]) + (tid % Gd) * kGroup;

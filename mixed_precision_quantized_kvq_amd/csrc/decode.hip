@@ -1109,6 +1109,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
     if (lane == 0) sm.new_s[wave] = acc * p.scale_log2;
   }
+  if (p.pages && h == 0 && wave == kWaves - 1) {
+    // the tiles this workgroup read must be mapped: an unmapped one was read from a clamped
+    // page (in bounds, meaningless values) and is reported through the sticky flag, bit 1
+    const int32_t* row_pages = p.pages + (size_t)b * p.page_stride;
+    bool bad = false;
+    for (int t = t0 + lane; t < t1; t += 64) {
+      const int pg = row_pages[t];
+      bad |= pg < 0 || pg >= p.n_pages;
+    }
+    if (__ballot(bad) && lane == 0) atomicOr(p.flag, 2u);
+  }
   __syncthreads();
   const size_t rows = (size_t)p.B * p.Q * p.Hq;
   for (int idx = tid; idx < R * D; idx += kThreads) {

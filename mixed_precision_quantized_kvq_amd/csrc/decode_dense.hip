@@ -401,7 +401,8 @@ __device__ __forceinline__ void value_rows16(const DSmem<D>& sm, int wave, int l
 
 // NRG: row groups of 4 in use (rows past G Q hold a zero query and are not written out)
 template <int D, int NRG>
-__global__ __launch_bounds__(kDThreads) void decode_dense_kernel(const DecodePlan p) {
+// two wavefronts per SIMD (two workgroups per CU): the register budget is 256
+__global__ __launch_bounds__(kDThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_dense_kernel(const DecodePlan p) {
   __shared__ DSmem<D> sm;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -521,6 +522,11 @@ __global__ __launch_bounds__(kDThreads) void decode_dense_kernel(const DecodePla
   const uint16_t* kr16 = reinterpret_cast<const uint16_t*>(p.blob + off[KC]);
   const uint16_t* vr16 = reinterpret_cast<const uint16_t*>(p.blob + off[VC]);
   for (int t = t0 + wave; t < t1; t += kDW) {
+    // the lane index, opaque to the compiler for this iteration: the per-lane offsets of every
+    // width's loads derive from it, and hoisting those of all widths out of the loop would hold
+    // dozens of registers across it
+    int lane = threadIdx.x & 63;
+    __asm__ __volatile__("" : "+v"(lane));
     const int pg = page_of(t);
     const int n_valid = min(kTile, body - t * kTile);
     const bool valid = lane < n_valid;
@@ -580,6 +586,8 @@ __global__ __launch_bounds__(kDThreads) void decode_dense_kernel(const DecodePla
     const int n_chunks = (n_wtok + kTile - 1) / kTile;
     for (int w = 0; w < n_chunks; ++w) {
       if (p.n_splits - 1 - w % p.n_splits != split || (w / p.n_splits) % kDW != wave) continue;
+      int lane = threadIdx.x & 63;  // opaque per chunk, as in the body loop
+      __asm__ __volatile__("" : "+v"(lane));
       const int u0 = w * kTile, n_valid = min(kTile, n_wtok - u0);
       const int u = u0 + min(lane, n_valid - 1);
       const uint16_t* krow = u < nsl ? sk + (size_t)u * D : rk + (size_t)slot(u) * D;
@@ -626,6 +634,16 @@ __global__ __launch_bounds__(kDThreads) void decode_dense_kernel(const DecodePla
         if (lane == r) mr = st.m[r];
       sm.red_m[wave][lane] = mr;
     }
+  }
+  if (pages && h == 0 && wave == kDW - 1) {
+    // the tiles this workgroup read must be mapped (an unmapped one was read from a clamped
+    // page): reported through the sticky flag, bit 1
+    bool bad = false;
+    for (int t = t0 + lane; t < t1; t += 64) {
+      const int pg = pages[t];
+      bad |= pg < 0 || pg >= p.n_pages;
+    }
+    if (__ballot(bad) && lane == 0) atomicOr(p.flag, 2u);
   }
   __syncthreads();
   const size_t rows = (size_t)p.B * p.Q * p.Hq;

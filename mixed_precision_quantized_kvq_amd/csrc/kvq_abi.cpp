@@ -177,6 +177,13 @@ kvq_status kvq_cache_map_pages(const kvq_cache* cache, int32_t row, int32_t firs
   for (int i = 0; i < n_tiles; ++i)
     if (pages[i] < -1 || pages[i] >= cache->n_pages)
       return fail(KVQ_ERR_ARG, "page index out of range at " + std::to_string(i));
+  {  // one page for two tiles of this call would alias them
+    std::vector<int32_t> sorted(pages, pages + n_tiles);
+    std::sort(sorted.begin(), sorted.end());
+    for (int i = 1; i < n_tiles; ++i)
+      if (sorted[i] >= 0 && sorted[i] == sorted[i - 1])
+        return fail(KVQ_ERR_ARG, "page " + std::to_string(sorted[i]) + " is given to two tiles");
+  }
   uint64_t pt_off = 0;
   plan_layout(cache->cfg, nullptr, cache->n_pages, &pt_off);
   char* dst = static_cast<char*>(cache->dev) + pt_off + ((size_t)row * stride + first_tile) * 4;
@@ -346,6 +353,7 @@ kvq_status decode_plan(const kvq_cache* cache, const void* q_dev, float* out_dev
   p.blob = static_cast<const char*>(cache->dev);
   p.off = table_ptr(cache);
   set_pages(cache, p);
+  p.flag = flag_ptr(cache);
   p.q = q_dev;
   p.out = out_dev;
   const size_t parts = (size_t)n_splits;

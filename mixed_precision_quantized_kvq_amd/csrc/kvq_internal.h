@@ -143,6 +143,7 @@ struct DecodePlan {
   float* ws_ml;          // [P][B][Hq][2]
   const int32_t* pages;  // paged caches: as in AppendPlan (null for contiguous caches)
   int page_stride, n_pages;
+  uint32_t* flag;        // the cache's sticky flag: bit 1 is set when a tile read is unmapped
   int B, H, Hq, G, D, T, body, n_sink_live, n_win, n_sink_cfg, ring;
   int Q;                 // query tokens per row: the last Q cached tokens, attended causally
   int ring0;             // ring slot of the oldest live window token (body mod ring)

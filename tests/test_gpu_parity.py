@@ -896,6 +896,36 @@ def test_paged_unmapped_tile_is_flagged():
         cache.map_pages(0, 0, [8])
     with pytest.raises(kvq.KvqError, match="ERR_ARG"):
         cache.map_pages(0, (O.body_len(400, 2, 8) // 32 + 1) // 2, [0])
+    with pytest.raises(kvq.KvqError, match="ERR_ARG.*two tiles"):
+        cache.map_pages(0, 0, [5, 5])
+
+
+def test_paged_decode_of_an_unmapped_tile_is_flagged():
+    # every tile mapped and appended, then one unmapped: decode (single query and the 16-row
+    # multi-token tile) still reads in bounds, and the sticky flag reports the unmapped read
+    say("case: paged decode over an unmapped tile")
+    ocfg = O.CacheConfig(1, 2, 8, 128, 700, 4, 40, "bf16", "asym", (3, 2), (2, 3))
+    rng = np.random.default_rng(712)
+    T = 600
+    k = workloads.random_raw16(rng, (1, 2, T, 128), "bf16")
+    v = workloads.random_raw16(rng, (1, 2, T, 128), "bf16")
+    for multi in (False, True):
+        cache, table = _paged_twin(ocfg, rng)
+        kvq.append(cache, to_dev(k), to_dev(v))
+        q = workloads.random_raw16(rng, (1, 8, 128), "bf16")
+        gpu_decode(cache, q, 3)
+        kvq.cache_check(cache)  # all mapped: clean
+        cache.map_pages(0, 2, [-1])
+        if multi:
+            qm = workloads.random_raw16(rng, (1, 4, 8, 128), "bf16")
+            out = torch.empty((1, 4, 8, 128), dtype=torch.float32, device=DEV)
+            ws = torch.zeros(kvq.decode_multi_workspace_bytes(cache, 3, 4), dtype=torch.uint8, device=DEV)
+            kvq.decode_multi(cache, to_dev(qm), out, 3, ws)
+        else:
+            gpu_decode(cache, q, 3)
+        torch.cuda.synchronize()
+        with pytest.raises(kvq.KvqError, match="ERR_PAGE"):
+            kvq.cache_check(cache)
 
 
 def _paged_twin(ocfg, rng, extra_pages=9):
