@@ -44,6 +44,9 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxG = 4;
 constexpr float kMaskedScore = -1e30f;  // causally masked window score (log2 units)
 constexpr int kEp = 11;  // softmax weights enter the value MFMA as p * 2^(kEp - e)
+// The key zero-term operand carries 2^kZShift on top of the packed-key scale, so that its
+// fp16 lo half stays a normal number for the usual group sums (at most 2^8 in all)
+constexpr int kZShift = 12;
 // Lazy rescaling: the running max m moves only when a score exceeds it by more than kTau
 // (log2 units), so weights stay below 2^kTau and p * 2^kEp * 2^kTau fits fp16.
 constexpr float kTau = 4.0f;
@@ -116,16 +119,11 @@ __device__ __forceinline__ float wave_max(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// Sums over the four 16-lane rows of a, b, c, d at once: lane (r, n) of the result holds
-// a, c, b, d summed over the rows at lane n, for r = 0, 1, 2, 3 (two 32-lane swaps fold the
-// halves, one 16-lane swap folds the rows; all VALU, no LDS).
-__device__ __forceinline__ float sum4(float a, float b, float c, float d) {
+// Sums over the two 32-lane halves of a and b at once: the 16-lane rows of the result hold
+// a0 + a2, a1 + a3, b0 + b2, b1 + b3 (row r of x is xr; one 32-lane swap, all VALU).
+__device__ __forceinline__ float sum_halves(float a, float b) {
   const auto ab = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  const auto cd = __builtin_amdgcn_permlane32_swap(__float_as_uint(c), __float_as_uint(d), false, false);
-  const float z = __uint_as_float(ab[0]) + __uint_as_float(ab[1]);  // rows: a0+a2, a1+a3, b0+b2, b1+b3
-  const float w = __uint_as_float(cd[0]) + __uint_as_float(cd[1]);
-  const auto zw = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(w), false, false);
-  return __uint_as_float(zw[0]) + __uint_as_float(zw[1]);
+  return __uint_as_float(ab[0]) + __uint_as_float(ab[1]);
 }
 
 // LDS traffic of one wavefront is executed in issue order, so a wavefront reading back what
@@ -152,7 +150,9 @@ struct Smem {
   // (16-byte alignment lets operand reads use one ds_read_b64 with an immediate offset)
   alignas(16) uint32_t qA[kWaves][kMaxG][D / 2 + 4];  // key-MFMA A operand: fp16 q * 2^(Eq - e), slot order
   alignas(16) uint32_t qW[kWaves][kMaxG][D / 2 + 4];  // 16-bit-row A operand: q in the cache dtype
-  alignas(16) float qsum[kWaves][kMaxG][D / 32];      // sum of q over each key group, times the softmax scale
+  // key zero term operand: sum of q over each key group times 2^(Eq - 24 + kZShift), as fp16
+  // hi + lo halves ([hi/lo][query][group], groups past D/32 zero)
+  alignas(8) uint16_t qz[kWaves][2][kMaxG][4];
   alignas(16) uint32_t pw[kWaves][2][kMaxG][36];  // per wave: hi/lo, query, 2 blocks x 16 words (+4 pad)
   // packed-body weights per wave: [32-token block][hi/lo][query][token], fp16, rows padded to
   // 40 halves; plus 32 zero halves for the operand rows of the other block
@@ -172,10 +172,10 @@ struct WaveState {
   float m[kMaxG];          // running max of the scores (log2 units), uniform over the wave
   float l[kMaxG];          // weight sum of the 16-bit rows, uniform over the wave
   float o[kMaxG][D / 64];  // 16-bit rows: channel (D/64) lane + h
-  // packed body: lane (g4, n) holds channel 16 nb + n for its (block, hi/lo) = g4; the four
-  // lane groups are added at the end
-  float ob[D / 16][kMaxG];
-  float lb[kMaxG];
+  // packed body: lane (g4, n) holds channel 16 nb + n of queries 2 (g4 % 2) and 2 (g4 % 2) + 1
+  // over the tokens of block g4 / 2; the two blocks' lanes are added at the end
+  float ob[D / 16][2];
+  float lb[2];
 };
 
 // Softmax for one tile (lane = token): the weight of query i, scaled by pscl, is written to
@@ -196,10 +196,11 @@ __device__ __forceinline__ void softmax_tile(bool valid, const float (&sc)[kMaxG
       st.l[i] *= alpha;
 #pragma unroll
       for (int h = 0; h < D / 64; ++h) st.o[i][h] *= alpha;
-      if (kBody) {
-        st.lb[i] *= alpha;
+      if (kBody) {  // the lanes holding query i: query pair i / 2, slot i % 2
+        const float f = ((__lane_id() >> 4) & 1) == (i >> 1) ? alpha : 1.0f;
+        st.lb[i & 1] *= f;
 #pragma unroll
-        for (int nb = 0; nb < D / 16; ++nb) st.ob[nb][i] *= alpha;
+        for (int nb = 0; nb < D / 16; ++nb) st.ob[nb][i & 1] *= f;
       }
     }
     const float mn = st.m[i];
@@ -409,27 +410,35 @@ __device__ __forceinline__ void key_phase(const Smem<D>& sm, int wave, const KTi
       const u32x2 a = *reinterpret_cast<const u32x2*>(&sm.qA[wave][qi][(g * 8 + s) * 2]);
       acc[g] = mfma_f16(a, unpack_step<KB>(t.w, g * KB, s), acc[g]);
     }
-  // fp16 s, z straight into mixed-precision FMAs: sum_g s_g acc_g and sum_g z_g qsum_g
-  float t1[kMaxG], t2[kMaxG];
+  // sum_g z_g sum(q)_g 2^(Eq - 24 + kZShift) on the same MFMA (A = the rows' group sums as
+  // fp16 hi + lo, B = the token's four fp16 zeros: exact products), scaled back by 2^-kZShift,
+  // then sum_g s_g acc_g on top with the fp16 scales straight into mixed-precision FMAs; the
+  // score is kscale times the total
+  const u32x2 zb = u32x2{__builtin_amdgcn_perm(t.m[1], t.m[0], 0x07060302u),
+                         NG == 4 ? __builtin_amdgcn_perm(t.m[3], t.m[2], 0x07060302u) : 0u};
+  float4_t tz = mfma_f16(*reinterpret_cast<const u32x2*>(&sm.qz[wave][0][qi][0]), zb, float4_t{0.0f, 0.0f, 0.0f, 0.0f});
+  tz = mfma_f16(*reinterpret_cast<const u32x2*>(&sm.qz[wave][1][qi][0]), zb, tz);
+  float t1[kMaxG];
+#pragma unroll
+  for (int i = 0; i < kMaxG; ++i) t1[i] = tz[i] * (1.0f / (float)(1 << kZShift));
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    const float sg = h2f(t.m[g] & 0xFFFFu), zg = h2f(t.m[g] >> 16);
+    const float sg = h2f(t.m[g] & 0xFFFFu);
 #pragma unroll
-    for (int i = 0; i < kMaxG; ++i) {
-      t1[i] = g == 0 ? sg * acc[g][i] : __builtin_fmaf(sg, acc[g][i], t1[i]);
-      t2[i] = g == 0 ? zg * sm.qsum[wave][i][0] : __builtin_fmaf(zg, sm.qsum[wave][i][g], t2[i]);
-    }
+    for (int i = 0; i < kMaxG; ++i) t1[i] = __builtin_fmaf(sg, acc[g][i], t1[i]);
   }
 #pragma unroll
-  for (int i = 0; i < kMaxG; ++i) sc[i] = __builtin_fmaf(kscale, t1[i], t2[i]);
+  for (int i = 0; i < kMaxG; ++i) sc[i] = kscale * t1[i];
 }
 
-// P.V of one packed tile on the 16x16x32 MFMA. Rows m = (block, hi/lo, query) = 8 blk + 4 hl
-// + i; the 32 K of a step are 16 tokens of each block (tokens 16 kk + 0..15), the A row of a
-// block reading zeros for the other block's tokens; columns are 16 channels. Two steps (kk)
-// give D[m][n] = sum over the block's 32 tokens; the weight sums come from the same A with
-// the constant operand. Lane (g4, n) then holds the 4 queries of (block, hl) = g4 for channel
-// 16 nb + n and applies that block's scale and zero. nblk: valid 32-token blocks (1 or 2).
+// P.V of one packed tile on the 16x16x32 MFMA. Rows m = (block, query pair, query bit, hi/lo)
+// = 8 blk + 4 qp + 2 qb + hl for query i = 2 qp + qb; the 32 K of a step are 16 tokens of each
+// block (tokens 16 kk + 0..15), the A row of a block reading zeros for the other block's
+// tokens; columns are 16 channels. Two steps (kk) give D[m][n] = sum over the block's 32
+// tokens; the weight sums come from the same A with the constant operand. Lane (g4, n) then
+// holds the hi and lo rows of queries 2 (g4 % 2) + 0, 1 of block g4 / 2 for channel 16 nb + n:
+// it adds each pair and applies that block's scale and zero. nblk: valid 32-token blocks (1
+// or 2).
 template <int D, int VB>
 __device__ __forceinline__ void value_phase(const Smem<D>& sm, int wave, const VTile<D, VB>& t, int lane, int nblk,
                                             WaveState<D>& st) {
@@ -437,16 +446,15 @@ __device__ __forceinline__ void value_phase(const Smem<D>& sm, int wave, const V
   constexpr float kV = (float)(1 << (24 - kEp));   // code products carry 2^(kEp - 24)
   constexpr float kV1 = (float)(1 << (14 - kEp));  // weight sums carry 2^(kEp - 14)
   const int m = lane & 15, g4 = lane >> 4;
-  const uint16_t* asrc = (m >> 3) == (g4 >> 1) ? &sm.pv[wave][m >> 3][(m >> 2) & 1][m & 3][8 * (g4 & 1)] : sm.zero16;
+  const uint16_t* asrc = (m >> 3) == (g4 >> 1) ? &sm.pv[wave][m >> 3][m & 1][(m >> 1) & 3][8 * (g4 & 1)] : sm.zero16;
   const u32x4 a0 = *reinterpret_cast<const u32x4*>(asrc);
   const u32x4 a1 = *reinterpret_cast<const u32x4*>(asrc + 16);
   float4_t d1 = mfma_f16_k32(a0, ones_chunk<VB>(0), float4_t{0.0f, 0.0f, 0.0f, 0.0f});
   d1 = mfma_f16_k32(a1, ones_chunk<VB>(1), d1);
   // the body accumulators hold sum s D + z D1 2^-10 and sum D1; the code products carry
   // 2^(kEp - 24) and the weight sums 2^(kEp - 14), so ob * kV and lb * kV1 are the sums
-  float4_t d1s;
-#pragma unroll
-  for (int i = 0; i < kMaxG; ++i) d1s[i] = d1[i] * (kV1 / kV);
+  const float w0 = d1[0] + d1[1], w1 = d1[2] + d1[3];  // the lane's two queries, hi + lo
+  const float w0s = w0 * (kV1 / kV), w1s = w1 * (kV1 / kV);
   const bool live = (g4 >> 1) < nblk;  // the lane's block holds body tokens
   // all MFMAs first (the kk = 1 step of a column block is issued after every kk = 0 one, so no
   // MFMA waits for its accumulator), then the scale and zero of every column block
@@ -467,12 +475,11 @@ __device__ __forceinline__ void value_phase(const Smem<D>& sm, int wave, const V
   for (int nb = 0; nb < NB; ++nb) {
     const uint32_t mw = live ? t.m[nb] : 0u;
     const float sv = h2f(mw & 0xFFFFu), zv = h2f(mw >> 16);
-#pragma unroll
-    for (int i = 0; i < kMaxG; ++i)
-      st.ob[nb][i] = __builtin_fmaf(sv, d[nb][i], __builtin_fmaf(zv, d1s[i], st.ob[nb][i]));
+    st.ob[nb][0] = __builtin_fmaf(sv, d[nb][0] + d[nb][1], __builtin_fmaf(zv, w0s, st.ob[nb][0]));
+    st.ob[nb][1] = __builtin_fmaf(sv, d[nb][2] + d[nb][3], __builtin_fmaf(zv, w1s, st.ob[nb][1]));
   }
-#pragma unroll
-  for (int i = 0; i < kMaxG; ++i) st.lb[i] += d1[i];
+  st.lb[0] += w0;
+  st.lb[1] += w1;
 }
 
 // Factor of the softmax weight of body token tb (0..31 of its block): 2^(kEp - e) with e the
@@ -971,13 +978,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // a 32-channel group spans 32 / E aligned lanes
 #pragma unroll
     for (int o2 = 16 / E; o2 >= 1; o2 >>= 1) qs += __shfl_xor(qs, o2, 64);
-    if (c0 % 32 == 0) sm.qsum[wave][i0][c0 / 32] = qs * p.scale_log2;
     if (lane < 32) sm.zero16[lane] = 0;
     qmax = wave_max(qmax);
-    wave_lds_sync();
     int qe = 0;
     if (qmax > 0.0f) (void)frexpf(qmax, &qe);
-    return 15 - qe;
+    const int Eq = 15 - qe;
+    // the key zero-term operand: |sum of q| * 2^Eq <= 2^20, so the value is at most 2^8
+    if (c0 % 32 == 0) {
+      const float v = __builtin_ldexpf(qs, Eq - 24 + kZShift);
+      const uint32_t hi = f2h(v);
+      sm.qz[wave][0][i0][c0 / 32] = (uint16_t)hi;
+      sm.qz[wave][1][i0][c0 / 32] = (uint16_t)f2h(v - h2f(hi));
+      if constexpr (D / 32 < 4) {
+        sm.qz[wave][0][i0][c0 / 32 + 2] = 0;
+        sm.qz[wave][1][i0][c0 / 32 + 2] = 0;
+      }
+    }
+    wave_lds_sync();
+    return Eq;
   };
 
   WaveState<D> st;
@@ -985,11 +1003,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int i = 0; i < kMaxG; ++i) {
     st.m[i] = -INFINITY;
     st.l[i] = 0.0f;
-    st.lb[i] = 0.0f;
 #pragma unroll
     for (int hh = 0; hh < D / 64; ++hh) st.o[i][hh] = 0.0f;
+  }
 #pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) st.ob[nb][i] = 0.0f;
+  for (int k = 0; k < 2; ++k) {
+    st.lb[k] = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) st.ob[nb][k] = 0.0f;
   }
 
   // ---- this workgroup's work: body tiles [t0, t1) round-robin over the wavefronts, and the
@@ -1067,15 +1088,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 
   // ---- combine the wavefronts of this workgroup into one partial (m, l, o). The packed-body
-  // sums of the four lane groups (block, hi/lo) are added with lane swaps (sum4), after which
-  // lane (r, n) holds query qr of channels 16 nb + n; the 16-bit-row sums (lane = channel
-  // pair) are added on top in LDS by the wavefronts that have any.
+  // sums of the two blocks' lanes are added with one lane swap (sum_halves), after which lane
+  // (r, n) holds query qr of channels 16 nb + n; the 16-bit-row sums (lane = channel pair) are
+  // added on top in LDS by the wavefronts that have any.
   const int r4 = lane >> 4, n16 = lane & 15;
   const int qr = ((r4 & 1) << 1) | (r4 >> 1);
-  const float lbr = sum4(st.lb[0], st.lb[1], st.lb[2], st.lb[3]);
+  const float lbr = sum_halves(st.lb[0], st.lb[1]);
 #pragma unroll
   for (int nb = 0; nb < D / 16; ++nb) {
-    const float v = sum4(st.ob[nb][0], st.ob[nb][1], st.ob[nb][2], st.ob[nb][3]);
+    const float v = sum_halves(st.ob[nb][0], st.ob[nb][1]);
     sm.red_o[wave][qr][16 * nb + n16] = v * (float)(1 << (24 - kEp));
   }
   if (n16 == 0) {
