@@ -28,6 +28,7 @@
 // weights.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
+#include <type_traits>
 
 #include <math.h>
 
@@ -234,6 +235,40 @@ __device__ __forceinline__ void softmax_body(Smem<D>& sm, int wave, int lane, bo
   softmax_tile<D, true>(valid, sc, st, dst, kMaxG * 40, 40, pscl, false);
 }
 
+// Softmax of one packed tile for the fast loop, from the unscaled scores t1 (score = kscale *
+// t1): y = score - m comes out of one FMA and is tested against kTau directly, so the common
+// path costs one FMA, one compare and one exp per query. FULL: every token of the tile is in
+// the body (no validity masking).
+template <int D, bool FULL>
+__device__ __forceinline__ void softmax_body_rel(Smem<D>& sm, int wave, int lane, bool valid, const float (&t1)[kMaxG],
+                                                 float kscale, WaveState<D>& st, float pscl) {
+  uint16_t* wdst = &sm.pv[wave][lane >> 5][0][0][lane & 31];
+#pragma unroll
+  for (int i = 0; i < kMaxG; ++i) {
+    float y = __builtin_fmaf(kscale, t1[i], -st.m[i]);
+    if (!FULL && !valid) y = -INFINITY;
+    if (__ballot(y > kTau)) {  // rare after the first tile (m = -inf gives y = +inf): move m
+      const float x = (FULL || valid) ? kscale * t1[i] : -INFINITY;
+      const float mn = fmaxf(st.m[i], wave_max(x));
+      const float alpha = __builtin_amdgcn_exp2f(st.m[i] - mn);
+      st.m[i] = mn;
+      st.l[i] *= alpha;
+#pragma unroll
+      for (int h = 0; h < D / 64; ++h) st.o[i][h] *= alpha;
+      const float f = ((__lane_id() >> 4) & 1) == (i >> 1) ? alpha : 1.0f;  // lanes of query i
+      st.lb[i & 1] *= f;
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb) st.ob[nb][i & 1] *= f;
+      y = x - mn;
+    }
+    const float pw = __builtin_amdgcn_exp2f(y) * pscl;
+    const uint32_t hi = f2h(pw), lo = f2h(pw - h2f(hi));
+    wdst[i * 40] = (uint16_t)hi;
+    wdst[kMaxG * 40 + i * 40] = (uint16_t)lo;
+  }
+  wave_lds_sync();
+}
+
 // The fp16 key-MFMA A operand of a wavefront, in slot order: slot (g * 8 + s) * 4 + k of query
 // row i holds q_i of channel 32 g + chan(s, k) times 2^(Eq - exp(s, k)) (q means q * n with
 // key normalization), from the wavefront's packed-key query in LDS. Lane l writes slots l,
@@ -394,9 +429,10 @@ __device__ __forceinline__ void load_v(VTile<D, VB>& t, const BodySrc& src, int 
 }
 
 // Scores (log2 units) of the lane's token for the 4 query slots.
+// Unscaled: the score of query i is kscale * t1[i].
 template <int D, int KB>
-__device__ __forceinline__ void key_phase(const Smem<D>& sm, int wave, const KTile<D, KB>& t, int lane, float kscale,
-                                          float (&sc)[kMaxG]) {
+__device__ __forceinline__ void key_phase_raw(const Smem<D>& sm, int wave, const KTile<D, KB>& t, int lane,
+                                              float (&t1)[kMaxG]) {
   const int qi = lane & 3;
   constexpr int NG = D / 32;
   // the groups' MFMA chains are interleaved so that no MFMA waits for the one before it
@@ -412,13 +448,11 @@ __device__ __forceinline__ void key_phase(const Smem<D>& sm, int wave, const KTi
     }
   // sum_g z_g sum(q)_g 2^(Eq - 24 + kZShift) on the same MFMA (A = the rows' group sums as
   // fp16 hi + lo, B = the token's four fp16 zeros: exact products), scaled back by 2^-kZShift,
-  // then sum_g s_g acc_g on top with the fp16 scales straight into mixed-precision FMAs; the
-  // score is kscale times the total
+  // then sum_g s_g acc_g on top with the fp16 scales straight into mixed-precision FMAs
   const u32x2 zb = u32x2{__builtin_amdgcn_perm(t.m[1], t.m[0], 0x07060302u),
                          NG == 4 ? __builtin_amdgcn_perm(t.m[3], t.m[2], 0x07060302u) : 0u};
   float4_t tz = mfma_f16(*reinterpret_cast<const u32x2*>(&sm.qz[wave][0][qi][0]), zb, float4_t{0.0f, 0.0f, 0.0f, 0.0f});
   tz = mfma_f16(*reinterpret_cast<const u32x2*>(&sm.qz[wave][1][qi][0]), zb, tz);
-  float t1[kMaxG];
 #pragma unroll
   for (int i = 0; i < kMaxG; ++i) t1[i] = tz[i] * (1.0f / (float)(1 << kZShift));
 #pragma unroll
@@ -427,6 +461,12 @@ __device__ __forceinline__ void key_phase(const Smem<D>& sm, int wave, const KTi
 #pragma unroll
     for (int i = 0; i < kMaxG; ++i) t1[i] = __builtin_fmaf(sg, acc[g][i], t1[i]);
   }
+}
+template <int D, int KB>
+__device__ __forceinline__ void key_phase(const Smem<D>& sm, int wave, const KTile<D, KB>& t, int lane, float kscale,
+                                          float (&sc)[kMaxG]) {
+  float t1[kMaxG];
+  key_phase_raw<D, KB>(sm, wave, t, lane, t1);
 #pragma unroll
   for (int i = 0; i < kMaxG; ++i) sc[i] = kscale * t1[i];
 }
@@ -439,7 +479,7 @@ __device__ __forceinline__ void key_phase(const Smem<D>& sm, int wave, const KTi
 // holds the hi and lo rows of queries 2 (g4 % 2) + 0, 1 of block g4 / 2 for channel 16 nb + n:
 // it adds each pair and applies that block's scale and zero. nblk: valid 32-token blocks (1
 // or 2).
-template <int D, int VB>
+template <int D, int VB, bool FULL = false>
 __device__ __forceinline__ void value_phase(const Smem<D>& sm, int wave, const VTile<D, VB>& t, int lane, int nblk,
                                             WaveState<D>& st) {
   constexpr int NB = D / 16;
@@ -455,7 +495,7 @@ __device__ __forceinline__ void value_phase(const Smem<D>& sm, int wave, const V
   // 2^(kEp - 24) and the weight sums 2^(kEp - 14), so ob * kV and lb * kV1 are the sums
   const float w0 = d1[0] + d1[1], w1 = d1[2] + d1[3];  // the lane's two queries, hi + lo
   const float w0s = w0 * (kV1 / kV), w1s = w1 * (kV1 / kV);
-  const bool live = (g4 >> 1) < nblk;  // the lane's block holds body tokens
+  const bool live = FULL || (g4 >> 1) < nblk;  // the lane's block holds body tokens
   // all MFMAs first (the kk = 1 step of a column block is issued after every kk = 0 one, so no
   // MFMA waits for its accumulator), then the scale and zero of every column block
   float4_t d[NB];
@@ -784,23 +824,43 @@ __device__ __forceinline__ void body_loop(Smem<D>& sm, const DecodePlan& p, cons
   window(wt);
   if (!any) return;
   const float pscl = value_pscale<VB>(lane & 31);
-  auto step = [&](const KTile<D, KB>& kcur, const VTile<D, VB>& vcur) {
-    float sc[kMaxG];
-    key_phase<D, KB>(sm, wave, kcur, lane, kscale, sc);
-    softmax_body<D>(sm, wave, lane, tile * kTile + lane < body, sc, st, pscl);
-    value_phase<D, VB>(sm, wave, vcur, lane, min(2, (body - tile * kTile) / 32), st);
+  // this workgroup's tiles below tfull hold 64 body tokens; only the row's last tile can hold
+  // 32, and it is then the last tile of its wavefront: only that step masks tokens and blocks
+  const int tfull = min(t1, body / kTile);
+  auto step = [&](auto full, const KTile<D, KB>& kcur, const VTile<D, VB>& vcur) {
+    constexpr bool FULL = decltype(full)::value;
+    float kraw[kMaxG];
+    key_phase_raw<D, KB>(sm, wave, kcur, lane, kraw);
+    softmax_body_rel<D, FULL>(sm, wave, lane, FULL || tile * kTile + lane < body, kraw, kscale, st, pscl);
+    value_phase<D, VB, FULL>(sm, wave, vcur, lane, FULL ? 2 : min(2, (body - tile * kTile) / 32), st);
     wave_lds_sync();
     tile += kWaves;
   };
-  step(kt[0], vt[0]);
-  while (tile < t1) {
-    fetch(kt[0], vt[0], tile + kWaves);  // buffer 0 is free: the tile after this one
-    issue_barrier();
-    step(kt[1], vt[1]);
-    if (tile >= t1) break;
-    fetch(kt[1], vt[1], tile + kWaves);
-    issue_barrier();
-    step(kt[0], vt[0]);
+  using Full = std::integral_constant<bool, true>;
+  using Part = std::integral_constant<bool, false>;
+  // the loop runs the full tiles; a partial tile (the wavefront's last) is computed after it,
+  // from the buffer that then holds it (in1)
+  bool in1 = false;
+  if (tile < tfull) {
+    step(Full{}, kt[0], vt[0]);
+    in1 = true;
+    while (tile < tfull) {
+      fetch(kt[0], vt[0], tile + kWaves);  // buffer 0 is free: the tile after this one
+      issue_barrier();
+      step(Full{}, kt[1], vt[1]);
+      in1 = false;
+      if (tile >= tfull) break;
+      fetch(kt[1], vt[1], tile + kWaves);
+      issue_barrier();
+      step(Full{}, kt[0], vt[0]);
+      in1 = true;
+    }
+  }
+  if (tile < t1) {
+    if (in1)
+      step(Part{}, kt[1], vt[1]);
+    else
+      step(Part{}, kt[0], vt[0]);
   }
 }
 
