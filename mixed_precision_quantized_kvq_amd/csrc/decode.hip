@@ -243,11 +243,19 @@ template <int D, bool FULL>
 __device__ __forceinline__ void softmax_body_rel(Smem<D>& sm, int wave, int lane, bool valid, const float (&t1)[kMaxG],
                                                  float kscale, WaveState<D>& st, float pscl) {
   uint16_t* wdst = &sm.pv[wave][lane >> 5][0][0][lane & 31];
+  // all four queries first, then one test: the common path has a single branch, so the four
+  // score chains and exponentials can interleave
+  float y[kMaxG];
 #pragma unroll
   for (int i = 0; i < kMaxG; ++i) {
-    float y = __builtin_fmaf(kscale, t1[i], -st.m[i]);
-    if (!FULL && !valid) y = -INFINITY;
-    if (__ballot(y > kTau)) {  // rare after the first tile (m = -inf gives y = +inf): move m
+    y[i] = __builtin_fmaf(kscale, t1[i], -st.m[i]);
+    if (!FULL && !valid) y[i] = -INFINITY;
+  }
+  if (__ballot(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])) > kTau)) {
+    // rare after the first tile (m = -inf gives y = +inf): move m for the queries that need it
+#pragma unroll
+    for (int i = 0; i < kMaxG; ++i) {
+      if (!__ballot(y[i] > kTau)) continue;
       const float x = (FULL || valid) ? kscale * t1[i] : -INFINITY;
       const float mn = fmaxf(st.m[i], wave_max(x));
       const float alpha = __builtin_amdgcn_exp2f(st.m[i] - mn);
@@ -259,9 +267,12 @@ __device__ __forceinline__ void softmax_body_rel(Smem<D>& sm, int wave, int lane
       st.lb[i & 1] *= f;
 #pragma unroll
       for (int nb = 0; nb < D / 16; ++nb) st.ob[nb][i & 1] *= f;
-      y = x - mn;
+      y[i] = x - mn;
     }
-    const float pw = __builtin_amdgcn_exp2f(y) * pscl;
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxG; ++i) {
+    const float pw = __builtin_amdgcn_exp2f(y[i]) * pscl;
     const uint32_t hi = f2h(pw), lo = f2h(pw - h2f(hi));
     wdst[i * 40] = (uint16_t)hi;
     wdst[kMaxG * 40 + i * 40] = (uint16_t)lo;
@@ -799,8 +810,9 @@ __device__ __forceinline__ void body_loop(Smem<D>& sm, const DecodePlan& p, cons
   int tile = t0 + wave;
   const bool any = tile < t1;
   // Two register buffers, each always in the same registers: a buffer is refilled while the
-  // other one is computed. The wavefront's first two tiles are in flight before the query
-  // prologue runs. Every fetch is issued, so the compiler's load counts stay fixed and no
+  // other one is computed. The wavefront's first tile is in flight before the query prologue
+  // runs, the second one from its end (a smaller flood ahead of the query loads lets them
+  // return sooner). Every fetch is issued, so the compiler's load counts stay fixed and no
   // wait covers a load still needed in flight; a fetch past the wavefront's last tile goes
   // through zero-length descriptors and reads nothing.
   const BodySrc nul = body_src_empty(p, off);
@@ -816,9 +828,10 @@ __device__ __forceinline__ void body_loop(Smem<D>& sm, const DecodePlan& p, cons
   WinUnit<D> wt;
   window_issue(wt);
   fetch(kt[0], vt[0], tile);
-  fetch(kt[1], vt[1], tile + kWaves);
   issue_barrier();
   const int Eq = prologue();
+  fetch(kt[1], vt[1], tile + kWaves);
+  issue_barrier();
   build_key_operand<D, KB>(sm, wave, lane, Eq);
   const float kscale = __builtin_ldexpf(p.scale_log2, 24 - Eq);
   window(wt);
