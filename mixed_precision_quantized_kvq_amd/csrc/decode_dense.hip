@@ -134,10 +134,21 @@ template <int D, int NRG>
 __device__ __forceinline__ void softmax_dense(DSmem<D>& sm, int wave, int lane, bool valid, const float (&sc)[kR],
                                               DState<D>& st, float pscl, bool bf16w) {
   const int grp = lane >> 4;
+  // every row's score relative to its running max first, then one test for all rows: the
+  // common path has a single branch, and the rows' exponentials interleave (the per-row test
+  // sits in the rare path)
+  float y[4 * NRG];
+  float ymax = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 4 * NRG; ++r) {
-    const float x = valid ? sc[r] : -INFINITY;
-    if (__ballot(x > st.m[r] + kTauD)) {
+    y[r] = (valid ? sc[r] : -INFINITY) - st.m[r];
+    ymax = fmaxf(ymax, y[r]);
+  }
+  if (__ballot(ymax > kTauD)) {
+#pragma unroll
+    for (int r = 0; r < 4 * NRG; ++r) {
+      if (!__ballot(y[r] > kTauD)) continue;
+      const float x = valid ? sc[r] : -INFINITY;
       const float mn = fmaxf(st.m[r], wave_max(x));
       const float alpha = __builtin_amdgcn_exp2f(st.m[r] - mn);
       st.m[r] = mn;
@@ -145,8 +156,12 @@ __device__ __forceinline__ void softmax_dense(DSmem<D>& sm, int wave, int lane, 
 #pragma unroll
       for (int nb = 0; nb < D / 16; ++nb) st.o[nb][r & 3] *= a;
       st.l[r & 3] *= a;
+      y[r] = x - mn;
     }
-    const float p = __builtin_amdgcn_exp2f(x - st.m[r]) * pscl;
+  }
+#pragma unroll
+  for (int r = 0; r < 4 * NRG; ++r) {
+    const float p = __builtin_amdgcn_exp2f(y[r]) * pscl;
     uint32_t hi, lo;
     if (bf16w) {
       hi = f2bf(p);
