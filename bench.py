@@ -485,6 +485,9 @@ def other_configs():
         for _ in range(4):
             c = kvq.KVCache(cfg, device=dev)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            # the launches queue behind a spin kernel, so the events time the GPU's work and
+            # not the host's launch latency
+            torch.cuda._sleep(5_000_000)
             e0.record(stream)
             kvq.append(c, kd, vd, stream=stream)
             e1.record(stream)
