@@ -366,13 +366,21 @@ __global__ __launch_bounds__(kNormThreads) void key_norm_kernel(const AppendPlan
   float m[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   const RowAppend ra = row_append(p, b);
   if (p.ragged && !(ra.len0 == 0 && ra.n > 0)) return;  // norms come from a row's first append
-  for (int t = r; t < ra.n; t += parts) {
-    const uint4 u = k[(size_t)t * pieces];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  // eight tokens' loads in flight per thread (a token past the end re-reads the last one,
+  // which leaves the maxima unchanged)
+  constexpr int kBatch = 8;
+  for (int t0 = r; t0 < ra.n; t0 += kBatch * parts) {
+    uint4 u[kBatch];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m[2 * i] = fmaxf(m[2 * i], fabsf(widen16((uint16_t)(w[i] & 0xFFFFu), p.dtype)));
-      m[2 * i + 1] = fmaxf(m[2 * i + 1], fabsf(widen16((uint16_t)(w[i] >> 16), p.dtype)));
+    for (int v = 0; v < kBatch; ++v) u[v] = k[(size_t)min(t0 + v * parts, ra.n - 1) * pieces];
+#pragma unroll
+    for (int v = 0; v < kBatch; ++v) {
+      const uint32_t w[4] = {u[v].x, u[v].y, u[v].z, u[v].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m[2 * i] = fmaxf(m[2 * i], fabsf(widen16((uint16_t)(w[i] & 0xFFFFu), p.dtype)));
+        m[2 * i + 1] = fmaxf(m[2 * i + 1], fabsf(widen16((uint16_t)(w[i] >> 16), p.dtype)));
+      }
     }
   }
 #pragma unroll
