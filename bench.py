@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run only the launches the HBM-counter passes measure: a 256 MiB "
                          "elementwise copy (counter calibration), then 30 decode launches")
-    ap.add_argument("--probe", choices=("decode", "append", "calib"),
+    ap.add_argument("--probe", choices=("decode", "step", "append", "calib"),
                     help="run only one kind of launch for a profiler pass, after the same 256 MiB "
                          "copy: 30 split-K decode launches of --workload (rotating caches), 4 "
                          "prefill appends of prefill_t4k, or 3 whole-model calibrations (K and V)")
@@ -65,22 +65,26 @@ def _copy_probe():
 def probe(kind, workload):
     """The launches behind a committed profiler summary: the copy, then one kind of launch.
     decode: 30 split-K decode launches of `workload` over rotating full-size caches (5, or 3
-    for the 128k-token context); append: 4 appends of the whole 16 x 4096-token prefill into
-    fresh caches; calib: 3 calibrations + fits of the 288-pair whole-model set, K and V."""
+    for the 128k-token context); step: 64 decode steps (append one token + split-K decode +
+    merge) over the same rotating caches; append: 4 appends of the whole 16 x 4096-token
+    prefill into fresh caches; calib: 3 calibrations + fits of the 288-pair whole-model set, K
+    and V."""
     import torch
 
     import mixed_precision_quantized_kvq_amd as kvq
     import workloads
     dev = torch.device("cuda:0")
     _copy_probe()
-    if kind == "decode":
+    if kind in ("decode", "step"):
         w = workloads.make(workload)
         s = w["spec"]
         kb, vb = workload_bits(kvq, w)
-        cfg = kvq.Config.make(s.batch, s.n_kv, s.n_q, s.head_dim, s.tokens, s.n_sink, s.n_recent, s.dtype,
-                              s.quant, kb, vb)
-        kd = torch.from_numpy(w["k"].view(np.int16)).to(dev)
-        vd = torch.from_numpy(w["v"].view(np.int16)).to(dev)
+        # decode: full caches; step: one token short, with room for the appended ones
+        T0 = s.tokens if kind == "decode" else s.tokens - 1
+        cfg = kvq.Config.make(s.batch, s.n_kv, s.n_q, s.head_dim, T0 + (0 if kind == "decode" else 64), s.n_sink,
+                              s.n_recent, s.dtype, s.quant, kb, vb)
+        kd = torch.from_numpy(np.ascontiguousarray(w["k"][:, :, :T0]).view(np.int16)).to(dev)
+        vd = torch.from_numpy(np.ascontiguousarray(w["v"][:, :, :T0]).view(np.int16)).to(dev)
         n_inst = 3 if s.tokens > 65536 else 5
         caches = []
         for _ in range(n_inst):
@@ -89,9 +93,18 @@ def probe(kind, workload):
             caches.append(c)
         del kd, vd
         q = torch.from_numpy(w["q"].view(np.int16)).to(dev)
-        ws = torch.zeros(kvq.decode_workspace_bytes(caches[0], s.n_splits), dtype=torch.uint8, device=dev)
-        for i in range(30):
-            kvq.decode_splitk(caches[i % n_inst], q, s.n_splits, ws)
+        ws = torch.zeros(kvq.decode_workspace_bytes(caches[0], s.n_splits) * 2, dtype=torch.uint8, device=dev)
+        if kind == "decode":
+            for i in range(30):
+                kvq.decode_splitk(caches[i % n_inst], q, s.n_splits, ws)
+        else:
+            rng = np.random.default_rng(1)
+            shape = (s.batch, s.n_kv, 1, s.head_dim)
+            newk = torch.from_numpy(workloads.random_raw16(rng, shape, s.dtype).view(np.int16)).to(dev)
+            newv = torch.from_numpy(workloads.random_raw16(rng, shape, s.dtype).view(np.int16)).to(dev)
+            out = torch.empty((s.batch, s.n_q, s.head_dim), dtype=torch.float32, device=dev)
+            for i in range(64):
+                kvq.decode_step(caches[i % n_inst], newk, newv, q, out, s.n_splits, ws)
     elif kind == "append":
         w = workloads.make("prefill_t4k")
         s = w["spec"]
