@@ -234,7 +234,7 @@ kvq_status kvq_decode_merge(const kvq_cache* cache, float* out_dev, int32_t n_sp
  * started at different times). The caller keeps each row's length in a host array
  * row_len[batch] (all 0 after kvq_cache_init) and passes it to these calls, which do not use
  * or change cache->len; a cache is used either through these calls or through the uniform
- * ones. At most 64 rows (else KVQ_ERR_UNSUPPORTED).
+ * ones. Any number of rows: the library launches them in groups of 64 on the stream.
  * kvq_append_ragged: row b appends n_new[b] >= 0 tokens, the first n_new[b] of its n_max input
  * slots: k_dev, v_dev [batch][n_kv_heads][n_max][head_dim] 16-bit. Each row follows the rules
  * of kvq_append on its own (sink, ring, 32-token flushes; with KVQ_KEY_NORM the norms come

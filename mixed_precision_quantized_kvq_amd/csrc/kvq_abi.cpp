@@ -260,54 +260,66 @@ kvq_status kvq_append_ragged(const kvq_cache* cache, const int32_t* row_len, con
   if (st != KVQ_OK) return st;
   const kvq_config& c = cache->cfg;
   if (!row_len || !n_new) return fail(KVQ_ERR_ARG, "NULL row_len or n_new");
-  if (c.batch > kMaxRaggedRows) return fail(KVQ_ERR_UNSUPPORTED, "ragged calls take at most 64 rows");
   if (n_max < 0) return fail(KVQ_ERR_ARG, "n_max must be >= 0");
-  bool any = false, first = false;
+  bool any = false;
   for (int b = 0; b < c.batch; ++b) {
     if (row_len[b] < 0 || n_new[b] < 0 || n_new[b] > n_max) return fail(KVQ_ERR_ARG, "row length or n_new out of range");
     if ((int64_t)row_len[b] + n_new[b] > c.capacity) return fail(KVQ_ERR_CAPACITY, "append exceeds capacity");
     any |= n_new[b] > 0;
-    first |= row_len[b] == 0 && n_new[b] > 0;
   }
   if (!any) return KVQ_OK;
   if (!k_dev || !v_dev) return fail(KVQ_ERR_ARG, "NULL input");
   if (!aligned(k_dev, 16) || !aligned(v_dev, 16)) return fail(KVQ_ERR_ARG, "inputs must be 16-byte aligned");
-  AppendPlan p{};
-  p.k_in = k_dev;
-  p.v_in = v_dev;
-  p.blob = static_cast<char*>(cache->dev);
-  p.off = table_ptr(cache);
-  set_pages(cache, p);
-  p.range_flag = flag_ptr(cache);
-  p.B = c.batch;
-  p.H = c.n_kv_heads;
-  p.D = c.head_dim;
-  p.n_new = n_max;  // the input's token stride
-  p.n_sink = c.n_sink;
-  p.n_recent = c.n_recent;
-  p.dtype = c.dtype;
-  p.hybrid = quant_mode(c) == KVQ_QUANT_HYBRID;
-  p.key_norm = key_norm(c);
-  std::memcpy(p.k_bits, c.k_bits, sizeof(p.k_bits));
-  std::memcpy(p.v_bits, c.v_bits, sizeof(p.v_bits));
-  p.ragged = 1;
-  bool flush = false;
-  for (int b = 0; b < c.batch; ++b) {
-    p.row_len0[b] = row_len[b];
-    p.row_new[b] = n_new[b];
-    const RowAppend a = host_row_append(p, b);
-    flush |= a.body1 > a.body0;
-  }
-  // same order as kvq_append: norms of rows appended for the first time, flushes, window copies
-  if (p.key_norm && first) {
-    st = check_launch(launch_key_norms(p, stream), "key norm launch");
+  // The per-row counts travel in the launch plan (kMaxRaggedRows of them), so a larger batch
+  // runs as consecutive groups of rows: each group's plan sees its rows as rows 0.. through
+  // offset region table, page table and input pointers. Groups touch disjoint rows.
+  const size_t row_elems = (size_t)c.n_kv_heads * n_max * c.head_dim;  // 16-bit input elements per row
+  const uint64_t* tab = table_ptr(cache);
+  for (int r0 = 0; r0 < c.batch; r0 += kMaxRaggedRows) {
+    const int nr = std::min(kMaxRaggedRows, c.batch - r0);
+    AppendPlan p{};
+    p.k_in = static_cast<const uint16_t*>(k_dev) + (size_t)r0 * row_elems;
+    p.v_in = static_cast<const uint16_t*>(v_dev) + (size_t)r0 * row_elems;
+    p.blob = static_cast<char*>(cache->dev);
+    p.off = tab + (size_t)r0 * c.n_kv_heads * kRegions;
+    set_pages(cache, p);
+    if (p.pages) p.pages += (size_t)r0 * p.page_stride;
+    p.range_flag = flag_ptr(cache);
+    p.B = nr;
+    p.H = c.n_kv_heads;
+    p.D = c.head_dim;
+    p.n_new = n_max;  // the input's token stride
+    p.n_sink = c.n_sink;
+    p.n_recent = c.n_recent;
+    p.dtype = c.dtype;
+    p.hybrid = quant_mode(c) == KVQ_QUANT_HYBRID;
+    p.key_norm = key_norm(c);
+    std::memcpy(p.k_bits, c.k_bits, sizeof(p.k_bits));
+    std::memcpy(p.v_bits, c.v_bits, sizeof(p.v_bits));
+    p.ragged = 1;
+    bool flush = false, first_here = false, any_here = false;
+    for (int b = 0; b < nr; ++b) {
+      p.row_len0[b] = row_len[r0 + b];
+      p.row_new[b] = n_new[r0 + b];
+      const RowAppend a = host_row_append(p, b);
+      flush |= a.body1 > a.body0;
+      first_here |= a.len0 == 0 && a.n > 0;
+      any_here |= a.n > 0;
+    }
+    if (!any_here) continue;
+    // same order as kvq_append: norms of rows appended for the first time, flushes, window copies
+    if (p.key_norm && first_here) {
+      st = check_launch(launch_key_norms(p, stream), "key norm launch");
+      if (st != KVQ_OK) return st;
+    }
+    if (flush) {
+      st = check_launch(launch_append_flush(p, stream), "append flush launch");
+      if (st != KVQ_OK) return st;
+    }
+    st = check_launch(launch_append_window(p, stream), "append window launch");
     if (st != KVQ_OK) return st;
   }
-  if (flush) {
-    st = check_launch(launch_append_flush(p, stream), "append flush launch");
-    if (st != KVQ_OK) return st;
-  }
-  return check_launch(launch_append_window(p, stream), "append window launch");
+  return KVQ_OK;
 }
 
 size_t kvq_decode_multi_workspace_bytes(const kvq_cache* cache, int32_t n_splits, int32_t n_qtok) {
@@ -481,20 +493,36 @@ kvq_status kvq_decode_ragged(const kvq_cache* cache, const int32_t* row_len, con
   kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
   const kvq_config& c = cache->cfg;
-  if (c.batch > kMaxRaggedRows) return fail(KVQ_ERR_UNSUPPORTED, "ragged calls take at most 64 rows");
   for (int b = 0; b < c.batch; ++b)
     if (row_len[b] < 1 || row_len[b] > c.capacity) return fail(KVQ_ERR_ARG, "every row needs 1..capacity tokens");
   // plan on a copy whose len is a valid stand-in; the kernels take each row's own length
   kvq_cache any = *cache;
   any.len = row_len[0];
-  DecodePlan p;
-  st = decode_plan(&any, q_dev, out_dev, n_splits, scale, ws, ws_bytes, p);
+  DecodePlan full;
+  st = decode_plan(&any, q_dev, out_dev, n_splits, scale, ws, ws_bytes, full);
   if (st != KVQ_OK) return st;
-  p.ragged = 1;
-  for (int b = 0; b < c.batch; ++b) p.row_len[b] = row_len[b];
-  st = check_launch(launch_decode_splitk(p, stream), "decode launch");
-  if (st != KVQ_OK) return st;
-  return check_launch(launch_decode_merge(p, stream), "merge launch");
+  // The row lengths travel in the launch plan (kMaxRaggedRows of them), so a larger batch runs
+  // as consecutive groups of rows, each a split-K launch and a merge whose plan sees its rows
+  // as rows 0.. through offset region table, page table, q and out pointers. The groups reuse
+  // the front of the workspace one after the other on the stream.
+  for (int r0 = 0; r0 < c.batch; r0 += kMaxRaggedRows) {
+    const int nr = std::min(kMaxRaggedRows, c.batch - r0);
+    DecodePlan p = full;
+    p.ragged = 1;
+    p.B = nr;
+    p.off = full.off + (size_t)r0 * c.n_kv_heads * kRegions;
+    if (p.pages) p.pages += (size_t)r0 * p.page_stride;
+    p.q = static_cast<const uint16_t*>(q_dev) + (size_t)r0 * c.n_q_heads * c.head_dim;
+    p.out = out_dev + (size_t)r0 * c.n_q_heads * c.head_dim;
+    const size_t rows = (size_t)nr * c.n_q_heads;
+    p.ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(p.ws_o) + align_up((size_t)n_splits * rows * c.head_dim * 4));
+    for (int b = 0; b < nr; ++b) p.row_len[b] = row_len[r0 + b];
+    st = check_launch(launch_decode_splitk(p, stream), "decode launch");
+    if (st != KVQ_OK) return st;
+    st = check_launch(launch_decode_merge(p, stream), "merge launch");
+    if (st != KVQ_OK) return st;
+  }
+  return KVQ_OK;
 }
 
 kvq_status kvq_decode_multi(const kvq_cache* cache, const void* q_dev, int32_t n_qtok, float* out_dev,

@@ -811,9 +811,9 @@ def test_ragged_rejects():
     big = O.CacheConfig(65, 1, 1, 64, 100, 2, 8, "bf16", "asym", (2,), (2,))
     cache65 = kvq.KVCache(lib_cfg(kvq, big), device=DEV)
     k65 = torch.zeros((65, 1, 1, 64), dtype=torch.int16, device=DEV)
-    with pytest.raises(kvq.KvqError) as e:
-        kvq.append_ragged(cache65, [0] * 65, [1] * 65, k65, k65)
-    assert e.value.status == -5
+    with pytest.raises(kvq.KvqError) as e:  # the last row (in the second row group) past the capacity
+        kvq.append_ragged(cache65, [0] * 64 + [100], [1] * 65, k65, k65)
+    assert e.value.status == -3
 
 
 # ------------------------------------------------------------------------- paged caches ---
@@ -938,6 +938,55 @@ def _paged_twin(ocfg, rng, extra_pages=9):
     for b in range(ocfg.batch):
         cache.map_pages(b, 0, table[b].tolist())
     return cache, table
+
+
+def test_ragged_batch_beyond_one_row_group():
+    """Ragged calls on 150 rows (row groups of 64, 64 and 22 inside the library): contiguous and
+    paged caches agree bit for bit, the logical content of rows on either side of each group
+    boundary matches the oracle, and every row's decode matches the oracle's one-row cache."""
+    say("case: ragged batch of 150 rows (three row groups)")
+    rng = np.random.default_rng(740)
+    B, H, D = 150, 1, 64
+    ocfg = O.CacheConfig(B, H, 2 * H, D, 260, 2, 32, "fp16", "hybrid", (3,), (2,))
+    k = workloads.random_raw16(rng, (B, H, 260, D), "fp16", 2.0)
+    v = workloads.random_raw16(rng, (B, H, 260, D), "fp16")
+    q = workloads.random_raw16(rng, (B, 2 * H, D), "fp16")
+    ref = kvq.KVCache(lib_cfg(kvq, ocfg), device=DEV)
+    paged, _ = _paged_twin(ocfg, rng)
+    lens = [0] * B
+    first = [int(n) for n in rng.integers(1, 200, size=B)]
+    for n_new in (first, [int(n) for n in rng.integers(0, 40, size=B)]):
+        n_max = max(n_new)
+        kk = np.zeros((B, H, n_max, D), dtype=np.uint16)
+        vv = np.zeros((B, H, n_max, D), dtype=np.uint16)
+        for b in range(B):
+            kk[b, :, :n_new[b]] = k[b, :, lens[b]:lens[b] + n_new[b]]
+            vv[b, :, :n_new[b]] = v[b, :, lens[b]:lens[b] + n_new[b]]
+        for c in (ref, paged):
+            kvq.append_ragged(c, lens, n_new, to_dev(kk), to_dev(vv))
+        lens = [l + n for l, n in zip(lens, n_new)]
+    torch.cuda.synchronize()
+    kvq.cache_check(ref)
+    kvq.cache_check(paged)
+    for b in (0, 63, 64, 127, 128, 149):
+        oc = O.build_cache(k[b:b + 1, :, :lens[b]], v[b:b + 1, :, :lens[b]], _row_cfg(ocfg))
+        assert_regions_equal(ref, oc, rows=[0], map_bh=lambda _b, h, b=b: (b, h))
+    for ns in (1, 3):
+        outs = []
+        for c in (ref, paged):
+            out = torch.empty((B, 2 * H, D), dtype=torch.float32, device=DEV)
+            ws = torch.zeros(kvq.decode_workspace_bytes(c, ns), dtype=torch.uint8, device=DEV)
+            kvq.decode_ragged(c, lens, to_dev(q), out, ns, ws)
+            torch.cuda.synchronize()
+            outs.append(out.cpu().numpy().astype(np.float64))
+        assert np.array_equal(outs[0], outs[1])
+        worst = 0.0
+        for b in range(B):
+            oc = O.build_cache(k[b:b + 1, :, :lens[b]], v[b:b + 1, :, :lens[b]], _row_cfg(ocfg))
+            ok, err, bound = within_tol(outs[0][b:b + 1], O.decode(oc, q[b:b + 1]))
+            assert ok, (b, lens[b], ns, err, bound)
+            worst = max(worst, err / bound)
+        say(f"    {ns} splits: every row within tolerance (worst err/bound {worst:.3f})")
 
 
 def test_paged_long_rows_and_every_entry_point():

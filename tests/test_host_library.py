@@ -190,11 +190,13 @@ def test_multi_and_ragged_host_checks():
     # ragged decode: an empty row, a row past the capacity
     assert L.kvq_decode_ragged(ctypes.byref(h), i32([4, 0]), p, p, 2, 0.0, p, 1 << 20, None) == -1
     assert L.kvq_decode_ragged(ctypes.byref(h), i32([4, 101]), p, p, 2, 0.0, p, 1 << 20, None) == -1
-    # more than 64 rows
+    # more than 64 rows (run as row groups): every row is still checked before any launch
     big = kvq.Config.make(65, 1, 1, 64, 100, 2, 8, "bf16", "asym", (2,), (2,))
     hb = _fake_cache(big, 0)
-    assert L.kvq_append_ragged(ctypes.byref(hb), i32([0] * 65), i32([1] * 65), p, p, 1, None) == -5
-    assert L.kvq_decode_ragged(ctypes.byref(hb), i32([1] * 65), p, p, 2, 0.0, p, 1 << 20, None) == -5
+    assert L.kvq_append_ragged(ctypes.byref(hb), i32([0] * 64 + [99]), i32([1] * 64 + [2]), p, p, 2, None) == -3
+    assert L.kvq_append_ragged(ctypes.byref(hb), i32([0] * 65), i32([1] * 64 + [2]), p, p, 1, None) == -1
+    assert L.kvq_decode_ragged(ctypes.byref(hb), i32([1] * 64 + [0]), p, p, 2, 0.0, p, 1 << 20, None) == -1
+    assert L.kvq_append_ragged(ctypes.byref(hb), i32([3] * 65), i32([0] * 65), None, None, 0, None) == 0
 
 
 def test_paged_cache_sizes_and_checks():
