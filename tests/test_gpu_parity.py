@@ -940,14 +940,15 @@ def _paged_twin(ocfg, rng, extra_pages=9):
     return cache, table
 
 
-def test_ragged_batch_beyond_one_row_group():
+@pytest.mark.parametrize("key_norm", [False, True], ids=["plain", "key-norm"])
+def test_ragged_batch_beyond_one_row_group(key_norm):
     """Ragged calls on 150 rows (row groups of 64, 64 and 22 inside the library): contiguous and
     paged caches agree bit for bit, the logical content of rows on either side of each group
     boundary matches the oracle, and every row's decode matches the oracle's one-row cache."""
-    say("case: ragged batch of 150 rows (three row groups)")
-    rng = np.random.default_rng(740)
+    say(f"case: ragged batch of 150 rows (three row groups), key norm {key_norm}")
+    rng = np.random.default_rng(740 + key_norm)
     B, H, D = 150, 1, 64
-    ocfg = O.CacheConfig(B, H, 2 * H, D, 260, 2, 32, "fp16", "hybrid", (3,), (2,))
+    ocfg = O.CacheConfig(B, H, 2 * H, D, 260, 2, 32, "fp16", "hybrid", (3,), (2,), key_norm=key_norm)
     k = workloads.random_raw16(rng, (B, H, 260, D), "fp16", 2.0)
     v = workloads.random_raw16(rng, (B, H, 260, D), "fp16")
     q = workloads.random_raw16(rng, (B, 2 * H, D), "fp16")
@@ -969,7 +970,7 @@ def test_ragged_batch_beyond_one_row_group():
     kvq.cache_check(ref)
     kvq.cache_check(paged)
     for b in (0, 63, 64, 127, 128, 149):
-        oc = O.build_cache(k[b:b + 1, :, :lens[b]], v[b:b + 1, :, :lens[b]], _row_cfg(ocfg))
+        oc = O.build_cache(k[b:b + 1, :, :lens[b]], v[b:b + 1, :, :lens[b]], _row_cfg(ocfg), norm_tokens=first[b])
         assert_regions_equal(ref, oc, rows=[0], map_bh=lambda _b, h, b=b: (b, h))
     for ns in (1, 3):
         outs = []
@@ -982,7 +983,8 @@ def test_ragged_batch_beyond_one_row_group():
         assert np.array_equal(outs[0], outs[1])
         worst = 0.0
         for b in range(B):
-            oc = O.build_cache(k[b:b + 1, :, :lens[b]], v[b:b + 1, :, :lens[b]], _row_cfg(ocfg))
+            oc = O.build_cache(k[b:b + 1, :, :lens[b]], v[b:b + 1, :, :lens[b]], _row_cfg(ocfg),
+                               norm_tokens=first[b])
             ok, err, bound = within_tol(outs[0][b:b + 1], O.decode(oc, q[b:b + 1]))
             assert ok, (b, lens[b], ns, err, bound)
             worst = max(worst, err / bound)
