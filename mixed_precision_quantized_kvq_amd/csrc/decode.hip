@@ -1252,40 +1252,47 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // Log-sum-exp merge of the n_splits partials (m_j, l_j, o_j) of one output row:
 //   out = sum_j 2^(m_j - m*) o_j / sum_j 2^(m_j - m*) l_j,  m* = max_j m_j.
 // A separate launch: the kernel boundary makes every partial visible, so no workgroup has
-// to write back or invalidate the L2 caches. One thread per output element; the partials
-// are read in chunks of kMergeChunk whose loads are all in flight together, and combined
-// online (the running sums are rescaled when a chunk raises the maximum).
+// to write back or invalidate the L2 caches. T lanes per output element, T the smallest power
+// of two with T * kMergeChunk >= n_splits: each lane loads its (at most kMergeChunk) partials
+// all at once and combines them, and the T lane results are combined with lane shuffles, so
+// a launch waits for one round of loads whatever the split count.
 // ---------------------------------------------------------------------------------------
 constexpr int kMergeChunk = 16;
 
-template <int D>
+template <int D, int T>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const DecodePlan p) {
   const size_t rows = (size_t)p.B * p.Q * p.Hq;
-  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  if (p.new_k != nullptr && idx < (size_t)p.B * p.H * (D / 4)) {
+  const size_t gid = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (p.new_k != nullptr && gid < (size_t)p.B * p.H * (D / 4)) {
     // fused decode step: the appended token enters its ring slot once every read of the ring
     // by the decode launch is done (one 16-byte piece of its key or value row per thread)
-    const size_t bh = idx / (D / 4);
-    const int piece = (int)(idx % (D / 4));
+    const size_t bh = gid / (D / 4);
+    const int piece = (int)(gid % (D / 4));
     const bool kv = piece >= D / 8;
     const uint4 x = reinterpret_cast<const uint4*>(kv ? p.new_v : p.new_k)[bh * (D / 8) + piece % (D / 8)];
     const uint64_t ring_off = p.off[bh * kRegions + (kv ? RV : RK)];
     uint4* dst = reinterpret_cast<uint4*>(const_cast<char*>(p.blob) + ring_off + (size_t)p.new_slot * D * 2);
     dst[piece % (D / 8)] = x;
   }
-  if (idx >= rows * D) return;
+  // T adjacent lanes share output element idx; lane `sub` of them combines the partials
+  // sub, sub + T, sub + 2T, ... (at most kMergeChunk of them), and the T results are then
+  // combined across the lanes, so every partial load of the launch is in flight at once
+  const size_t idx = gid / T;
+  const int sub = (int)(gid % T);
+  if (idx >= rows * D) return;  // all T lanes of an element leave together
   const size_t r = idx / D;
   const int parts = p.n_splits;
+  const int mine = parts > sub ? (parts - sub + T - 1) / T : 0;  // partials of this lane
   const float* op = p.ws_o + idx;
   const float* mlp = p.ws_ml + r * 2;
   float mx = -INFINITY, num = 0.0f, den = 0.0f;
-  for (int j0 = 0; j0 < parts; j0 += kMergeChunk) {
+  for (int k0 = 0; k0 < mine; k0 += kMergeChunk) {
     float m[kMergeChunk], l[kMergeChunk], o[kMergeChunk];
 #pragma unroll
     for (int u = 0; u < kMergeChunk; ++u) {
-      const int j = min(j0 + u, parts - 1);  // past the end: a repeat, weighted 0 below
+      const int j = sub + T * min(k0 + u, mine - 1);  // past the end: a repeat, weighted 0 below
       const float2 ml = *reinterpret_cast<const float2*>(mlp + (size_t)j * rows * 2);
-      m[u] = j0 + u < parts ? ml.x : -INFINITY;
+      m[u] = k0 + u < mine ? ml.x : -INFINITY;
       l[u] = ml.y;
       o[u] = op[(size_t)j * rows * D];
     }
@@ -1304,7 +1311,19 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const DecodePlan p) {
     }
     mx = cm;
   }
-  p.out[idx] = num / den;
+#pragma unroll
+  for (int x = 1; x < T; x <<= 1) {
+    const float m2 = __shfl_xor(mx, x, 64), n2 = __shfl_xor(num, x, 64), d2 = __shfl_xor(den, x, 64);
+    const float cm = fmaxf(mx, m2);
+    if (cm != -INFINITY) {
+      const float f1 = mx == -INFINITY ? 0.0f : exp2f(mx - cm);
+      const float f2 = m2 == -INFINITY ? 0.0f : exp2f(m2 - cm);
+      num = f1 * num + f2 * n2;
+      den = f1 * den + f2 * d2;
+      mx = cm;
+    }
+  }
+  if (sub == 0) p.out[idx] = num / den;
 }
 
 }  // namespace
@@ -1365,11 +1384,28 @@ int static_scratch(void** ptr, size_t* bytes) {
 
 int launch_decode_merge(const DecodePlan& p, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  const unsigned blocks = (unsigned)(((size_t)p.B * p.Q * p.Hq * p.D + kThreads - 1) / kThreads);
-  if (p.D == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, dim3(blocks), dim3(kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(merge_kernel<64>, dim3(blocks), dim3(kThreads), 0, s, p);
+  // lanes per output element: enough that no lane combines more than kMergeChunk partials
+  int T = 1;
+  while (T * kMergeChunk < p.n_splits) T *= 2;
+  // (the fused step's ring store needs B H D / 4 threads, never more than the B Hq D elements)
+  const size_t threads = (size_t)p.B * p.Q * p.Hq * p.D * T;
+  const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
+#define KVQ_MERGE(D_, T_) hipLaunchKernelGGL((merge_kernel<D_, T_>), dim3(blocks), dim3(kThreads), 0, s, p)
+#define KVQ_MERGE_T(D_)             \
+  switch (T) {                      \
+    case 1: KVQ_MERGE(D_, 1); break;  \
+    case 2: KVQ_MERGE(D_, 2); break;  \
+    case 4: KVQ_MERGE(D_, 4); break;  \
+    case 8: KVQ_MERGE(D_, 8); break;  \
+    default: KVQ_MERGE(D_, 16); break; \
+  }
+  if (p.D == 128) {
+    KVQ_MERGE_T(128)
+  } else {
+    KVQ_MERGE_T(64)
+  }
+#undef KVQ_MERGE_T
+#undef KVQ_MERGE
   return (int)hipGetLastError();
 }
 
