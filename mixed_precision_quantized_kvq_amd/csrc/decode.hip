@@ -1253,13 +1253,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 //   out = sum_j 2^(m_j - m*) o_j / sum_j 2^(m_j - m*) l_j,  m* = max_j m_j.
 // A separate launch: the kernel boundary makes every partial visible, so no workgroup has
 // to write back or invalidate the L2 caches. T lanes per output element, T the smallest power
-// of two with T * kMergeChunk >= n_splits: each lane loads its (at most kMergeChunk) partials
-// all at once and combines them, and the T lane results are combined with lane shuffles, so
-// a launch waits for one round of loads whatever the split count.
+// of two with T * kMergeChunk >= n_splits, and C the smallest power of two that holds a lane's
+// share: each lane loads its (at most C) partials all at once and combines them, and the T
+// lane results are combined with lane shuffles, so a launch waits for one round of loads
+// whatever the split count.
 // ---------------------------------------------------------------------------------------
 constexpr int kMergeChunk = 16;
 
-template <int D, int T>
+template <int D, int T, int C>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const DecodePlan p) {
   const size_t rows = (size_t)p.B * p.Q * p.Hq;
   const size_t gid = (size_t)blockIdx.x * kThreads + threadIdx.x;
@@ -1275,7 +1276,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const DecodePlan p) {
     dst[piece % (D / 8)] = x;
   }
   // T adjacent lanes share output element idx; lane `sub` of them combines the partials
-  // sub, sub + T, sub + 2T, ... (at most kMergeChunk of them), and the T results are then
+  // sub, sub + T, sub + 2T, ... (at most C of them), and the T results are then
   // combined across the lanes, so every partial load of the launch is in flight at once
   const size_t idx = gid / T;
   const int sub = (int)(gid % T);
@@ -1286,10 +1287,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const DecodePlan p) {
   const float* op = p.ws_o + idx;
   const float* mlp = p.ws_ml + r * 2;
   float mx = -INFINITY, num = 0.0f, den = 0.0f;
-  for (int k0 = 0; k0 < mine; k0 += kMergeChunk) {
-    float m[kMergeChunk], l[kMergeChunk], o[kMergeChunk];
+  for (int k0 = 0; k0 < mine; k0 += C) {
+    float m[C], l[C], o[C];
 #pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u) {
+    for (int u = 0; u < C; ++u) {
       const int j = sub + T * min(k0 + u, mine - 1);  // past the end: a repeat, weighted 0 below
       const float2 ml = *reinterpret_cast<const float2*>(mlp + (size_t)j * rows * 2);
       m[u] = k0 + u < mine ? ml.x : -INFINITY;
@@ -1298,13 +1299,13 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const DecodePlan p) {
     }
     float cm = mx;
 #pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u) cm = fmaxf(cm, m[u]);
+    for (int u = 0; u < C; ++u) cm = fmaxf(cm, m[u]);
     if (cm == -INFINITY) continue;  // nothing but empty partials so far
     const float rescale = exp2f(mx - cm);  // 0 while mx is still -inf
     num *= rescale;
     den *= rescale;
 #pragma unroll
-    for (int u = 0; u < kMergeChunk; ++u) {
+    for (int u = 0; u < C; ++u) {
       const float f = m[u] == -INFINITY ? 0.0f : exp2f(m[u] - cm);
       num += f * o[u];
       den += f * l[u];
@@ -1384,27 +1385,38 @@ int static_scratch(void** ptr, size_t* bytes) {
 
 int launch_decode_merge(const DecodePlan& p, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  // lanes per output element: enough that no lane combines more than kMergeChunk partials
-  int T = 1;
-  while (T * kMergeChunk < p.n_splits) T *= 2;
+  // lanes per output element (T) and partials per lane (C): C the smallest power of two that
+  // holds every split, up to kMergeChunk; past that, T lanes of kMergeChunk each
+  int T = 1, C = 1;
+  while (C < p.n_splits && C < kMergeChunk) C *= 2;
+  while (T * C < p.n_splits) T *= 2;
   // (the fused step's ring store needs B H D / 4 threads, never more than the B Hq D elements)
   const size_t threads = (size_t)p.B * p.Q * p.Hq * p.D * T;
   const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
-#define KVQ_MERGE(D_, T_) hipLaunchKernelGGL((merge_kernel<D_, T_>), dim3(blocks), dim3(kThreads), 0, s, p)
-#define KVQ_MERGE_T(D_)             \
-  switch (T) {                      \
-    case 1: KVQ_MERGE(D_, 1); break;  \
-    case 2: KVQ_MERGE(D_, 2); break;  \
-    case 4: KVQ_MERGE(D_, 4); break;  \
-    case 8: KVQ_MERGE(D_, 8); break;  \
-    default: KVQ_MERGE(D_, 16); break; \
+#define KVQ_MERGE(D_, T_, C_) hipLaunchKernelGGL((merge_kernel<D_, T_, C_>), dim3(blocks), dim3(kThreads), 0, s, p)
+#define KVQ_MERGE_TC(D_)                                 \
+  if (T == 1) {                                          \
+    switch (C) {                                         \
+      case 1: KVQ_MERGE(D_, 1, 1); break;                \
+      case 2: KVQ_MERGE(D_, 1, 2); break;                \
+      case 4: KVQ_MERGE(D_, 1, 4); break;                \
+      case 8: KVQ_MERGE(D_, 1, 8); break;                \
+      default: KVQ_MERGE(D_, 1, kMergeChunk); break;     \
+    }                                                    \
+  } else {                                               \
+    switch (T) {                                         \
+      case 2: KVQ_MERGE(D_, 2, kMergeChunk); break;      \
+      case 4: KVQ_MERGE(D_, 4, kMergeChunk); break;      \
+      case 8: KVQ_MERGE(D_, 8, kMergeChunk); break;      \
+      default: KVQ_MERGE(D_, 16, kMergeChunk); break;    \
+    }                                                    \
   }
   if (p.D == 128) {
-    KVQ_MERGE_T(128)
+    KVQ_MERGE_TC(128)
   } else {
-    KVQ_MERGE_T(64)
+    KVQ_MERGE_TC(64)
   }
-#undef KVQ_MERGE_T
+#undef KVQ_MERGE_TC
 #undef KVQ_MERGE
   return (int)hipGetLastError();
 }
