@@ -297,10 +297,10 @@ def workload_bits(kvq, w, xk=None, xv=None):
 
 
 def other_configs():
-    """The other full-size workloads, one GPU: split-K decode time of the 8k-token Llama-shaped
-    layer, of the 128k-token context and of the 32k-token workload with per-channel key
-    normalization (caches rotated so their reads come from HBM, launches back to back behind
-    a spin kernel, HIP events on the launch stream), decode + merge of one and of several query
+    """The other full-size workloads, one GPU: split-K decode time (and split-K + merge time) of
+    the 8k-token Llama-shaped layer, of the 128k-token context and of the 32k-token workload with
+    per-channel key normalization (caches rotated so their reads come from HBM, launches back to
+    back behind a spin kernel, HIP events on the launch stream), decode + merge of one and of several query
     tokens per row on the multi-head 7B-shaped layer and on the 32k-token GQA workload, a ragged serving step (rows of 32767,
     28000, 20000 and 12000 tokens; host loop, append + decode + merge), and the ingest rate of the 16 x
     4096-token prefill (calibration, allocation, then one append of every token), with and
@@ -342,11 +342,25 @@ def other_configs():
             torch.cuda.synchronize()
             t_us.append(e0.elapsed_time(e1) * 1e3 / 50)
         us = float(np.median(t_us))
+        # the whole call: split-K launch and merge launch, same method
+        out = torch.empty((s.batch, s.n_q, s.head_dim), dtype=torch.float32, device=dev)
+        t_us = []
+        for _ in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(20_000_000)
+            e0.record(stream)
+            for i in range(50):
+                kvq.decode_attention(caches[i % n_inst], q, out, s.n_splits, ws, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t_us.append(e0.elapsed_time(e1) * 1e3 / 50)
+        us_merge = float(np.median(t_us))
         nbytes = decode_bytes(s, kb, vb, s.tokens, s.n_splits)
-        res[name + ("_key_norm" if key_norm else "")] = {"decode_us": us, "bytes_per_launch": nbytes, "achieved_gbs": nbytes / (us * 1e-6) / 1e9,
+        res[name + ("_key_norm" if key_norm else "")] = {"decode_us": us, "decode_merge_us": us_merge,
+                     "bytes_per_launch": nbytes, "achieved_gbs": nbytes / (us * 1e-6) / 1e9,
                      "frac_of_8tbs": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "k_bits": kb, "v_bits": vb,
                      "n_splits": s.n_splits, "kv_tokens_heads_per_s": s.batch * s.n_kv * s.tokens / (us * 1e-6)}
-        del caches, ws, q
+        del caches, ws, q, out
         torch.cuda.empty_cache()
     # the 32k-token workload on paged caches: 64-token pages dealt to (row, tile) from a pool
     # in a shuffled order, one permutation per cache instance
