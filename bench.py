@@ -160,8 +160,8 @@ def decode_bytes(spec, k_bits, v_bits, T, n_splits):
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "decode_kernel_qwen8b_t32k_traffic.txt")
-KERNEL_SRCS = [os.path.join(os.path.dirname(os.path.abspath(__file__)), "mixed_precision_quantized_kvq_amd",
-                            "csrc", f) for f in ("decode.hip", "code_plans.h", "kvq_internal.h")]
+KERNEL_SRCS = [os.path.join(os.path.dirname(os.path.abspath(__file__)), "mixed_precision_quantized_kvq_amd", f)
+               for f in ("csrc/decode.hip", "csrc/code_plans.h", "csrc/kvq_internal.h", "build.py")]
 
 
 def kernel_sources_sha256():

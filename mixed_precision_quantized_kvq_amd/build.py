@@ -28,8 +28,11 @@ SOURCES = {
     "kvq_abi.cpp": EXACT,
     "append.hip": EXACT,
     "calib.hip": EXACT,
-    # MFMA accumulators in ordinary VGPRs: no accumulator-register copies in the decode loop
-    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # MFMA accumulators in ordinary VGPRs: no accumulator-register copies in the decode loop.
+    # The iterative ILP scheduler: 2-3 % faster split-K decode on the 32k- and 128k-token
+    # workloads than the default schedule (same instructions, no spills); it made the append
+    # flush slower and does not compile the 16-row tile, so those keep the default
+    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
     "decode_dense.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
