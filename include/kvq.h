@@ -134,7 +134,9 @@ kvq_status kvq_cache_init_paged(kvq_cache* cache, const kvq_config* cfg, int32_t
  * (host array; each entry in [0, n_pages), or -1 to unmap; no page twice). Tile t holds body tokens
  * 64t .. 64t + 63 of the row, i.e. tokens n_sink + 64t .. of the sequence; a row holding T
  * tokens needs its first ceil(body(T) / 64) tiles mapped, body(T) as in the decode
- * description. Copies synchronously on `stream` (host order with earlier work on it). */
+ * description. KVQ_ERR_ARG, with nothing written, if after the call one page would hold two
+ * tiles (of this or any other row): the call reads the table back to check. Copies
+ * synchronously on `stream` (host order with earlier work on it). */
 kvq_status kvq_cache_map_pages(const kvq_cache* cache, int32_t row, int32_t first_tile, int32_t n_tiles,
                                const int32_t* pages, void* stream);
 

@@ -177,17 +177,32 @@ kvq_status kvq_cache_map_pages(const kvq_cache* cache, int32_t row, int32_t firs
   for (int i = 0; i < n_tiles; ++i)
     if (pages[i] < -1 || pages[i] >= cache->n_pages)
       return fail(KVQ_ERR_ARG, "page index out of range at " + std::to_string(i));
-  {  // one page for two tiles of this call would alias them
-    std::vector<int32_t> sorted(pages, pages + n_tiles);
-    std::sort(sorted.begin(), sorted.end());
-    for (int i = 1; i < n_tiles; ++i)
-      if (sorted[i] >= 0 && sorted[i] == sorted[i - 1])
-        return fail(KVQ_ERR_ARG, "page " + std::to_string(sorted[i]) + " is given to two tiles");
-  }
   uint64_t pt_off = 0;
   plan_layout(cache->cfg, nullptr, cache->n_pages, &pt_off);
-  char* dst = static_cast<char*>(cache->dev) + pt_off + ((size_t)row * stride + first_tile) * 4;
-  hipError_t e = hipMemcpyAsync(dst, pages, (size_t)n_tiles * 4, hipMemcpyHostToDevice, as_stream(stream));
+  char* table = static_cast<char*>(cache->dev) + pt_off;
+  // The table as it will be after this call must give no page to two tiles (of any row):
+  // read it back, apply the new entries on the host and count every page's uses.
+  const size_t entries = (size_t)cache->cfg.batch * stride;
+  std::vector<int32_t> after(entries);
+  hipError_t e = hipMemcpyAsync(after.data(), table, entries * 4, hipMemcpyDeviceToHost, as_stream(stream));
+  if (e == hipSuccess) e = hipStreamSynchronize(as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "page table read");
+  std::copy(pages, pages + n_tiles, after.begin() + (size_t)row * stride + first_tile);
+  std::vector<int64_t> owner(cache->n_pages, -1);
+  for (size_t i = 0; i < entries; ++i) {
+    const int32_t pg = after[i];
+    if (pg < 0) continue;
+    if (pg >= cache->n_pages) return fail(KVQ_ERR_ARG, "the page table holds an out-of-range page");
+    if (owner[pg] >= 0) {
+      const size_t j = (size_t)owner[pg];
+      return fail(KVQ_ERR_ARG, "page " + std::to_string(pg) + " would hold two tiles: row " + std::to_string(j / stride) +
+                                   " tile " + std::to_string(j % stride) + " and row " + std::to_string(i / stride) +
+                                   " tile " + std::to_string(i % stride));
+    }
+    owner[pg] = (int64_t)i;
+  }
+  char* dst = table + ((size_t)row * stride + first_tile) * 4;
+  e = hipMemcpyAsync(dst, pages, (size_t)n_tiles * 4, hipMemcpyHostToDevice, as_stream(stream));
   if (e == hipSuccess) e = hipStreamSynchronize(as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "page table copy");
   return KVQ_OK;

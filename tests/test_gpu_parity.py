@@ -877,6 +877,26 @@ def test_paged_cache(kb, vb, quant, dtype, D):
     say("    paged decode equals the contiguous cache's decode bit for bit")
 
 
+def test_page_given_to_two_tiles_is_rejected():
+    """kvq_cache_map_pages refuses any call after which one page would hold two tiles, within
+    the call, across calls or across rows, and then writes nothing; remapping a tile, freeing a
+    page and giving it to another tile is allowed."""
+    ocfg = O.CacheConfig(2, 1, 1, 64, 400, 2, 32, "fp16", "asym", (2,), (2,))
+    cache = kvq.cache_init_paged(lib_cfg(kvq, ocfg), 8, device=DEV)
+    cache.map_pages(0, 0, [5, 7])
+    cache.map_pages(0, 0, [5, 7])  # the same mapping again
+    for row, first, pages in ((1, 0, [5]), (0, 2, [7]), (1, 0, [3, 3])):
+        with pytest.raises(kvq.KvqError) as e:
+            cache.map_pages(row, first, pages)
+        assert e.value.status == -1
+    cache.map_pages(1, 0, [6])  # row 1 tile 0 was left unmapped by the rejected calls
+    cache.map_pages(0, 0, [2, -1])  # frees pages 5 and 7
+    cache.map_pages(1, 1, [5, 7])
+    with pytest.raises(kvq.KvqError) as e:
+        cache.map_pages(0, 1, [6])
+    assert e.value.status == -1
+
+
 def test_paged_unmapped_tile_is_flagged():
     say("case: paged cache append into an unmapped tile")
     ocfg = O.CacheConfig(1, 1, 1, 64, 400, 2, 8, "bf16", "asym", (2,), (3,))
